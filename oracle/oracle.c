@@ -1,0 +1,293 @@
+/*
+ * oracle.c -- CPU oracle for the fused dual RMSNorm + per-1x128 FP8 group
+ * quantisation of an MLA decode step, and for the block-scaled FP8 GEMM that
+ * consumes its (q_fp8, scale) pair.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load this library.  The product path
+ * (the HIP library and its Python binding) never links, imports or calls it,
+ * and this file shares no code, header, table or constant generator with it.
+ *
+ * Plain, slow and meant to be checked by eye: every value is carried in fp64
+ * unless a step of the method fixes another precision (the stored scale is an
+ * fp32 number, the outputs are bf16 / e4m3fn codes).  No blocking, fusion or
+ * reordering beyond the definitions below.  The row loops and the GEMM column
+ * loop carry an OpenMP pragma; it changes nothing in the arithmetic of a row
+ * or of an output element.
+ *
+ * Sources (web pages; cited by title and section):
+ *  [PR53540]  GitHub page "[ROCm][Perf] Fuse SWA q/kv RMSNorm and q FP8 group
+ *             quant for DeepSeek-V4 #53540" (vllm-project/vllm), section
+ *             "Purpose".
+ *  [D53540]   PRHub digest of vLLM PR #53540, sections "功能与动机"
+ *             (motivation), "实现拆解" (implementation breakdown) and the
+ *             source excerpt of _fused_mla_dual_rms_norm_group_quant_impl.
+ *  [D56433]   PRHub report of vLLM PR #56433 "Fix AITER preshuffled FP8
+ *             block-scale kernel", "实现拆解" items 2 and 4.
+ *  [D27289]   PRHub digest of SGLang PR #27289 (fp8 scale transpose copy),
+ *             "功能与动机" and the aiter_w8a8_block_fp8_linear excerpt.
+ *
+ * Readings taken where the pages are silent (each also listed in the design
+ * notes of the repository):
+ *  - FP8 is OCP e4m3fn: bias 7, largest finite 448 (0x7E), 0x7F/0xFF NaN,
+ *    no infinities, subnormals down to 2^-9.
+ *  - RMSNorm: y = x * gamma / sqrt(mean(x^2) + eps), gamma a plain multiplier.
+ *  - The group scale is the dequantisation multiplier s = amax/448, stored as
+ *    an fp32 number, floored at 1e-12f; codes = RNE_e4m3(clamp(y/s, +-448)).
+ *  - kv_out = bf16 round-to-nearest-even of the exact normalised value.
+ *  - Column-major ("transposed") scales: the [M, G] logical array stored as
+ *    its transpose, element (m, g) at offset g*M + m, leading dimension M.
+ *  - GEMM: out[m,n] = sum_kb As[m,kb]*Bs[n/128,kb]*sum_{k in kb} a*w, with
+ *    As in the layout the caller states and Bs row-major [N/128, K/128].
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_GROUP 128
+#define ORACLE_E4M3_MAX 448.0
+#define ORACLE_SCALE_FLOOR 1e-12f
+
+/* ---------------------------------------------------------------------------
+ * bf16: 1 sign bit, 8 exponent bits (bias 127), 7 stored mantissa bits.
+ * ------------------------------------------------------------------------- */
+
+/* Exact value of a bf16 bit pattern: the top half of the fp32 with the same
+ * sign, exponent and mantissa bits. */
+double oracle_bf16_decode(uint16_t bits)
+{
+    int sign = bits >> 15;
+    int e = (bits >> 7) & 0xFF;
+    int f = bits & 0x7F;
+    double v;
+    if (e == 0xFF)
+        v = f ? NAN : INFINITY;
+    else if (e == 0)
+        v = ldexp((double)f, -133);            /* subnormal: f * 2^-126 * 2^-7 */
+    else
+        v = ldexp((double)(128 + f), e - 134); /* (1 + f/128) * 2^(e-127) */
+    return sign ? -v : v;
+}
+
+/* Round an fp64 value straight to the nearest bf16 (ties to even mantissa),
+ * with a single rounding (never via fp32).  Overflow gives +-inf. */
+uint16_t oracle_bf16_encode(double v)
+{
+    if (isnan(v))
+        return 0x7FC0;
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (a == 0.0)
+        return sign;
+    if (isinf(a))
+        return sign | 0x7F80;
+    int e2;
+    frexp(a, &e2);                  /* a = f * 2^e2, f in [0.5, 1) */
+    int E = e2 - 1;                 /* a in [2^E, 2^(E+1)) */
+    /* spacing of bf16 values around a: 2^(E-7) for normals, 2^-133 below 2^-126 */
+    int qexp = (E < -126) ? -133 : E - 7;
+    double r = nearbyint(ldexp(a, -qexp)); /* RNE under the default mode */
+    /* normals: bits = ((E+127) << 7) + (r - 128); r == 256 carries into the
+     * exponent.  subnormals: bits = r; r == 128 is the smallest normal. */
+    long bits = (E < -126) ? (long)r : ((long)(E + 127) << 7) + ((long)r - 128);
+    if (bits >= 0x7F80)
+        return sign | 0x7F80;
+    return (uint16_t)(sign | bits);
+}
+
+/* ---------------------------------------------------------------------------
+ * e4m3fn: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits, exponent
+ * field 15 with mantissa 7 is NaN, everything else finite (max 448).
+ * ------------------------------------------------------------------------- */
+
+double oracle_e4m3_decode(uint8_t code)
+{
+    int sign = code >> 7;
+    int e = (code >> 3) & 0xF;
+    int f = code & 0x7;
+    double v;
+    if (e == 0xF && f == 0x7)
+        v = NAN;
+    else if (e == 0)
+        v = ldexp((double)f, -9);              /* f/8 * 2^-6 */
+    else
+        v = ldexp((double)(8 + f), e - 10);    /* (1 + f/8) * 2^(e-7) */
+    return sign ? -v : v;
+}
+
+/* Nearest e4m3fn code, ties to even mantissa, saturating at +-448 (0x7E /
+ * 0xFE).  NaN input gives 0x7F.  -0.0 gives 0x80. */
+uint8_t oracle_e4m3_encode(double v)
+{
+    if (isnan(v))
+        return 0x7F;
+    uint8_t sign = signbit(v) ? 0x80 : 0;
+    double a = fabs(v);
+    if (a >= ORACLE_E4M3_MAX)
+        return sign | 0x7E;
+    if (a == 0.0)
+        return sign;
+    int e2;
+    frexp(a, &e2);
+    int E = e2 - 1;                             /* a in [2^E, 2^(E+1)) */
+    int qexp = (E < -6) ? -9 : E - 3;           /* spacing of codes around a */
+    double r = nearbyint(ldexp(a, -qexp));
+    int bits = (E < -6) ? (int)r : ((E + 7) << 3) + ((int)r - 8);
+    /* a < 448 keeps bits <= 0x7E (ties at 464 cannot occur below 448) */
+    return (uint8_t)(sign | bits);
+}
+
+/* fp32 round-to-nearest of an fp64 value (the C conversion rounds to nearest
+ * even in the default mode). */
+static float to_f32(double v) { return (float)v; }
+
+/* ---------------------------------------------------------------------------
+ * Fused dual RMSNorm + per-1x128 FP8 group quantisation.
+ *
+ * [PR53540] "Purpose": one kernel RMSNorms both latents with fp32
+ * accumulation and quantises the q latent per 1x128 with fp32 scales; the
+ * quantisation reads the fp32 normalised values directly (one rounding), kv
+ * stays bf16.  [D53540] impl excerpt: outputs are q_out [M, Nq] fp8, q_scale
+ * [M, Nq/group] fp32, kv_normed with kv's shape, all freshly allocated
+ * (contiguous); q and kv may be strided split views with unit inner stride.
+ * [D56433] item 4 / [D27289]: transpose_scale selects the column-major scale
+ * layout, the bytes of x_scale.transpose(-1,-2).contiguous().
+ *
+ * Oracle arithmetic: everything in fp64 from the exactly decoded bf16 inputs,
+ * i.e. the exact mathematical value up to fp64 rounding (far below the fp32
+ * accumulation the pages describe).
+ *
+ * sequential != 0 gives the pre-fusion semantics instead ([PR53540]
+ * "Purpose", the three-launch pipeline): the normalised q is first rounded to
+ * bf16, then group-quantised.
+ *
+ * out_ratio (nullable): y/s before clamping and rounding, fp64, [M, Nq]; the
+ * value whose rounding decides each code.
+ * out_y (nullable): the normalised q value y (after the optional bf16 step).
+ * ------------------------------------------------------------------------- */
+void oracle_dual_rmsnorm_group_quant(
+    const uint16_t *q, int64_t q_row_stride,
+    const uint16_t *kv, int64_t kv_row_stride,
+    const uint16_t *gamma_q, const uint16_t *gamma_kv,
+    float eps, int64_t M, int64_t Nq, int64_t Nkv,
+    int transpose_scale, int sequential,
+    uint8_t *out_q, float *out_scale, uint16_t *out_kv,
+    double *out_ratio, double *out_y)
+{
+    const int64_t G = Nq / ORACLE_GROUP;
+
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t *xq = q + m * q_row_stride;
+        const uint16_t *xk = kv + m * kv_row_stride;
+
+        /* mean of squares and reciprocal RMS, per latent */
+        double ssq_q = 0.0, ssq_k = 0.0;
+        for (int64_t i = 0; i < Nq; ++i) {
+            double x = oracle_bf16_decode(xq[i]);
+            ssq_q += x * x;
+        }
+        for (int64_t i = 0; i < Nkv; ++i) {
+            double x = oracle_bf16_decode(xk[i]);
+            ssq_k += x * x;
+        }
+        double rstd_q = 1.0 / sqrt(ssq_q / (double)Nq + (double)eps);
+        double rstd_k = 1.0 / sqrt(ssq_k / (double)Nkv + (double)eps);
+
+        /* kv: normalise, scale by gamma, round once to bf16 */
+        for (int64_t i = 0; i < Nkv; ++i) {
+            double y = oracle_bf16_decode(xk[i]) * rstd_k * oracle_bf16_decode(gamma_kv[i]);
+            out_kv[m * Nkv + i] = oracle_bf16_encode(y);
+        }
+
+        /* q: per group of 128 consecutive columns */
+        for (int64_t g = 0; g < G; ++g) {
+            double y[ORACLE_GROUP];
+            double amax = 0.0;
+            for (int j = 0; j < ORACLE_GROUP; ++j) {
+                int64_t i = g * ORACLE_GROUP + j;
+                y[j] = oracle_bf16_decode(xq[i]) * rstd_q * oracle_bf16_decode(gamma_q[i]);
+                if (sequential)
+                    y[j] = oracle_bf16_decode(oracle_bf16_encode(y[j]));
+                if (fabs(y[j]) > amax)
+                    amax = fabs(y[j]);
+            }
+            /* dequantisation multiplier, stored in fp32, floored */
+            float s = to_f32(amax / ORACLE_E4M3_MAX);
+            if (s < ORACLE_SCALE_FLOOR)
+                s = ORACLE_SCALE_FLOOR;
+
+            int64_t scale_at = transpose_scale ? g * M + m : m * G + g;
+            out_scale[scale_at] = s;
+
+            for (int j = 0; j < ORACLE_GROUP; ++j) {
+                int64_t i = g * ORACLE_GROUP + j;
+                double ratio = y[j] / (double)s;
+                if (out_ratio)
+                    out_ratio[m * Nq + i] = ratio;
+                if (out_y)
+                    out_y[m * Nq + i] = y[j];
+                double c = ratio;
+                if (c > ORACLE_E4M3_MAX)
+                    c = ORACLE_E4M3_MAX;
+                if (c < -ORACLE_E4M3_MAX)
+                    c = -ORACLE_E4M3_MAX;
+                out_q[m * Nq + i] = oracle_e4m3_encode(c);
+            }
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * Block-scaled FP8 GEMM on the pre-quantised activation.
+ *
+ * [D53540] excerpt of apply_pre_quantized_block_scaled_mm: the linear's
+ * block-scaled GEMM is called as (A = x_fp8, B = weight, As = x_scale,
+ * Bs = weight_scale or weight_scale_inv), the weight scale used as given.
+ * [D27289] excerpt of aiter_w8a8_block_fp8_linear: weight [N, K], output
+ * [M, N] in bf16 for a pre-quantised input.  [D56433] item 2: a GEMM reads As
+ * either row-major or column-major, and both have the same logical shape.
+ *
+ * out[m, n] = sum over K-blocks kb of  As[m, kb] * Bs[n/128, kb]
+ *             * sum_{k in kb} dec(a[m, k]) * dec(w[n, k])
+ * The inner block sums are exact in fp64 (e4m3 products carry <= 8
+ * significant bits); the result is returned in fp64, unrounded.
+ * ------------------------------------------------------------------------- */
+void oracle_block_scaled_fp8_gemm(
+    const uint8_t *a, const float *a_scale, int a_scale_transposed,
+    const uint8_t *w, const float *w_scale,
+    double *out, int64_t M, int64_t N, int64_t K)
+{
+    const int64_t KB = K / ORACLE_GROUP;
+
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        const int64_t nb = n / ORACLE_GROUP;
+        for (int64_t m = 0; m < M; ++m) {
+            double acc = 0.0;
+            for (int64_t kb = 0; kb < KB; ++kb) {
+                double block = 0.0;
+                for (int64_t k = kb * ORACLE_GROUP; k < (kb + 1) * ORACLE_GROUP; ++k)
+                    block += oracle_e4m3_decode(a[m * K + k]) * oracle_e4m3_decode(w[n * K + k]);
+                double as = a_scale_transposed ? a_scale[kb * M + m] : a_scale[m * KB + kb];
+                double bs = w_scale[nb * KB + kb];
+                acc += as * bs * block;
+            }
+            out[m * N + n] = acc;
+        }
+    }
+}
+
+/* Number of threads the parallel loops above use (1 without OpenMP). */
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
