@@ -1,0 +1,401 @@
+#!/usr/bin/env python3
+"""Benchmark of the MLA decode hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  1. fused dual RMSNorm + per-1x128 FP8 group quant of M tokens (q latent
+     [M, 1536] and kv latent [M, 512], strided split views of one [M, 2048]
+     bf16 projection buffer), scales in the layout both consumers agreed on;
+  2. block-scaled FP8 GEMM of the quantised q with W_a [24576, 1536]
+     (attention wq_b);
+  3. the same with W_b [8192, 1536] (indexer wq_b), sharing the pair.
+Default M = 64 (a decode batch).  Inputs are resident in HBM before the
+timed region; every step uses the next of several buffer sets (weights,
+activations, outputs) whose total exceeds the 256 MB Infinity Cache, so the
+weights stream from HBM as they do in a real decode step ("cold").  The step
+is captured once as a HIP graph and replayed.
+
+Prints ONE JSON line.  ``value`` is microseconds per step (lower is better).
+``roofline`` is for the kernel that dominates the step, from HIP events
+around back-to-back launches of that kernel on the stream it runs on.
+``cpu_baseline`` is the CPU oracle timed on this host on one full step.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "norm+FP8-quant µs/call & HBM GB/s (% peak) at M=1/64/8192; FP8 GEMM % MFMA"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP8_MFMA_PEAK_TFLOPS = 5000.0  # MI355X dense FP8
+MALL_BYTES = 256 << 20
+COLD_BYTES = 1 << 30           # rotate buffer sets past 1 GiB
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--M", type=int, default=64, help="tokens per step")
+    ap.add_argument("--scale-layout", choices=("row", "col"), default="col")
+    ap.add_argument("--warm", action="store_true", help="reuse one buffer set (cache-warm numbers)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the M=1 / M=8192 / M=256 extras")
+    ap.add_argument("--kernel-loop", default="", help="only launch this kernel in a loop (profiling)")
+    return ap.parse_args()
+
+
+# --------------------------------------------------------------- helpers
+
+def algorithmic_bytes_normquant(M, Nq=1536, Nkv=512):
+    """Bytes the fused norm-quant must move: read q and kv rows (bf16) and
+    both gammas once; write codes (1 B), scales (4 B per 128) and kv (bf16)."""
+    G = Nq // 128
+    return M * (2 * Nq + 2 * Nkv + Nq + 4 * G + 2 * Nkv) + 2 * (Nq + Nkv)
+
+
+def algorithmic_bytes_gemm(M, N, K):
+    """Weight codes + weight scales + activation codes + activation scales +
+    bf16 output, each moved once."""
+    return N * K + 4 * (N // 128) * (K // 128) + M * K + 4 * M * (K // 128) + 2 * M * N
+
+
+def gemm_flops(M, N, K):
+    return 2 * M * N * K
+
+
+def source_sha(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "rmsnorm_fp8_block_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, sha):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(kernel)
+    if not e or e.get("source_sha") != sha:
+        return None
+    return e.get("bytes_per_launch")
+
+
+class Timer:
+    """HIP events on torch's current stream (the stream every launch below
+    goes to)."""
+
+    def __init__(self, torch):
+        self.t = torch
+        self.a = torch.cuda.Event(enable_timing=True)
+        self.b = torch.cuda.Event(enable_timing=True)
+
+    def start(self):
+        self.a.record()
+
+    def stop_ms(self):
+        self.b.record()
+        self.b.synchronize()
+        return self.a.elapsed_time(self.b)
+
+
+def make_graph(torch, fns):
+    """Capture the given launches once (warm-up run first, on a side stream
+    as torch requires) and return the replayable graph."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for f in fns:
+            f()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(torch, g, launches_per_replay, replays, warmup=2):
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    tm.start()
+    for _ in range(replays):
+        g.replay()
+    ms = tm.stop_ms()
+    return 1000.0 * ms / (replays * launches_per_replay)
+
+
+def time_eager(torch, fns, reps, warmup=3):
+    """Back-to-back eager launches cycling through ``fns``; us per launch."""
+    for i in range(warmup * len(fns)):
+        fns[i % len(fns)]()
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    tm.start()
+    for i in range(reps):
+        fns[i % len(fns)]()
+    ms = tm.stop_ms()
+    return 1000.0 * ms / reps
+
+
+# ----------------------------------------------------------- workloads
+
+def bf16_dev(torch, np, a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def build_sets(torch, np, mi, W, M, layout, wa, wb, nsets, dev):
+    """``nsets`` independent buffer sets for the full step (device copies of
+    the same seeded inputs), each with its own outputs."""
+    case = W.producer_activations(M) if M <= 256 else W.strided_batch(M)
+    buf0 = bf16_dev(torch, np, case.buffer, dev)
+    gq = bf16_dev(torch, np, case.gamma_q, dev)
+    gk = bf16_dev(torch, np, case.gamma_kv, dev)
+    wa_c0 = torch.from_numpy(wa.codes).to(dev)
+    wa_s0 = torch.from_numpy(wa.scale).to(dev)
+    wb_c0 = torch.from_numpy(wb.codes).to(dev)
+    wb_s0 = torch.from_numpy(wb.scale).to(dev)
+    G = W.NQ // 128
+    sets = []
+    for i in range(nsets):
+        buf = buf0 if i == 0 else buf0.clone()
+        q, kv = buf[:, :W.NQ], buf[:, W.NQ:]
+        oq = torch.empty((M, W.NQ), dtype=torch.uint8, device=dev)
+        osc = torch.empty(M * G, dtype=torch.float32, device=dev)
+        okv = torch.empty((M, W.NKV), dtype=torch.bfloat16, device=dev)
+        scale = osc.as_strided((M, G), (1, M)) if layout else osc.view(M, G)
+        wa_c = wa_c0 if i == 0 else wa_c0.clone()
+        wb_c = wb_c0 if i == 0 else wb_c0.clone()
+        oa = torch.empty((M, wa.codes.shape[0]), dtype=torch.bfloat16, device=dev)
+        ob = torch.empty((M, wb.codes.shape[0]), dtype=torch.bfloat16, device=dev)
+        sets.append({
+            "nq": mi.prepare_fused_dual_rmsnorm_group_quant(q, kv, gq, gk, W.EPS, layout, oq, osc, okv),
+            "ga": mi.prepare_block_scaled_fp8_gemm(oq, scale, wa_c, wa_s0, oa),
+            "gb": mi.prepare_block_scaled_fp8_gemm(oq, scale, wb_c, wb_s0, ob),
+        })
+    return sets
+
+
+def cpu_baseline(np, W, M, layout, wa, wb):
+    """The oracle as it stands, on this host: one full step (norm-quant of
+    the same M rows, then both GEMMs over all their columns)."""
+    import oracle
+    case = W.producer_activations(M) if M <= 256 else W.strided_batch(M)
+    t0 = time.perf_counter()
+    r = oracle.dual_rmsnorm_group_quant(case.q, case.kv, case.gamma_q, case.gamma_kv, W.EPS, layout)
+    oracle.block_scaled_fp8_gemm(r["q"], r["scale"], layout, wa.codes, wa.scale)
+    oracle.block_scaled_fp8_gemm(r["q"], r["scale"], layout, wb.codes, wb.scale)
+    dt = time.perf_counter() - t0
+    return {"value": round(dt * 1e6, 1), "unit": "µs/step", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"one full step at M={M}: fp64 norm-quant of {M} rows + both GEMMs over all "
+                      f"{wa.codes.shape[0] + wb.codes.shape[0]} output columns ({dt:.1f} s wall)"}
+
+
+def sweep(torch, np, mi, W, wa, wb, dev, cold):
+    """Extra figures of the metric: norm-quant at M=1 (us/call) and M=8192
+    (GB/s, both layouts); the GEMMs at M=256 (TFLOP/s, % of FP8 MFMA peak)."""
+    res = {}
+    gq = bf16_dev(torch, np, W.gammas()[0], dev)
+    gk = bf16_dev(torch, np, W.gammas()[1], dev)
+    # M = 1: latency.  Many tiny buffer sets, one launch each, in a graph.
+    one = W.decode_single()
+    q1 = bf16_dev(torch, np, one.q, dev)
+    k1 = bf16_dev(torch, np, one.kv, dev)
+    fns = []
+    for i in range(64):
+        q = q1.clone()
+        k = k1.clone()
+        fns.append(mi.prepare_fused_dual_rmsnorm_group_quant(
+            q, k, gq, gk, W.EPS, False, torch.empty(1536, dtype=torch.uint8, device=dev),
+            torch.empty(12, dtype=torch.float32, device=dev),
+            torch.empty(512, dtype=torch.bfloat16, device=dev)))
+    g = make_graph(torch, fns)
+    res["normquant_M1_us_per_call_graph"] = round(time_graph(torch, g, len(fns), 20), 3)
+    res["normquant_M1_us_per_call_eager"] = round(time_eager(torch, fns, 2000), 3)
+    del g, fns
+    # M = 8192 prefill, both layouts
+    pre = W.prefill(8192)
+    bufp = bf16_dev(torch, np, pre.buffer, dev)
+    nbytes = algorithmic_bytes_normquant(8192)
+    nsets = max(1, COLD_BYTES // nbytes + 1) if cold else 1
+    for layout in (0, 1):
+        fns = []
+        for i in range(nsets):
+            b = bufp if i == 0 else bufp.clone()
+            fns.append(mi.prepare_fused_dual_rmsnorm_group_quant(
+                b[:, :W.NQ], b[:, W.NQ:], gq, gk, W.EPS, layout,
+                torch.empty((8192, 1536), dtype=torch.uint8, device=dev),
+                torch.empty(8192 * 12, dtype=torch.float32, device=dev),
+                torch.empty((8192, 512), dtype=torch.bfloat16, device=dev)))
+        g = make_graph(torch, fns)
+        us = time_graph(torch, g, len(fns), max(1, 200 // len(fns)))
+        gbs = nbytes / us / 1e3
+        res[f"normquant_M8192_{'col' if layout else 'row'}"] = {
+            "us": round(us, 3), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+        del g, fns
+        torch.cuda.empty_cache()
+    del bufp
+    # GEMMs at M = 256
+    M = 256
+    a = torch.randint(0, 0x78, (M, 1536), dtype=torch.uint8, device=dev)
+    asc = torch.rand((M, 12), dtype=torch.float32, device=dev) + 0.5
+    for name, wt in (("W_a", wa), ("W_b", wb)):
+        N, K = wt.codes.shape
+        wc0 = torch.from_numpy(wt.codes).to(dev)
+        ws = torch.from_numpy(wt.scale).to(dev)
+        per = algorithmic_bytes_gemm(M, N, K)
+        nsets = max(1, COLD_BYTES // per + 1) if cold else 1
+        fns = []
+        for i in range(nsets):
+            wc = wc0 if i == 0 else wc0.clone()
+            fns.append(mi.prepare_block_scaled_fp8_gemm(
+                a, asc, wc, ws, torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
+        g = make_graph(torch, fns)
+        us = time_graph(torch, g, len(fns), max(1, 200 // len(fns)))
+        tf = gemm_flops(M, N, K) / us / 1e6
+        res[f"gemm_{name}_M256"] = {"us": round(us, 3), "TFLOP/s": round(tf, 1),
+                                    "frac_fp8_mfma": round(tf / FP8_MFMA_PEAK_TFLOPS, 4),
+                                    "GB/s": round(per / us / 1e3, 1)}
+        del g, fns
+        torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); "
+              "the path has no cross-GPU step to measure", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import rmsnorm_fp8_block_amd as mi
+    from rmsnorm_fp8_block_amd import workloads as W
+
+    mi.lib()  # fails loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+    layout = 1 if args.scale_layout == "col" else 0
+    M = args.M
+
+    wa = W.block_fp8_weight(*W.W_A_SHAPE, W.W_A_SEED)
+    wb = W.block_fp8_weight(*W.W_B_SHAPE, W.W_B_SEED)
+    step_bytes = (algorithmic_bytes_normquant(M) + algorithmic_bytes_gemm(M, *W.W_A_SHAPE)
+                  + algorithmic_bytes_gemm(M, *W.W_B_SHAPE))
+    nsets = 1 if args.warm else max(2, COLD_BYTES // step_bytes + 1)
+    sets = build_sets(torch, np, mi, W, M, layout, wa, wb, nsets, dev)
+    torch.cuda.synchronize()
+
+    if args.kernel_loop:
+        # profiling aid: only the named kernel, back to back over the sets
+        key = {"normquant": "nq", "gemm_a": "ga", "gemm_b": "gb"}[args.kernel_loop]
+        fns = [s[key] for s in sets]
+        us = time_eager(torch, fns, args.steps)
+        print(json.dumps({"kernel_loop": args.kernel_loop, "us_per_launch": us}))
+        return
+
+    # ---- the timed region: K steps, graph-replayed over the buffer sets ----
+    step_fns = []
+    for s in sets:
+        step_fns += [s["nq"], s["ga"], s["gb"]]
+    g = make_graph(torch, step_fns)
+    replays_warm = max(1, -(-args.warmup // nsets))
+    replays = max(1, -(-args.steps // nsets))
+    steps = replays * nsets
+    for _ in range(replays_warm):
+        g.replay()
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    tm.start()
+    for _ in range(replays):
+        g.replay()
+    ms = tm.stop_ms()
+    torch.cuda.synchronize()
+    us_step = 1000.0 * ms / steps
+
+    # ---- per-kernel average launch duration (events around back-to-back
+    # launches of one kernel over the same buffer sets, same stream) ----
+    kernels = {}
+    specs = {
+        "fused_dual_rmsnorm_group_quant": ("nq", algorithmic_bytes_normquant(M), None, "normquant.hip"),
+        "block_scaled_fp8_gemm_W_a": ("ga", algorithmic_bytes_gemm(M, *W.W_A_SHAPE),
+                                      gemm_flops(M, *W.W_A_SHAPE), "gemm_fp8_bs.hip"),
+        "block_scaled_fp8_gemm_W_b": ("gb", algorithmic_bytes_gemm(M, *W.W_B_SHAPE),
+                                      gemm_flops(M, *W.W_B_SHAPE), "gemm_fp8_bs.hip"),
+    }
+    for name, (key, nbytes, flops, src) in specs.items():
+        fns = [s[key] for s in sets]
+        gk = make_graph(torch, fns)
+        us = time_graph(torch, gk, len(fns), max(2, 400 // len(fns)))
+        del gk
+        gbs = nbytes / us / 1e3
+        k = {"us": round(us, 3), "bytes": nbytes, "GB/s": round(gbs, 1),
+             "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "source_sha": source_sha(src)}
+        if flops:
+            k["TFLOP/s"] = round(flops / us / 1e6, 2)
+        kernels[name] = k
+    dom = max(kernels, key=lambda n: kernels[n]["us"])
+    dk = kernels[dom]
+    roofline = {"bound": "hbm", "achieved": dk["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": dk["frac_hbm"], "traffic": measured_traffic(dom, dk["source_sha"]),
+                "kernel": dom, "bytes_per_launch": dk["bytes"], "us_per_launch": dk["us"]}
+
+    line = {
+        "metric": METRIC,
+        "value": round(us_step, 3),
+        "unit": "µs/call",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": replays_warm * nsets,
+        "ms_per_step": round(us_step / 1000.0, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 norm, e4m3 x e4m3 -> f32 MFMA",
+        "data": "synthetic",
+        "config": {
+            "workload": f"mla_decode_step: fused dual RMSNorm + 1x128 FP8 group quant of M={M} tokens "
+                        f"(q [M,1536] and kv [M,512] as strided views of a [M,2048] bf16 buffer), then "
+                        f"block-scaled FP8 GEMMs with W_a [24576,1536] and W_b [8192,1536] sharing "
+                        f"the (q_fp8, scale) pair",
+            "M": M, "scale_layout": "column-major" if layout else "row-major",
+            "cache": "warm" if args.warm else f"cold ({nsets} rotating buffer sets, "
+                                              f"{nsets * step_bytes / 2**30:.2f} GiB)",
+            "timing": "HIP graph of one step per buffer set, replayed; HIP events",
+            "parallelism": "single GPU",
+        },
+        "roofline": roofline,
+        "kernels": kernels,
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", "?"),
+                   "cus": props.multi_processor_count},
+    }
+    if not args.no_sweep:
+        line["sweep"] = sweep(torch, np, mi, W, wa, wb, dev, cold=not args.warm)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(np, W, M, layout, wa, wb)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,155 @@
+/*
+ * mi_normquant.h -- C ABI of the MI355X (gfx950) library for the MLA decode
+ * hot path: fused dual RMSNorm + per-1x128 FP8 group quantisation of the q
+ * and kv latents, and the block-scaled FP8 GEMM that consumes the quantised
+ * q.
+ *
+ * Conventions shared by every entry point
+ *  - Every array argument is a DEVICE pointer owned by the caller.  The
+ *    library allocates nothing, keeps no state between calls, never
+ *    synchronises, and enqueues its work on `stream` (0 = the null stream).
+ *  - bf16 values are passed as uint16_t bit patterns, FP8 values as uint8_t
+ *    OCP e4m3fn codes (bias 7, largest finite 448 = 0x7E, 0x7F/0xFF NaN, no
+ *    infinities), scales as IEEE fp32.
+ *  - All checks run on the host before anything is enqueued; a non-MI_OK
+ *    status means nothing was enqueued (MI_ERR_HIP: the launch itself
+ *    failed).  M == 0 is a valid no-op.
+ *  - Inputs and outputs must not overlap (not checked).
+ *  - Two calls that write the same outputs must be ordered by the caller
+ *    (same stream or events); the kernels use no atomics, so repeated calls
+ *    on the same inputs give bit-identical outputs.
+ *
+ * Sources (web pages; title and section):
+ *  [PR53540] GitHub, vllm-project/vllm pull request #53540 "[ROCm][Perf]
+ *            Fuse SWA q/kv RMSNorm and q FP8 group quant for DeepSeek-V4",
+ *            section "Purpose".
+ *  [D53540]  PRHub digest of the same PR: "实现拆解" (implementation
+ *            breakdown) and the source excerpts of
+ *            _fused_mla_dual_rms_norm_group_quant_impl and
+ *            apply_pre_quantized_block_scaled_mm.
+ *  [D56433]  PRHub report of vLLM PR #56433 "[ROCm][Bugfix] Fix AITER
+ *            preshuffled FP8 block-scale kernel", "实现拆解" items 2 and 4.
+ *  [D27289]  PRHub digest of SGLang PR #27289, "功能与动机" (motivation) and
+ *            the aiter_w8a8_block_fp8_linear excerpt.
+ */
+#ifndef MI_NORMQUANT_H
+#define MI_NORMQUANT_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MI_OK = 0,
+    MI_ERR_NULL = 1,    /* a required pointer is NULL */
+    MI_ERR_SHAPE = 2,   /* a size is negative, not a multiple of 128 where one
+                           is required, or above a documented limit */
+    MI_ERR_STRIDE = 3,  /* a row stride is smaller than the row width */
+    MI_ERR_ALIGN = 4,   /* a GEMM operand is not 16-byte aligned */
+    MI_ERR_HIP = 5      /* the HIP launch reported an error */
+} mi_status;
+
+/* Quantisation group: one fp32 scale per 1 x 128 consecutive q elements. */
+#define MI_GROUP 128
+/* Largest supported widths of the fused norm-quant (one row per wavefront). */
+#define MI_MAX_NQ 4096
+#define MI_MAX_NKV 2048
+
+/*
+ * mi_fused_dual_rmsnorm_group_quant
+ *
+ * [PR53540] "Purpose" and [D53540] step 1: in one kernel launch, RMSNorm the
+ * q latent and the kv latent of each row with fp32 accumulation, quantise
+ * the normalised q per 1x128 group to FP8 with one fp32 scale per group
+ * straight from the fp32 values (a single rounding), and write kv as bf16.
+ * [D56433] item 4 and [D27289]: the scale layout is chosen by
+ * `transpose_scale` so that a consumer reading column-major scales needs no
+ * transpose copy.
+ *
+ * Per row m (x = q row, gamma = gamma_q; likewise for kv):
+ *   rstd   = 1 / sqrt(sum_i x_i^2 / Nq + eps)            (fp32 accumulation)
+ *   y_i    = x_i * rstd * gamma_i                         (fp32)
+ *   s_g    = max(max_{i in g} |y_i| / 448, 1e-12)         (fp32)
+ *   code_i = e4m3fn_rne(clamp(y_i / s_g, -448, 448))
+ *   kv_out = bf16_rne(x * rstd_kv * gamma_kv)
+ * s_g is the dequantisation multiplier: y_i ~= dec(code_i) * s_g.
+ *
+ * q, q_row_stride   [M, Nq] bf16, row m at q + m*q_row_stride (elements),
+ *                   inner stride 1; q_row_stride >= Nq.  May be a column
+ *                   slice of a wider fused projection buffer.
+ * kv, kv_row_stride [M, Nkv] bf16, same rules; kv_row_stride >= Nkv.
+ * gamma_q, gamma_kv [Nq], [Nkv] bf16 RMSNorm weights.
+ * eps               added to the mean of squares (same value for q and kv).
+ * M, Nq, Nkv        rows and widths: Nq % 128 == 0, 128 <= Nq <= MI_MAX_NQ,
+ *                   1 <= Nkv <= MI_MAX_NKV, M >= 0.
+ * transpose_scale   0: out_scale[m*G + g]; 1: out_scale[g*M + m], G = Nq/128
+ *                   (the [M, G] array stored column-major, leading dim M).
+ * out_q_fp8         [M, Nq] e4m3fn codes, contiguous.
+ * out_scale         M*G fp32 values in the layout above.
+ * out_kv            [M, Nkv] bf16, contiguous (whatever kv_row_stride is).
+ * Rows, strides and base addresses need no particular alignment; 16-byte
+ * aligned rows take the vector path.
+ */
+mi_status mi_fused_dual_rmsnorm_group_quant(
+    const uint16_t *q, int64_t q_row_stride,
+    const uint16_t *kv, int64_t kv_row_stride,
+    const uint16_t *gamma_q, const uint16_t *gamma_kv,
+    float eps, int64_t M, int64_t Nq, int64_t Nkv,
+    int transpose_scale,
+    uint8_t *out_q_fp8, float *out_scale, uint16_t *out_kv,
+    hipStream_t stream);
+
+/*
+ * mi_block_scaled_fp8_gemm
+ *
+ * [D53540] excerpt of apply_pre_quantized_block_scaled_mm: the linear's
+ * block-scaled GEMM is driven directly by the pre-quantised activation and
+ * its per-1x128 scales (A = x_fp8, B = weight, As = x_scale, Bs = the weight
+ * block scale, used as given), skipping a second quantisation of the input.
+ * [D27289] aiter_w8a8_block_fp8_linear excerpt: weight [N, K], bf16 output
+ * [M, N].  [D56433] item 2: a GEMM may read As column-major; row-major and
+ * column-major As have the same logical shape, so the layout is an explicit
+ * argument here, never inferred.
+ *
+ *   out[m, n] = bf16_rne( sum_{kb < K/128} As[m, kb] * Bs[n/128, kb]
+ *                         * sum_{k in block kb} dec(a[m, k]) * dec(w[n, k]) )
+ *   accumulated in fp32 on the matrix cores.
+ *
+ * a_fp8              [M, K] e4m3fn codes, contiguous, 16-byte aligned.
+ * a_scale            M*K/128 fp32: a_scale_transposed == 0 -> As[m*(K/128)
+ *                    + kb]; == 1 -> As[kb*M + m].
+ * w_fp8              [N, K] e4m3fn codes, row-major, 16-byte aligned.
+ * w_scale            [N/128, K/128] fp32, row-major.
+ * out_bf16           [M, N] bf16, contiguous, 16-byte aligned.
+ * M, N, K            M >= 0, N % 128 == 0, K % 128 == 0, N > 0, K > 0.
+ */
+mi_status mi_block_scaled_fp8_gemm(
+    const uint8_t *a_fp8, const float *a_scale, int a_scale_transposed,
+    const uint8_t *w_fp8, const float *w_scale,
+    uint16_t *out_bf16,
+    int64_t M, int64_t N, int64_t K,
+    hipStream_t stream);
+
+/*
+ * mi_negotiate_scale_layout
+ *
+ * [D56433] item 4: the producer writes one scale buffer for several
+ * consumers, so they must agree on its major order.  Returns 1 if every
+ * consumer wants column-major (transposed) scales, 0 if every one wants
+ * row-major, and -1 if they disagree or n <= 0 / the pointer is NULL (the
+ * caller then must not share one pre-quantised pair).  Host-only; touches
+ * no GPU.
+ */
+int mi_negotiate_scale_layout(const int *consumer_wants_transposed, int n);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *mi_status_string(mi_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MI_NORMQUANT_H */

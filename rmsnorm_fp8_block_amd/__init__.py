@@ -1,0 +1,21 @@
+"""MI355X (gfx950) library for the MLA decode hot path: fused dual RMSNorm +
+per-1x128 FP8 group quantisation of the q/kv latents, and the block-scaled
+FP8 GEMM that consumes the quantised q.
+
+The computation runs in HIP kernels behind the C ABI of
+``include/mi_normquant.h`` (``libmi_normquant.so``); the functions below are
+its ctypes binding.  ``workloads`` holds the seeded synthetic inputs.
+"""
+from ._binding import (  # noqa: F401
+    EXPORTED,
+    LIB_PATH,
+    MiError,
+    lib,
+    mi_block_scaled_fp8_gemm,
+    mi_fused_dual_rmsnorm_group_quant,
+    mi_negotiate_scale_layout,
+    mi_status_string,
+    prepare_block_scaled_fp8_gemm,
+    prepare_fused_dual_rmsnorm_group_quant,
+    scale_is_transposed,
+)

@@ -1,0 +1,233 @@
+"""Thin ctypes binding of ``libmi_normquant.so`` (the C ABI of
+``include/mi_normquant.h``).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of the library.  torch supplies device memory and the current
+stream.  If the library is not built the first call raises; there is no
+CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmi_normquant.so")
+GROUP = 128
+
+MI_OK, MI_ERR_NULL, MI_ERR_SHAPE, MI_ERR_STRIDE, MI_ERR_ALIGN, MI_ERR_HIP = range(6)
+
+EXPORTED = (
+    "mi_fused_dual_rmsnorm_group_quant",
+    "mi_block_scaled_fp8_gemm",
+    "mi_negotiate_scale_layout",
+    "mi_status_string",
+)
+
+
+class MiError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn}: {text}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with `python -m rmsnorm_fp8_block_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        p, i64, c_int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.mi_fused_dual_rmsnorm_group_quant.restype = c_int
+        L.mi_fused_dual_rmsnorm_group_quant.argtypes = [
+            p, i64, p, i64, p, p, ctypes.c_float, i64, i64, i64, c_int, p, p, p, p]
+        L.mi_block_scaled_fp8_gemm.restype = c_int
+        L.mi_block_scaled_fp8_gemm.argtypes = [p, p, c_int, p, p, p, i64, i64, i64, p]
+        L.mi_negotiate_scale_layout.restype = c_int
+        L.mi_negotiate_scale_layout.argtypes = [ctypes.POINTER(c_int), c_int]
+        L.mi_status_string.restype = ctypes.c_char_p
+        L.mi_status_string.argtypes = [c_int]
+        _lib = L
+    return _lib
+
+
+def mi_status_string(status: int) -> str:
+    return lib().mi_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != MI_OK:
+        raise MiError(fn, status, mi_status_string(status))
+
+
+def _stream(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _rows(t: torch.Tensor, name: str, dtype: torch.dtype) -> int:
+    """Row stride (elements) of a 2-D tensor with unit inner stride."""
+    if t.dim() != 2 or t.dtype != dtype:
+        raise ValueError(f"{name}: expected a 2-D {dtype} tensor, got {tuple(t.shape)} {t.dtype}")
+    if t.shape[0] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name}: inner stride must be 1, got {t.stride()}")
+    return t.stride(0) if t.shape[0] > 1 else t.shape[1]
+
+
+def mi_fused_dual_rmsnorm_group_quant(q: torch.Tensor, kv: torch.Tensor,
+                                      gamma_q: torch.Tensor, gamma_kv: torch.Tensor,
+                                      eps: float, transpose_scale: bool,
+                                      out_q: torch.Tensor | None = None,
+                                      out_scale: torch.Tensor | None = None,
+                                      out_kv: torch.Tensor | None = None):
+    """Fused dual RMSNorm + per-1x128 FP8 group quant on the current stream.
+
+    ``q`` [M, Nq] and ``kv`` [M, Nkv] are bf16 device tensors with unit inner
+    stride (split views of one fused buffer are fine).  Returns
+    ``(q_fp8, scale, kv_out)``: ``q_fp8`` uint8 e4m3fn codes [M, Nq],
+    ``scale`` fp32 with logical shape [M, Nq/128] whose strides give the
+    layout ((G, 1) row-major, or (1, M) when ``transpose_scale``), and
+    ``kv_out`` bf16 [M, Nkv], contiguous."""
+    qs = _rows(q, "q", torch.bfloat16)
+    ks = _rows(kv, "kv", torch.bfloat16)
+    M, Nq = q.shape
+    Nkv = kv.shape[1]
+    if kv.shape[0] != M:
+        raise ValueError("q and kv must have the same number of rows")
+    if gamma_q.dtype != torch.bfloat16 or gamma_kv.dtype != torch.bfloat16:
+        raise ValueError("gammas must be bf16")
+    if not (gamma_q.is_contiguous() and gamma_kv.is_contiguous()):
+        raise ValueError("gammas must be contiguous")
+    if gamma_q.numel() != Nq or gamma_kv.numel() != Nkv:
+        raise ValueError("gamma sizes must match the row widths")
+    G = Nq // GROUP
+    dev = q.device
+    if out_q is None:
+        out_q = torch.empty((M, Nq), dtype=torch.uint8, device=dev)
+    if out_scale is None:
+        out_scale = torch.empty(M * G, dtype=torch.float32, device=dev)
+    if out_kv is None:
+        out_kv = torch.empty((M, Nkv), dtype=torch.bfloat16, device=dev)
+    if not (out_q.is_contiguous() and out_kv.is_contiguous()):
+        raise ValueError("outputs must be contiguous")
+    if out_q.numel() < M * Nq or out_scale.numel() < M * G or out_kv.numel() < M * Nkv:
+        raise ValueError("output buffers too small")
+    status = lib().mi_fused_dual_rmsnorm_group_quant(
+        _ptr(q), qs, _ptr(kv), ks, _ptr(gamma_q), _ptr(gamma_kv), ctypes.c_float(eps),
+        M, Nq, Nkv, int(bool(transpose_scale)), _ptr(out_q), _ptr(out_scale), _ptr(out_kv),
+        _stream(q))
+    _check("mi_fused_dual_rmsnorm_group_quant", status)
+    flat = out_scale.reshape(-1)[:M * G]
+    scale = flat.as_strided((M, G), (1, M)) if transpose_scale else flat.view(M, G)
+    return out_q, scale, out_kv
+
+
+def scale_is_transposed(a_scale: torch.Tensor) -> bool:
+    """Layout of a [M, K/128] scale tensor, read from its strides."""
+    M, KB = a_scale.shape
+    if M == 1 or KB == 1:
+        return False          # both layouts hold the same bytes
+    if a_scale.stride() == (KB, 1):
+        return False
+    if a_scale.stride() == (1, M):
+        return True
+    raise ValueError(f"a_scale strides {a_scale.stride()} are neither row- nor column-major")
+
+
+def mi_block_scaled_fp8_gemm(a: torch.Tensor, a_scale: torch.Tensor,
+                             w: torch.Tensor, w_scale: torch.Tensor,
+                             out: torch.Tensor | None = None,
+                             a_scale_transposed: bool | None = None):
+    """Block-scaled FP8 GEMM on the current stream: ``a`` uint8 [M, K],
+    ``a_scale`` fp32 [M, K/128] (row- or column-major, read from its strides
+    unless ``a_scale_transposed`` is given and agrees), ``w`` uint8 [N, K],
+    ``w_scale`` fp32 [N/128, K/128].  Returns bf16 [M, N]."""
+    for name, t, dt in (("a", a, torch.uint8), ("w", w, torch.uint8),
+                        ("w_scale", w_scale, torch.float32), ("a_scale", a_scale, torch.float32)):
+        if t.dtype != dt or t.dim() != 2:
+            raise ValueError(f"{name}: expected a 2-D {dt} tensor")
+    if not (a.is_contiguous() and w.is_contiguous() and w_scale.is_contiguous()):
+        raise ValueError("a, w and w_scale must be contiguous")
+    M, K = a.shape
+    N = w.shape[0]
+    if w.shape[1] != K or tuple(a_scale.shape) != (M, K // GROUP) or \
+            tuple(w_scale.shape) != (N // GROUP, K // GROUP):
+        raise ValueError("shape mismatch between a, a_scale, w, w_scale")
+    layout = scale_is_transposed(a_scale)
+    if a_scale_transposed is not None and M > 1 and bool(a_scale_transposed) != layout:
+        raise ValueError("a_scale_transposed disagrees with the strides of a_scale")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    if out.dtype != torch.bfloat16 or not out.is_contiguous() or tuple(out.shape) != (M, N):
+        raise ValueError("out must be a contiguous bf16 [M, N] tensor")
+    status = lib().mi_block_scaled_fp8_gemm(
+        _ptr(a), _ptr(a_scale), int(layout), _ptr(w), _ptr(w_scale), _ptr(out), M, N, K, _stream(a))
+    _check("mi_block_scaled_fp8_gemm", status)
+    return out
+
+
+def mi_negotiate_scale_layout(consumer_wants_transposed) -> bool | None:
+    """True / False when every consumer wants column-major / row-major
+    scales, None when they disagree (do not share one quantised pair)."""
+    vals = [int(bool(v)) for v in consumer_wants_transposed]
+    arr = (ctypes.c_int * max(len(vals), 1))(*vals)
+    r = lib().mi_negotiate_scale_layout(arr, len(vals))
+    return None if r < 0 else bool(r)
+
+
+class PreparedCall:
+    """One entry point with its arguments marshalled once: calling it
+    enqueues the launch on torch's current stream of the tensors' device
+    (so it can be captured into a HIP graph) and raises on a non-zero
+    status.  The tensors must stay alive as long as the call is used."""
+
+    def __init__(self, name: str, args: tuple, keep: tuple, device):
+        self.name = name
+        self._fn = getattr(lib(), name)
+        self._args = args
+        self._keep = keep
+        self._device = device
+
+    def __call__(self) -> None:
+        st = self._fn(*self._args, ctypes.c_void_p(torch.cuda.current_stream(self._device).cuda_stream))
+        if st != MI_OK:
+            raise MiError(self.name, st, mi_status_string(st))
+
+
+def prepare_fused_dual_rmsnorm_group_quant(q, kv, gamma_q, gamma_kv, eps, transpose_scale,
+                                           out_q, out_scale, out_kv) -> PreparedCall:
+    """Marshal the arguments of mi_fused_dual_rmsnorm_group_quant once (same
+    rules as :func:`mi_fused_dual_rmsnorm_group_quant`; outputs required)."""
+    qs = _rows(q, "q", torch.bfloat16)
+    ks = _rows(kv, "kv", torch.bfloat16)
+    M, Nq = q.shape
+    Nkv = kv.shape[1]
+    G = Nq // GROUP
+    if out_q.numel() < M * Nq or out_scale.numel() < M * G or out_kv.numel() < M * Nkv:
+        raise ValueError("output buffers too small")
+    args = (_ptr(q), qs, _ptr(kv), ks, _ptr(gamma_q), _ptr(gamma_kv), ctypes.c_float(eps),
+            M, Nq, Nkv, int(bool(transpose_scale)), _ptr(out_q), _ptr(out_scale), _ptr(out_kv))
+    return PreparedCall("mi_fused_dual_rmsnorm_group_quant", args,
+                        (q, kv, gamma_q, gamma_kv, out_q, out_scale, out_kv), q.device)
+
+
+def prepare_block_scaled_fp8_gemm(a, a_scale, w, w_scale, out) -> PreparedCall:
+    """Marshal the arguments of mi_block_scaled_fp8_gemm once; the As layout
+    is read from the strides of ``a_scale`` ([M, K/128])."""
+    M, K = a.shape
+    N = w.shape[0]
+    if tuple(a_scale.shape) != (M, K // GROUP) or tuple(out.shape) != (M, N):
+        raise ValueError("shape mismatch")
+    args = (_ptr(a), _ptr(a_scale), int(scale_is_transposed(a_scale)), _ptr(w), _ptr(w_scale),
+            _ptr(out), M, N, K)
+    return PreparedCall("mi_block_scaled_fp8_gemm", args, (a, a_scale, w, w_scale, out), a.device)

@@ -1,0 +1,104 @@
+// api.cpp -- the C ABI declared in include/mi_normquant.h: argument
+// validation on the host, then one kernel launch on the caller's stream.
+#include "mi_normquant.h"
+
+#include "launch.h"
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+}  // namespace
+
+extern "C" mi_status mi_fused_dual_rmsnorm_group_quant(
+    const uint16_t *q, int64_t q_row_stride,
+    const uint16_t *kv, int64_t kv_row_stride,
+    const uint16_t *gamma_q, const uint16_t *gamma_kv,
+    float eps, int64_t M, int64_t Nq, int64_t Nkv,
+    int transpose_scale,
+    uint8_t *out_q_fp8, float *out_scale, uint16_t *out_kv,
+    hipStream_t stream) {
+    if (M < 0 || Nq < MI_GROUP || Nq > MI_MAX_NQ || (Nq % MI_GROUP) != 0 || Nkv < 1 ||
+        Nkv > MI_MAX_NKV)
+        return MI_ERR_SHAPE;
+    if (M == 0)
+        return MI_OK;
+    if (!q || !kv || !gamma_q || !gamma_kv || !out_q_fp8 || !out_scale || !out_kv)
+        return MI_ERR_NULL;
+    if (q_row_stride < Nq || kv_row_stride < Nkv)
+        return MI_ERR_STRIDE;
+
+    mi::NormQuantParams p;
+    p.q = q;
+    p.q_stride = q_row_stride;
+    p.kv = kv;
+    p.kv_stride = kv_row_stride;
+    p.gamma_q = gamma_q;
+    p.gamma_kv = gamma_kv;
+    p.eps = eps;
+    p.M = M;
+    p.Nq = static_cast<int>(Nq);
+    p.Nkv = static_cast<int>(Nkv);
+    p.transpose_scale = transpose_scale ? 1 : 0;
+    p.out_q = out_q_fp8;
+    p.out_scale = out_scale;
+    p.out_kv = out_kv;
+    return mi::launch_normquant(p, stream) == hipSuccess ? MI_OK : MI_ERR_HIP;
+}
+
+extern "C" mi_status mi_block_scaled_fp8_gemm(
+    const uint8_t *a_fp8, const float *a_scale, int a_scale_transposed,
+    const uint8_t *w_fp8, const float *w_scale,
+    uint16_t *out_bf16,
+    int64_t M, int64_t N, int64_t K,
+    hipStream_t stream) {
+    if (M < 0 || N <= 0 || K <= 0 || (N % MI_GROUP) != 0 || (K % MI_GROUP) != 0)
+        return MI_ERR_SHAPE;
+    if (M == 0)
+        return MI_OK;
+    if (!a_fp8 || !a_scale || !w_fp8 || !w_scale || !out_bf16)
+        return MI_ERR_NULL;
+    if (!aligned16(a_fp8) || !aligned16(w_fp8) || !aligned16(out_bf16) ||
+        (reinterpret_cast<uintptr_t>(a_scale) & 3) || (reinterpret_cast<uintptr_t>(w_scale) & 3))
+        return MI_ERR_ALIGN;
+
+    mi::GemmParams p;
+    p.a = a_fp8;
+    p.a_scale = a_scale;
+    p.a_scale_transposed = a_scale_transposed ? 1 : 0;
+    p.w = w_fp8;
+    p.w_scale = w_scale;
+    p.out = out_bf16;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    return mi::launch_block_scaled_gemm(p, stream) == hipSuccess ? MI_OK : MI_ERR_HIP;
+}
+
+extern "C" int mi_negotiate_scale_layout(const int *consumer_wants_transposed, int n) {
+    if (!consumer_wants_transposed || n <= 0)
+        return -1;
+    const int first = consumer_wants_transposed[0] ? 1 : 0;
+    for (int i = 1; i < n; ++i)
+        if ((consumer_wants_transposed[i] ? 1 : 0) != first)
+            return -1;
+    return first;
+}
+
+extern "C" const char *mi_status_string(mi_status s) {
+    switch (s) {
+    case MI_OK:
+        return "MI_OK";
+    case MI_ERR_NULL:
+        return "MI_ERR_NULL: a required pointer is NULL";
+    case MI_ERR_SHAPE:
+        return "MI_ERR_SHAPE: unsupported size";
+    case MI_ERR_STRIDE:
+        return "MI_ERR_STRIDE: row stride smaller than the row width";
+    case MI_ERR_ALIGN:
+        return "MI_ERR_ALIGN: operand not 16-byte aligned";
+    case MI_ERR_HIP:
+        return "MI_ERR_HIP: kernel launch failed";
+    }
+    return "unknown mi_status";
+}

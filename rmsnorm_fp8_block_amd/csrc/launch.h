@@ -1,0 +1,43 @@
+// launch.h -- host-side launchers behind the C ABI (internal).  Arguments
+// have been validated by the caller; these only pick a kernel variant and a
+// grid and enqueue it.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace mi {
+
+struct NormQuantParams {
+    const uint16_t *q;
+    int64_t q_stride;
+    const uint16_t *kv;
+    int64_t kv_stride;
+    const uint16_t *gamma_q;
+    const uint16_t *gamma_kv;
+    float eps;
+    int64_t M;
+    int Nq;
+    int Nkv;
+    int transpose_scale;
+    uint8_t *out_q;
+    float *out_scale;
+    uint16_t *out_kv;
+};
+
+struct GemmParams {
+    const uint8_t *a;
+    const float *a_scale;
+    int a_scale_transposed;
+    const uint8_t *w;
+    const float *w_scale;
+    uint16_t *out;
+    int64_t M;
+    int64_t N;
+    int64_t K;
+};
+
+hipError_t launch_normquant(const NormQuantParams &p, hipStream_t stream);
+hipError_t launch_block_scaled_gemm(const GemmParams &p, hipStream_t stream);
+
+}  // namespace mi

@@ -1,0 +1,115 @@
+"""CPU checks of the C ABI: the library loads, exports every function that
+``include/*.h`` declares, rejects invalid arguments on the host before
+anything is enqueued (no GPU needed: these calls return before any HIP
+call), and negotiates the scale layout between consumers (a host-only
+helper; PRHub report of vLLM PR #56433, item 4)."""
+import ctypes
+import glob
+import os
+import re
+import subprocess
+
+import pytest
+
+import rmsnorm_fp8_block_amd as mi
+from rmsnorm_fp8_block_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(mi_\w+)\s*\(", text, re.M))
+    return names
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail(f"{B.LIB_PATH} not built (run `python -m rmsnorm_fp8_block_amd.build`)")
+    return mi.lib()
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == set(B.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(L, name)
+
+
+def test_status_strings(L):
+    for s in range(6):
+        assert mi.mi_status_string(s).startswith(("MI_OK", "MI_ERR"))
+    assert mi.mi_status_string(99) == "unknown mi_status"
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+NULL = ctypes.c_void_p(0)
+
+
+def nq(L, **kw):
+    a = dict(q=FAKE, qs=1536, kv=FAKE, ks=512, gq=FAKE, gk=FAKE, eps=1e-6, M=4, Nq=1536,
+             Nkv=512, t=0, oq=FAKE, os_=FAKE, okv=FAKE)
+    a.update(kw)
+    return L.mi_fused_dual_rmsnorm_group_quant(a["q"], a["qs"], a["kv"], a["ks"], a["gq"], a["gk"],
+                                               ctypes.c_float(a["eps"]), a["M"], a["Nq"], a["Nkv"],
+                                               a["t"], a["oq"], a["os_"], a["okv"], NULL)
+
+
+def test_normquant_validation(L):
+    assert nq(L, M=-1) == B.MI_ERR_SHAPE
+    assert nq(L, Nq=1500) == B.MI_ERR_SHAPE          # not a multiple of 128
+    assert nq(L, Nq=0) == B.MI_ERR_SHAPE
+    assert nq(L, Nq=4096 + 128) == B.MI_ERR_SHAPE
+    assert nq(L, Nkv=0) == B.MI_ERR_SHAPE
+    assert nq(L, Nkv=2049) == B.MI_ERR_SHAPE
+    assert nq(L, M=0) == B.MI_OK                      # no-op, nothing enqueued
+    assert nq(L, M=0, q=NULL, oq=NULL) == B.MI_OK
+    for k in ("q", "kv", "gq", "gk", "oq", "os_", "okv"):
+        assert nq(L, **{k: NULL}) == B.MI_ERR_NULL, k
+    assert nq(L, qs=1535) == B.MI_ERR_STRIDE
+    assert nq(L, ks=511) == B.MI_ERR_STRIDE
+
+
+def gemm(L, **kw):
+    a = dict(a=FAKE, As=FAKE, t=0, w=FAKE, Bs=FAKE, out=FAKE, M=4, N=1024, K=1536)
+    a.update(kw)
+    return L.mi_block_scaled_fp8_gemm(a["a"], a["As"], a["t"], a["w"], a["Bs"], a["out"],
+                                      a["M"], a["N"], a["K"], NULL)
+
+
+def test_gemm_validation(L):
+    assert gemm(L, M=-1) == B.MI_ERR_SHAPE
+    assert gemm(L, N=1000) == B.MI_ERR_SHAPE
+    assert gemm(L, K=1000) == B.MI_ERR_SHAPE
+    assert gemm(L, N=0) == B.MI_ERR_SHAPE
+    assert gemm(L, M=0) == B.MI_OK
+    for k in ("a", "As", "w", "Bs", "out"):
+        assert gemm(L, **{k: NULL}) == B.MI_ERR_NULL, k
+    assert gemm(L, a=ctypes.c_void_p(0x1008)) == B.MI_ERR_ALIGN
+    assert gemm(L, w=ctypes.c_void_p(0x1004)) == B.MI_ERR_ALIGN
+    assert gemm(L, out=ctypes.c_void_p(0x1002)) == B.MI_ERR_ALIGN
+    assert gemm(L, As=ctypes.c_void_p(0x1002)) == B.MI_ERR_ALIGN
+
+
+def test_negotiate_scale_layout(L):
+    assert mi.mi_negotiate_scale_layout([1, 1]) is True
+    assert mi.mi_negotiate_scale_layout([0, 0, 0]) is False
+    assert mi.mi_negotiate_scale_layout([1, 0]) is None
+    assert mi.mi_negotiate_scale_layout([]) is None
+    assert L.mi_negotiate_scale_layout(None, 2) == -1
+    assert mi.mi_negotiate_scale_layout([5, 1]) is True    # any non-zero means "transposed"
+
+
+def test_binding_raises_on_error_status():
+    with pytest.raises(mi.MiError) as e:
+        B._check("x", B.MI_ERR_SHAPE)
+    assert e.value.status == B.MI_ERR_SHAPE

@@ -1,0 +1,188 @@
+"""GPU parity of the fused dual RMSNorm + per-1x128 FP8 group quant (HIP,
+gfx950) against the CPU oracle, through the C ABI.
+
+Cases follow the workloads (single-token decode, strided split views of the
+fused projection buffer, outliers with zero groups and column-major scales,
+8192-token prefill in both layouts) plus tiny / ragged / unaligned shapes on
+the kernel's generic path and an exhaustive check of the device e4m3fn
+conversion.  Bar: codes within 1 e4m3 ULP and >= 99.9 % identical (and any
+mismatch only next to a rounding midpoint of the oracle's exact y/s), scales
+within 1e-6 relative, kv within 1 bf16 ULP.  Self-consistency (strided ==
+contiguous, repeat runs, M = 1 layouts, column-major == transposed
+row-major) is bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rmsnorm_fp8_block_amd as mi
+from rmsnorm_fp8_block_amd import workloads as W
+
+from helpers import (compare_normquant, dev_u16_as_bf16, gpu_or_skip, host_bf16_bits,
+                     run_oracle_case, scale_buffer)
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_run(case, transpose, dev, contiguous=False):
+    """Upload the case (keeping split views as views of one device buffer)
+    and run the HIP kernel."""
+    if case.buffer is not None and not contiguous:
+        buf = dev_u16_as_bf16(case.buffer, dev)
+        nq = case.q.shape[1]
+        q, kv = buf[:, :nq], buf[:, nq:]
+    else:
+        q = dev_u16_as_bf16(case.q, dev)
+        kv = dev_u16_as_bf16(case.kv, dev)
+    gq = dev_u16_as_bf16(case.gamma_q, dev)
+    gk = dev_u16_as_bf16(case.gamma_kv, dev)
+    codes, scale, kv_out = mi.mi_fused_dual_rmsnorm_group_quant(q, kv, gq, gk, case.eps, transpose)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), scale_buffer(scale), host_bf16_bits(kv_out)
+
+
+WORKLOADS = {
+    "decode_M1": lambda: W.decode_single(),
+    "strided_M64": lambda: W.strided_batch(64),
+    "outliers_M256": lambda: W.outlier_stress(256),
+    "prefill_M8192": lambda: W.prefill(8192),
+}
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_workload_parity(name):
+    dev = gpu_or_skip()
+    case = WORKLOADS[name]()
+    for t in case.layouts:
+        ref = run_oracle_case(case, t)
+        got = gpu_run(case, t, dev)
+        stats = compare_normquant(*got, ref, label=f"{name} transpose={t}")
+        print(f"{name} transpose={t}: {stats}")
+
+
+def test_m1_layouts_identical_and_colmajor_is_transpose():
+    dev = gpu_or_skip()
+    one = W.decode_single()
+    a = gpu_run(one, 0, dev)
+    b = gpu_run(one, 1, dev)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    case = W.strided_batch(64)
+    r = gpu_run(case, 0, dev)
+    c = gpu_run(case, 1, dev)
+    assert np.array_equal(c[1], r[1].reshape(64, 12).T.reshape(-1))
+    assert np.array_equal(c[0], r[0]) and np.array_equal(c[2], r[2])
+
+
+def test_strided_views_equal_contiguous_and_repeat_runs():
+    dev = gpu_or_skip()
+    case = W.strided_batch(64)
+    s = gpu_run(case, 0, dev)
+    c = gpu_run(case, 0, dev, contiguous=True)
+    s2 = gpu_run(case, 0, dev)
+    for x, y, z in zip(s, c, s2):
+        assert np.array_equal(x, y) and np.array_equal(x, z)
+
+
+def _case(q, kv, gq, gk, eps=W.EPS, name="adhoc"):
+    return W.NormQuantCase(name, q, kv, gq, gk, eps=eps)
+
+
+@pytest.mark.parametrize("M,Nq,Nkv,seed", [(1, 128, 8, 1), (3, 256, 64, 2), (2, 128, 40, 3),
+                                           (7, 640, 100, 4), (5, 4096, 2048, 5), (9, 1536, 512, 6),
+                                           (33, 1536, 576, 7)])
+def test_generic_shapes(M, Nq, Nkv, seed):
+    """Tiny, ragged (partial 512-chunks, Nkv % 8 != 0, M not a multiple of
+    the 4 rows per block) and largest supported widths."""
+    dev = gpu_or_skip()
+    r = np.random.default_rng(seed)
+    q = W.f32_to_bf16_bits(r.standard_normal((M, Nq)).astype(np.float32))
+    kv = W.f32_to_bf16_bits(r.standard_normal((M, Nkv)).astype(np.float32))
+    gq = W.f32_to_bf16_bits((1 + 0.1 * r.standard_normal(Nq)).astype(np.float32))
+    gk = W.f32_to_bf16_bits((1 + 0.1 * r.standard_normal(Nkv)).astype(np.float32))
+    case = _case(q, kv, gq, gk)
+    for t in (0, 1):
+        ref = run_oracle_case(case, t)
+        compare_normquant(*gpu_run(case, t, dev), ref, label=f"M{M} Nq{Nq} Nkv{Nkv} t{t}")
+
+
+def test_unaligned_rows_take_the_scalar_path():
+    """Row stride 2049 and a kv view starting at an odd element: no 16-byte
+    alignment anywhere; results must still match the oracle and equal the
+    aligned run bit for bit."""
+    dev = gpu_or_skip()
+    M = 10
+    r = np.random.default_rng(8)
+    wide = W.f32_to_bf16_bits(r.standard_normal((M, 2049)).astype(np.float32))
+    q_np, kv_np = wide[:, :1536], wide[:, 1537:2049]
+    gq, gk = W.gammas()
+    case = _case(q_np, kv_np, gq, gk)
+    buf = dev_u16_as_bf16(wide, dev)
+    q, kv = buf[:, :1536], buf[:, 1537:2049]
+    for t in (0, 1):
+        codes, scale, kvo = mi.mi_fused_dual_rmsnorm_group_quant(
+            q, kv, dev_u16_as_bf16(gq, dev), dev_u16_as_bf16(gk, dev), W.EPS, t)
+        got = (codes.cpu().numpy(), scale_buffer(scale), host_bf16_bits(kvo))
+        ref = run_oracle_case(case, t)
+        compare_normquant(*got, ref, label=f"unaligned t{t}")
+        aligned = gpu_run(_case(np.ascontiguousarray(q_np), np.ascontiguousarray(kv_np), gq, gk), t, dev)
+        for x, y in zip(got, aligned):
+            assert np.array_equal(x, y)
+
+
+def exhaustive_bf16_rows():
+    """Every bf16 magnitude in [2^-20, 448] with both signs, packed into rows
+    of 12 groups; element 0 of every group is 448, so with gamma = 1 the
+    group's scale is rstd and y/s equals x exactly (see the eps choice)."""
+    vals = []
+    for b in range(0x0000, 0x7F80):
+        v = oracle.bf16_decode(b)
+        if 2.0 ** -20 <= v <= 448.0:
+            vals += [b, b | 0x8000]
+    vals.append(0)
+    per_row = 12 * 127
+    rows = (len(vals) + per_row - 1) // per_row
+    vals += [0] * (rows * per_row - len(vals))
+    v = np.array(vals, np.uint16).reshape(rows, 12, 127)
+    q = np.empty((rows, 12, 128), np.uint16)
+    q[:, :, 0] = W.f32_to_bf16_bits(np.array([448.0], np.float32))[0]
+    q[:, :, 1:] = v
+    return q.reshape(rows, 1536)
+
+
+def test_device_e4m3_conversion_exhaustive():
+    """eps = 2^72 swamps the mean of squares (< 2^18) in both fp32 and fp64,
+    so rstd = 2^-36 exactly on both sides, y = x * 2^-36, amax = 448 * 2^-36,
+    s = 2^-36 (above the 1e-12 floor) and y/s = x: every code is a single
+    rounding of a bf16 value, midpoints and subnormals included, so GPU and
+    oracle must agree bit for bit; kv = x * 2^-36 exactly."""
+    dev = gpu_or_skip()
+    q = exhaustive_bf16_rows()
+    M = q.shape[0]
+    kv = q[:, :512].copy()
+    one = np.float32(1.0)
+    gq = W.f32_to_bf16_bits(np.full(1536, one))
+    gk = W.f32_to_bf16_bits(np.full(512, one))
+    eps = float(np.float32(2.0 ** 72))
+    case = _case(q, kv, gq, gk, eps=eps)
+    for t in (0, 1):
+        ref = run_oracle_case(case, t)
+        assert np.all(ref["scale"] == np.float32(2.0 ** -36))
+        got = gpu_run(case, t, dev)
+        assert np.array_equal(got[0], ref["q"]), "device e4m3 conversion differs from RNE"
+        assert np.array_equal(got[1], ref["scale"])
+        assert np.array_equal(got[2], ref["kv"])
+    # and the codes are torch's RNE cast of the bf16 values themselves
+    x = torch.from_numpy(q.view(np.int16)).view(torch.bfloat16).float().clamp(-448, 448)
+    assert np.array_equal(got[0], x.to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+
+
+def test_zero_rows_is_a_noop():
+    dev = gpu_or_skip()
+    q = torch.zeros((0, 1536), dtype=torch.bfloat16, device=dev)
+    kv = torch.zeros((0, 512), dtype=torch.bfloat16, device=dev)
+    g = torch.ones(1536, dtype=torch.bfloat16, device=dev)
+    gk = torch.ones(512, dtype=torch.bfloat16, device=dev)
+    codes, scale, kvo = mi.mi_fused_dual_rmsnorm_group_quant(q, kv, g, gk, W.EPS, False)
+    assert codes.shape == (0, 1536) and scale.shape == (0, 12) and kvo.shape == (0, 512)
