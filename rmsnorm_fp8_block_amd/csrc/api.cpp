@@ -36,6 +36,8 @@ extern "C" mi_status mi_fused_dual_rmsnorm_group_quant(
     p.gamma_q = gamma_q;
     p.gamma_kv = gamma_kv;
     p.eps = eps;
+    p.inv_nq = static_cast<float>(1.0 / static_cast<double>(Nq));
+    p.inv_nkv = static_cast<float>(1.0 / static_cast<double>(Nkv));
     p.M = M;
     p.Nq = static_cast<int>(Nq);
     p.Nkv = static_cast<int>(Nkv);

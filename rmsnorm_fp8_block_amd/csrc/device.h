@@ -73,11 +73,20 @@ __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float 
     return static_cast<uint32_t>(w);
 }
 
-// Two fp32 -> two bf16 (RNE), first value in the low half.
+typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
+typedef float v2f32 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> two bf16 (RNE, one packed convert), first value in the low half.
 __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
-    const uint32_t lo = __builtin_bit_cast(uint16_t, static_cast<__bf16>(a));
-    const uint32_t hi = __builtin_bit_cast(uint16_t, static_cast<__bf16>(b));
-    return lo | (hi << 16);
+    const v2f32 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, v2bf16));
+}
+
+// Products of packed bf16 pairs, exact in fp32: dot2(x, g masked to one
+// half) = x_lo * g_lo (or x_hi * g_hi) + 0.
+__device__ __forceinline__ float bf16_dot2(uint32_t x, uint32_t y, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf16, x), __builtin_bit_cast(v2bf16, y), acc,
+                                          false);
 }
 
 // Workgroups are dealt round-robin over the 8 XCDs.  Renumber them so that

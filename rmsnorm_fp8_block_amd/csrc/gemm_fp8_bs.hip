@@ -31,6 +31,8 @@
 // The K order inside one MFMA is irrelevant to the result as long as both
 // operands use the same one; both are loaded with the same lane/byte -> k
 // assignment.
+#include <algorithm>
+
 #include "device.h"
 #include "launch.h"
 
@@ -152,6 +154,253 @@ __global__ __launch_bounds__(256) void block_scaled_fp8_gemm_kernel(GemmParams p
     }
 }
 
+// ---------------------------------------------------------------------------
+// Weight-streaming variant (M <= 256, K/128 = kKB known at compile time).
+// Each wave owns one 16-row weight subtile and loads all kKB K-blocks of it
+// with one burst of 16-byte loads (24 KB in flight per wave at K = 1536),
+// so the whole weight matrix is read from HBM once, in a single round trip
+// spread over every CU.  The activations are processed in chunks of up to
+// 64 rows: the block stages a chunk (in fragment order) and its scales in
+// LDS with direct global -> LDS loads, then every wave multiplies it with
+// the weight fragments it keeps in registers.
+//
+// Ordering: the first chunk's LDS loads are issued before the weight burst,
+// and before the barrier each wave waits only until those have landed
+// (loads complete in issue order), so the MFMAs start while the weight
+// K-blocks are still arriving.
+// ---------------------------------------------------------------------------
+constexpr int kStreamMaxWaves = 8;
+constexpr int kChunkRows = 64;
+
+// vmcnt-only waits (gfx9 encoding: vmcnt[3:0] + vmcnt[5:4] at bits 15:14,
+// expcnt 6:4 and lgkmcnt 11:8 left at their maxima = no wait)
+template <int kVm>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(kVm >= 0 && kVm < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((kVm & 15) | ((kVm >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int kMT, int kKB>
+__device__ __forceinline__ void stage_chunk(const GemmParams &p, int64_t m0, uint4 *s_act, float *s_as,
+                                           int wave, int waves, int lane) {
+    const int64_t M = p.M, K = p.K;
+    // Every block reads the same (small) activation rows.  Each block starts
+    // at a different slab so that, at any moment, the CUs ask for different
+    // cache lines instead of queueing on the same L2 channel.
+    constexpr int kSlabs = kKB * kMT * 2;
+    const int rot = static_cast<int>((blockIdx.x * 7u) % kSlabs);
+    // Slab i = (kb * kMT + mt) * 2 + h of the fragment layout is 64 lanes x
+    // 16 bytes; one global_load_lds_dwordx4 fills it, lane L fetching bytes
+    // [kb*128 + 32*(L/16) + 16*h, +16) of activation row m0 + mt*16 + L%16.
+    // Rows at or beyond M repeat row M-1: they only feed output columns that
+    // are never stored.
+    for (int j = wave; j < kSlabs; j += waves) {
+        const int i = (j + rot) % kSlabs;
+        const int h = i & 1, mt = (i >> 1) % kMT, kb = (i >> 1) / kMT;
+        const int64_t r = min<int64_t>(m0 + mt * 16 + (lane & 15), M - 1);
+        const uint8_t *src = p.a + r * K + kb * kBlk + 32 * (lane >> 4) + 16 * h;
+        __builtin_amdgcn_global_load_lds(src, s_act + i * kWave, 16, 0, 0);
+    }
+    // activation scales: one 4-byte direct load per K-block, lane = row
+    const int krot = static_cast<int>((blockIdx.x * 5u) % kKB);
+    for (int j = wave; j < kKB; j += waves) {
+        const int kb = (j + krot) % kKB;
+        const int64_t r = min<int64_t>(m0 + lane, M - 1);
+        const float *src = p.a_scale_transposed ? p.a_scale + static_cast<int64_t>(kb) * M + r
+                                                : p.a_scale + r * kKB + kb;
+        __builtin_amdgcn_global_load_lds(src, s_as + kb * kWave, 4, 0, 0);
+    }
+}
+
+// One 64-row chunk: each wave multiplies the staged activations with its
+// weight fragments and writes its 16 output columns of the chunk's rows.
+template <int kMT, int kKB>
+__device__ __forceinline__ void compute_chunk(const GemmParams &p, int64_t m0, int64_t n0, int lane,
+                                              const uint4 *s_act, const float *s_as,
+                                              const v8i (&wf)[kKB], const float (&bs)[kKB]) {
+    v4f acc[kMT];
+#pragma unroll
+    for (int t = 0; t < kMT; ++t)
+        acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    // Pipeline: the MFMAs of K-block kb+1 are issued before the scale FMAs
+    // of K-block kb (so the FMAs' wait for the matrix-core results overlaps
+    // the next MFMAs), and the activation fragments and scales are read from
+    // LDS two K-blocks ahead.  The empty asm statements pin that order: the
+    // compiler would otherwise be free to issue every MFMA first and keep all
+    // partial results live, which does not fit next to the weight burst.
+    auto frag = [&](int kb, int t, uint4 &lo, uint4 &hi, float &as) {
+        lo = s_act[((kb * kMT + t) * 2 + 0) * kWave + lane];
+        hi = s_act[((kb * kMT + t) * 2 + 1) * kWave + lane];
+        as = s_as[kb * kWave + t * 16 + (lane & 15)];
+    };
+    uint4 lo[kMT], hi[kMT];     // fragments of the next K-block to multiply
+    float as_m[kMT];
+    v4f part[kMT];              // MFMA results of the K-block being folded
+    float sc[kMT];
+#pragma unroll
+    for (int t = 0; t < kMT; ++t) {
+        uint4 l0, h0;
+        float a0;
+        frag(0, t, l0, h0, a0);
+        part[t] = mfma_e4m3_16x16x128(wf[0], join(l0, h0));
+        sc[t] = a0 * bs[0];
+    }
+    if (kKB > 1) {
+#pragma unroll
+        for (int t = 0; t < kMT; ++t)
+            frag(1, t, lo[t], hi[t], as_m[t]);
+    }
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb) {
+        v4f next[kMT];
+        float nsc[kMT];
+        if (kb + 1 < kKB) {
+#pragma unroll
+            for (int t = 0; t < kMT; ++t) {
+                next[t] = mfma_e4m3_16x16x128(wf[kb + 1], join(lo[t], hi[t]));
+                nsc[t] = as_m[t] * bs[kb + 1];
+            }
+            if (kb + 2 < kKB) {
+#pragma unroll
+                for (int t = 0; t < kMT; ++t)
+                    frag(kb + 2, t, lo[t], hi[t], as_m[t]);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < kMT; ++t) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[t][i] = fmaf(part[t][i], sc[t], acc[t][i]);
+            if (kb + 1 < kKB) {
+                part[t] = next[t];
+                sc[t] = nsc[t];
+            }
+            asm volatile("" : "+v"(acc[t]), "+v"(part[t]), "+v"(lo[t].x), "+v"(lo[t].y), "+v"(lo[t].z),
+                         "+v"(lo[t].w), "+v"(hi[t].x), "+v"(hi[t].y), "+v"(hi[t].z), "+v"(hi[t].w),
+                         "+v"(as_m[t]));
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < kMT; ++t) {
+        const int64_t m = m0 + t * 16 + (lane & 15);
+        if (m < p.M) {
+            const int64_t n = n0 + 4 * (lane >> 4);
+            *reinterpret_cast<uint2 *>(p.out + m * p.N + n) =
+                make_uint2(pack2_bf16(acc[t][0], acc[t][1]), pack2_bf16(acc[t][2], acc[t][3]));
+        }
+    }
+}
+
+template <int kMT, int kKB>
+__global__ __launch_bounds__(kStreamMaxWaves * kWave) void block_scaled_fp8_gemm_stream_kernel(
+    GemmParams p, int subtiles_per_block) {
+    extern __shared__ uint4 s_dyn[];
+    uint4 *s_act = s_dyn;                                                   // [kb][mt][half][lane]
+    float *s_as = reinterpret_cast<float *>(s_dyn + kKB * kMT * 2 * kWave);  // [kb][64 rows]
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: scalar addressing
+    const int waves = blockDim.x / kWave;
+    const int64_t M = p.M, K = p.K;
+    const int64_t S = p.N / 16;  // 16-row weight subtiles
+    const int64_t st = static_cast<int64_t>(blockIdx.x) * subtiles_per_block + wave;
+    const bool active = wave < subtiles_per_block && st < S;
+    const int64_t n0 = st * 16;
+
+    float bs[kKB];  // the subtile's weight scales (one 128-row block)
+    if (active) {
+        const float *bs_row = p.w_scale + (n0 / kBlk) * kKB;
+#pragma unroll
+        for (int kb = 0; kb < kKB; ++kb)
+            bs[kb] = bs_row[kb];
+    }
+    stage_chunk<kMT, kKB>(p, 0, s_act, s_as, wave, waves, lane);
+    // The fences keep the program order of the memory operations: scales and
+    // staging loads, then the weight burst, then the wait.  Loads complete in
+    // issue order, so waiting until only the burst is outstanding means this
+    // wave's staging loads have landed in LDS.
+    asm volatile("" ::: "memory");
+    v8i wf[kKB];
+    if (active) {
+        const uint8_t *wrow = p.w + (n0 + (lane & 15)) * K + 32 * (lane >> 4);
+#pragma unroll
+        for (int kb = 0; kb < kKB; ++kb) {
+            const uint4 *src = reinterpret_cast<const uint4 *>(wrow + kb * kBlk);
+            wf[kb] = join(src[0], src[1]);
+        }
+        asm volatile("" ::: "memory");
+        wait_vmcnt<2 * kKB>();
+    } else {
+        wait_vmcnt<0>();
+    }
+    // A bare barrier: the LDS data is visible once every wave's own staging
+    // loads have landed (waited for above).  __syncthreads() would add a
+    // release fence that drains the whole weight burst first.
+    __builtin_amdgcn_s_barrier();
+    if (active)
+        compute_chunk<kMT, kKB>(p, 0, n0, lane, s_act, s_as, wf, bs);
+
+    for (int64_t m0 = kChunkRows; m0 < M; m0 += kChunkRows) {
+        __syncthreads();  // every wave is done reading the previous chunk
+        stage_chunk<kMT, kKB>(p, m0, s_act, s_as, wave, waves, lane);
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (active)
+            compute_chunk<kMT, kKB>(p, m0, n0, lane, s_act, s_as, wf, bs);
+    }
+}
+
+int device_cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+template <int kMT, int kKB>
+hipError_t launch_stream(const GemmParams &p, hipStream_t stream) {
+    // one subtile per wave, at most 8 waves per block, at least one block per CU
+    const int64_t S = p.N / 16;
+    const int64_t cus = device_cu_count();
+    int spb = static_cast<int>(std::min<int64_t>(kStreamMaxWaves, (S + cus - 1) / cus));
+    const int64_t blocks = (S + spb - 1) / spb;
+    if (blocks > 0x7FFFFFFF)
+        return hipErrorInvalidValue;
+    const int waves = std::max(4, spb);  // spare waves only help stage the activations
+    const size_t lds = static_cast<size_t>(kKB) * kMT * 2 * kWave * sizeof(uint4) +
+                       static_cast<size_t>(kKB) * kWave * sizeof(float);
+    auto kern = block_scaled_fp8_gemm_stream_kernel<kMT, kKB>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+        if (e != hipSuccess)
+            return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(waves * kWave), lds, stream, p, spb);
+    return hipGetLastError();
+}
+
+template <int kKB>
+hipError_t launch_stream_kb(const GemmParams &p, hipStream_t stream) {
+    // m-tiles per 64-row chunk: only the M <= 48 cases stage less than 4
+    if (p.M <= 16)
+        return launch_stream<1, kKB>(p, stream);
+    if (p.M <= 32)
+        return launch_stream<2, kKB>(p, stream);
+    if (p.M <= 48)
+        return launch_stream<3, kKB>(p, stream);
+    return launch_stream<4, kKB>(p, stream);
+}
+
 template <int kMT>
 hipError_t launch_mt(const GemmParams &p, hipStream_t stream) {
     const int64_t mgrid = (p.M + kMT * 16 - 1) / (kMT * 16);
@@ -166,6 +415,21 @@ hipError_t launch_mt(const GemmParams &p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_block_scaled_gemm(const GemmParams &p, hipStream_t stream) {
+    // Up to 256 rows: stream the weights once, activations through LDS.
+    if (p.M <= 4 * kChunkRows) {
+        switch (p.K / kBlk) {
+        case 4:
+            return launch_stream_kb<4>(p, stream);
+        case 8:
+            return launch_stream_kb<8>(p, stream);
+        case 12:
+            return launch_stream_kb<12>(p, stream);
+        case 16:
+            return launch_stream_kb<16>(p, stream);
+        default:
+            break;
+        }
+    }
     // N % 128 == 0 (validated) so N is a whole number of 64-row tiles.
     if (p.M <= 16)
         return launch_mt<1>(p, stream);

@@ -16,6 +16,8 @@ struct NormQuantParams {
     const uint16_t *gamma_q;
     const uint16_t *gamma_kv;
     float eps;
+    float inv_nq;   // 1 / Nq and 1 / Nkv, rounded to fp32
+    float inv_nkv;
     int64_t M;
     int Nq;
     int Nkv;

@@ -13,12 +13,19 @@
 // Mapping onto CDNA4:
 //  - one wave64 per row; each lane owns 8 consecutive elements of every
 //    512-element chunk, fetched with one 16-byte load (a 1536 + 512 row is
-//    3 + 1 loads per lane, all issued before any arithmetic);
+//    3 + 1 loads per lane), and all loads are issued before any arithmetic;
+//  - the row is normalised as z = x * gamma (exact: a product of two bf16
+//    values, formed with the packed bf16 dot instruction) times rstd, and
+//    the group quantisation uses z * (rstd / s), so the per-element work is
+//    a handful of VALU operations (wave64 fp32 VALU ops cost 4 cycles, and
+//    at 8192 rows the VALU time is of the same order as the memory time);
 //  - a 128-element group is exactly the 16 lanes of one DPP row, so the
 //    group amax is a 4-step DPP butterfly and every lane of the row ends up
 //    holding its group's scale;
-//  - the sums of squares are pairwise trees in each lane, then a DPP row
-//    butterfly and a combination of the four row totals (fp32 throughout);
+//  - the sums of squares use the packed bf16 dot instruction per lane, then
+//    a DPP row butterfly and a combination of the four row totals (fp32
+//    throughout); rstd is the hardware reciprocal square root refined by one
+//    Newton step;
 //  - codes come from the packed fp32 -> e4m3fn convert, kv from the packed
 //    fp32 -> bf16 convert;
 //  - row-major scales: 4 lanes per chunk store 16 contiguous bytes;
@@ -34,12 +41,16 @@ namespace {
 constexpr int kChunk = 512;     // elements per 16-byte-per-lane wave load
 constexpr int kGroup = 128;
 constexpr float kE4m3Max = 448.0f;
+constexpr float kInvE4m3Max = 1.0f / 448.0f;  // rounded to fp32
 constexpr float kScaleFloor = 1e-12f;
 
 // 8 consecutive bf16 at p[col, col+8); elements at or beyond n read as zero.
-// kVec: p + col is 16-byte aligned whenever col + 8 <= n.
-template <bool kVec>
+// kVec: p + col is 16-byte aligned whenever col + 8 <= n.  kFull: the caller
+// guarantees col + 8 <= n (no bounds test, a single 16-byte load).
+template <bool kVec, bool kFull = false>
 __device__ __forceinline__ uint4 load8(const uint16_t *p, int col, int n) {
+    if (kFull)
+        return *reinterpret_cast<const uint4 *>(p + col);
     if (kVec && col + 8 <= n)
         return *reinterpret_cast<const uint4 *>(p + col);
     uint32_t e[8];
@@ -49,98 +60,109 @@ __device__ __forceinline__ uint4 load8(const uint16_t *p, int col, int n) {
     return make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16));
 }
 
-// Pairwise sum of the squares of 8 values.
-__device__ __forceinline__ float sumsq8(const float (&x)[8]) {
-    const float a = x[0] * x[0] + x[1] * x[1];
-    const float b = x[2] * x[2] + x[3] * x[3];
-    const float c = x[4] * x[4] + x[5] * x[5];
-    const float d = x[6] * x[6] + x[7] * x[7];
-    return (a + b) + (c + d);
+// Sum of squares of the 8 bf16 values of a 16-byte slice, with the packed
+// bf16 dot product (products exact in fp32, fp32 accumulation).
+__device__ __forceinline__ float sumsq8(const uint4 &v) {
+    return bf16_dot2(v.x, v.x, bf16_dot2(v.y, v.y, 0.0f)) + bf16_dot2(v.z, v.z, bf16_dot2(v.w, v.w, 0.0f));
 }
 
-// Pairwise sum of a small fixed-size array.
+// A gamma slice prepared for bf16_dot2: word 2i keeps the low bf16 of
+// gamma word i (high half zero), word 2i+1 the high bf16 (low half zero).
+struct GammaSlice {
+    uint32_t w[8];
+};
+
+__device__ __forceinline__ GammaSlice prepare_gamma(const uint4 &g) {
+    const uint32_t v[4] = {g.x, g.y, g.z, g.w};
+    GammaSlice r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r.w[2 * i] = v[i] & 0x0000FFFFu;
+        r.w[2 * i + 1] = v[i] & 0xFFFF0000u;
+    }
+    return r;
+}
+
+// z = x * gamma for the 8 elements of a slice, exact in fp32.
+__device__ __forceinline__ void times_gamma8(const uint4 &x, const GammaSlice &g, float (&z)[8]) {
+    const uint32_t v[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        z[2 * i] = bf16_dot2(v[i], g.w[2 * i], 0.0f);
+        z[2 * i + 1] = bf16_dot2(v[i], g.w[2 * i + 1], 0.0f);
+    }
+}
+
+// Output stores that no kernel of this call reads back: marked non-temporal
+// so they stream to memory instead of displacing cached lines.
+typedef unsigned v4u32 __attribute__((ext_vector_type(4)));
+typedef unsigned v2u32 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void store_streaming(uint16_t *p, const uint4 &v) {
+    __builtin_nontemporal_store(v4u32{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u32 *>(p));
+}
+__device__ __forceinline__ void store_streaming(uint8_t *p, uint32_t lo, uint32_t hi) {
+    __builtin_nontemporal_store(v2u32{lo, hi}, reinterpret_cast<v2u32 *>(p));
+}
+
+// Left-to-right sum of the per-chunk partial sums.  Chunks past the row
+// width contribute +0.0, which leaves a left fold unchanged, so every kernel
+// variant sums a row in the same order and gives the same bits.
 template <int N>
-__device__ __forceinline__ float tree_sum(const float *v) {
-    if constexpr (N == 1) {
-        return v[0];
-    } else {
-        constexpr int H = N / 2;
-        return tree_sum<H>(v) + tree_sum<N - H>(v + H);
-    }
+__device__ __forceinline__ float fold_sum(const float *v) {
+    float s = v[0];
+#pragma unroll
+    for (int i = 1; i < N; ++i)
+        s += v[i];
+    return s;
 }
 
-// Reciprocal RMS from the fp32 sum of squares.  The division and square root
-// are taken in fp64 and rounded once to fp32.
-__device__ __forceinline__ float rstd_from_ssq(float ssq, int n, float eps) {
-    return static_cast<float>(1.0 / sqrt(static_cast<double>(ssq) / n + static_cast<double>(eps)));
+// 1 / sqrt(mean of squares + eps) in fp32: hardware reciprocal square root
+// refined by one Newton step (exact for powers of four).
+__device__ __forceinline__ float rstd_from_ssq(float ssq, float inv_n, float eps) {
+    const float x = ssq * inv_n + eps;
+    const float r = __builtin_amdgcn_rsqf(x);
+    return r * (1.5f - (0.5f * x) * r * r);
 }
 
-// kQ / kKv: number of 512-element chunks held per lane (compile-time bound);
-// the actual widths are a.Nq / a.Nkv.  kVec: every row start, gamma and
-// output row is 16-byte aligned and Nkv % 8 == 0.
-template <int kQ, int kKv, bool kVec>
-__global__ __launch_bounds__(256) void fused_dual_rmsnorm_group_quant_kernel(NormQuantParams a) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    const int rows_per_block = blockDim.x / kWave;
-    const int64_t m = static_cast<int64_t>(xcd_contiguous_block(blockIdx.x, gridDim.x)) * rows_per_block + wave;
-    if (m >= a.M)
-        return;
-
-    const uint16_t *qrow = a.q + m * a.q_stride;
-    const uint16_t *krow = a.kv + m * a.kv_stride;
-
-    // -- all loads first: row data and gammas --------------------------------
-    uint4 xq[kQ], gq[kQ], xk[kKv], gk[kKv];
-#pragma unroll
-    for (int c = 0; c < kQ; ++c) {
-        const int col = c * kChunk + lane * 8;
-        xq[c] = load8<kVec>(qrow, col, a.Nq);
-        gq[c] = load8<kVec>(a.gamma_q, col, a.Nq);
-    }
-#pragma unroll
-    for (int c = 0; c < kKv; ++c) {
-        const int col = c * kChunk + lane * 8;
-        xk[c] = load8<kVec>(krow, col, a.Nkv);
-        gk[c] = load8<kVec>(a.gamma_kv, col, a.Nkv);
-    }
-
+// One row.  With z = x * gamma (exact in fp32: a product of two bf16 values)
+// and r = rstd, the normalised value is y = z * r; the group scale is
+// s = max(max|z| * r / 448, 1e-12) and the quantised value y / s is formed
+// as z * (r / s), so the row's rstd is applied once per group instead of
+// once per element.
+template <int kQ, int kKv, bool kVec, bool kFull>
+__device__ __forceinline__ void process_row(const NormQuantParams &a, int64_t m, int lane,
+                                            const uint4 (&xq)[kQ], const uint4 (&xk)[kKv],
+                                            const GammaSlice (&gq)[kQ], const GammaSlice (&gk)[kKv]) {
     // -- sums of squares (fp32) and reciprocal RMS -----------------------------
     float part_q[kQ], part_k[kKv];
 #pragma unroll
-    for (int c = 0; c < kQ; ++c) {
-        float x[8];
-        unpack8_bf16(xq[c], x);
-        part_q[c] = sumsq8(x);
-    }
+    for (int c = 0; c < kQ; ++c)
+        part_q[c] = sumsq8(xq[c]);
 #pragma unroll
-    for (int c = 0; c < kKv; ++c) {
-        float x[8];
-        unpack8_bf16(xk[c], x);
-        part_k[c] = sumsq8(x);
-    }
-    const float ssq_q = wave_sum(tree_sum<kQ>(part_q));
-    const float ssq_k = wave_sum(tree_sum<kKv>(part_k));
-    const float rq = rstd_from_ssq(ssq_q, a.Nq, a.eps);
-    const float rk = rstd_from_ssq(ssq_k, a.Nkv, a.eps);
+    for (int c = 0; c < kKv; ++c)
+        part_k[c] = sumsq8(xk[c]);
+    const float ssq_q = wave_sum(fold_sum<kQ>(part_q));
+    const float ssq_k = wave_sum(fold_sum<kKv>(part_k));
+    const float rq = rstd_from_ssq(ssq_q, a.inv_nq, a.eps);
+    const float rk = rstd_from_ssq(ssq_k, a.inv_nkv, a.eps);
 
-    // -- kv: normalise, scale, round to bf16 -----------------------------------
+    // -- kv: y = (x * gamma) * rstd, rounded to bf16 ---------------------------
     uint16_t *kout = a.out_kv + m * a.Nkv;
 #pragma unroll
     for (int c = 0; c < kKv; ++c) {
         const int col = c * kChunk + lane * 8;
-        if (col >= a.Nkv)
+        if (!kFull && col >= a.Nkv)
             continue;
-        float x[8], g[8];
-        unpack8_bf16(xk[c], x);
-        unpack8_bf16(gk[c], g);
         float y[8];
+        times_gamma8(xk[c], gk[c], y);
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-            y[j] = x[j] * rk * g[j];
+            y[j] *= rk;
         const uint4 packed = make_uint4(pack2_bf16(y[0], y[1]), pack2_bf16(y[2], y[3]),
                                         pack2_bf16(y[4], y[5]), pack2_bf16(y[6], y[7]));
-        if (kVec && col + 8 <= a.Nkv) {
+        if (kFull) {
+            store_streaming(kout + col, packed);
+        } else if (kVec && col + 8 <= a.Nkv) {
             *reinterpret_cast<uint4 *>(kout + col) = packed;
         } else {
             const uint32_t w[4] = {packed.x, packed.y, packed.z, packed.w};
@@ -151,35 +173,34 @@ __global__ __launch_bounds__(256) void fused_dual_rmsnorm_group_quant_kernel(Nor
         }
     }
 
-    // -- q: normalise, group amax, scale, e4m3fn codes -------------------------
+    // -- q: group amax, scale, e4m3fn codes -------------------------------------
     const int G = a.Nq / kGroup;
     uint8_t *qout = a.out_q + m * a.Nq;
 #pragma unroll
     for (int c = 0; c < kQ; ++c) {
         const int col = c * kChunk + lane * 8;
-        if (c * kChunk >= a.Nq)
+        if (!kFull && c * kChunk >= a.Nq)
             break;  // uniform across the wave
-        float x[8], g[8], y[8];
-        unpack8_bf16(xq[c], x);
-        unpack8_bf16(gq[c], g);
+        float z[8];
+        times_gamma8(xq[c], gq[c], z);
         float amax = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            y[j] = x[j] * rq * g[j];
-            amax = fmaxf(amax, fabsf(y[j]));
-        }
+        for (int j = 0; j < 8; ++j)
+            amax = fmaxf(amax, fabsf(z[j]));
         // 16 lanes x 8 elements = one 128-element group
         amax = row16_max(amax);
-        const float s = fmaxf(amax / kE4m3Max, kScaleFloor);
-        const float inv = 1.0f / s;
+        const float s = fmaxf((amax * rq) * kInvE4m3Max, kScaleFloor);
+        const float inv = rq * __builtin_amdgcn_rcpf(s);
         float r[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-            r[j] = fminf(fmaxf(y[j] * inv, -kE4m3Max), kE4m3Max);
+            r[j] = __builtin_amdgcn_fmed3f(z[j] * inv, -kE4m3Max, kE4m3Max);
         const uint32_t lo = pack4_e4m3(r[0], r[1], r[2], r[3]);
         const uint32_t hi = pack4_e4m3(r[4], r[5], r[6], r[7]);
-        if (col < a.Nq) {  // Nq % 128 == 0: a lane's 8 codes are all in range
-            if (kVec) {
+        if (kFull || col < a.Nq) {  // Nq % 128 == 0: a lane's 8 codes are all in range
+            if (kFull) {
+                store_streaming(qout + col, lo, hi);
+            } else if (kVec) {
                 *reinterpret_cast<uint2 *>(qout + col) = make_uint2(lo, hi);
             } else {
 #pragma unroll
@@ -189,7 +210,7 @@ __global__ __launch_bounds__(256) void fused_dual_rmsnorm_group_quant_kernel(Nor
         }
 
         const int grp = c * (kChunk / kGroup) + lane / 16;
-        if ((lane & 15) == 0 && grp < G) {
+        if ((lane & 15) == 0 && (kFull || grp < G)) {
             const int64_t at = a.transpose_scale ? static_cast<int64_t>(grp) * a.M + m
                                                  : m * G + grp;
             a.out_scale[at] = s;
@@ -197,14 +218,71 @@ __global__ __launch_bounds__(256) void fused_dual_rmsnorm_group_quant_kernel(Nor
     }
 }
 
-template <int kQ, int kKv, bool kVec>
+// kQ / kKv: number of 512-element chunks held per lane (compile-time bound);
+// the actual widths are a.Nq / a.Nkv.  kVec: every row start, gamma and
+// output row is 16-byte aligned and Nkv % 8 == 0.  kRows: consecutive rows
+// per wave; all their loads are issued together, gammas once per wave.
+// kFull: Nq == 512 * kQ and Nkv == 512 * kKv (no bounds tests).
+template <int kQ, int kKv, bool kVec, int kRows, bool kFull>
+__global__ __launch_bounds__(256) void fused_dual_rmsnorm_group_quant_kernel(NormQuantParams a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: scalar row addressing
+    const int waves_per_block = blockDim.x / kWave;
+    const int64_t row0 =
+        (static_cast<int64_t>(xcd_contiguous_block(blockIdx.x, gridDim.x)) * waves_per_block + wave) * kRows;
+    if (row0 >= a.M)
+        return;
+
+    // -- all loads first: gammas, then every row's data ------------------------
+    uint4 gq_raw[kQ], gk_raw[kKv];
+#pragma unroll
+    for (int c = 0; c < kQ; ++c)
+        gq_raw[c] = load8<kVec, kFull>(a.gamma_q, c * kChunk + lane * 8, a.Nq);
+#pragma unroll
+    for (int c = 0; c < kKv; ++c)
+        gk_raw[c] = load8<kVec, kFull>(a.gamma_kv, c * kChunk + lane * 8, a.Nkv);
+    uint4 xq[kRows][kQ], xk[kRows][kKv];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+        const int64_t m = row0 + r;
+        if (m >= a.M)
+            break;
+        const uint16_t *qrow = a.q + m * a.q_stride;
+        const uint16_t *krow = a.kv + m * a.kv_stride;
+#pragma unroll
+        for (int c = 0; c < kQ; ++c)
+            xq[r][c] = load8<kVec, kFull>(qrow, c * kChunk + lane * 8, a.Nq);
+#pragma unroll
+        for (int c = 0; c < kKv; ++c)
+            xk[r][c] = load8<kVec, kFull>(krow, c * kChunk + lane * 8, a.Nkv);
+    }
+    // gammas prepared once per wave, shared by its rows
+    GammaSlice gq[kQ], gk[kKv];
+#pragma unroll
+    for (int c = 0; c < kQ; ++c)
+        gq[c] = prepare_gamma(gq_raw[c]);
+#pragma unroll
+    for (int c = 0; c < kKv; ++c)
+        gk[c] = prepare_gamma(gk_raw[c]);
+
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+        const int64_t m = row0 + r;
+        if (m >= a.M)
+            break;
+        process_row<kQ, kKv, kVec, kFull>(a, m, lane, xq[r], xk[r], gq, gk);
+    }
+}
+
+template <int kQ, int kKv, bool kVec, int kRows, bool kFull = false>
 hipError_t launch_variant(const NormQuantParams &p, hipStream_t stream) {
-    const int rows_per_block = p.M >= 4 ? 4 : static_cast<int>(p.M);
-    const int64_t blocks = (p.M + rows_per_block - 1) / rows_per_block;
+    const int64_t waves = (p.M + kRows - 1) / kRows;
+    const int waves_per_block = waves >= 4 ? 4 : static_cast<int>(waves);
+    const int64_t blocks = (waves + waves_per_block - 1) / waves_per_block;
     if (blocks > 0x7FFFFFFF)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((fused_dual_rmsnorm_group_quant_kernel<kQ, kKv, kVec>),
-                       dim3(static_cast<unsigned>(blocks)), dim3(rows_per_block * kWave), 0, stream, p);
+    hipLaunchKernelGGL((fused_dual_rmsnorm_group_quant_kernel<kQ, kKv, kVec, kRows, kFull>),
+                       dim3(static_cast<unsigned>(blocks)), dim3(waves_per_block * kWave), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -220,10 +298,10 @@ hipError_t launch_normquant(const NormQuantParams &p, hipStream_t stream) {
                      (p.q_stride % 8) == 0 && (p.kv_stride % 8) == 0 && (p.Nkv % 8) == 0;
     const int qch = (p.Nq + kChunk - 1) / kChunk;
     const int kch = (p.Nkv + kChunk - 1) / kChunk;
-    if (qch == 3 && kch == 1)  // the MLA latent shape: 1536 + 512
-        return vec ? launch_variant<3, 1, true>(p, stream) : launch_variant<3, 1, false>(p, stream);
+    if (vec && p.Nq == 3 * kChunk && p.Nkv == kChunk)  // the MLA latent shape: 1536 + 512
+        return launch_variant<3, 1, true, 1, true>(p, stream);
     if (qch <= 8 && kch <= 4)
-        return vec ? launch_variant<8, 4, true>(p, stream) : launch_variant<8, 4, false>(p, stream);
+        return vec ? launch_variant<8, 4, true, 1>(p, stream) : launch_variant<8, 4, false, 1>(p, stream);
     return hipErrorInvalidValue;
 }
 

@@ -49,7 +49,7 @@ def run_gemm(a, As, w, Bs, transposed, dev):
     return out
 
 
-@pytest.mark.parametrize("M,N,K,seed", [(1, 256, 256, 1), (5, 384, 640, 2), (16, 256, 1536, 3),
+@pytest.mark.parametrize("M,N,K,seed", [(1, 256, 256, 1), (5, 384, 640, 2), (16, 256, 1536, 3), (3, 1280, 512, 8), (40, 384, 1024, 9), (64, 8192, 2048, 10),
                                         (17, 512, 384, 4), (64, 128, 1536, 5), (100, 640, 896, 6),
                                         (256, 256, 1536, 7)])
 def test_gemm_random_vs_oracle(M, N, K, seed):

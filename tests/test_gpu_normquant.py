@@ -91,7 +91,7 @@ def _case(q, kv, gq, gk, eps=W.EPS, name="adhoc"):
 
 @pytest.mark.parametrize("M,Nq,Nkv,seed", [(1, 128, 8, 1), (3, 256, 64, 2), (2, 128, 40, 3),
                                            (7, 640, 100, 4), (5, 4096, 2048, 5), (9, 1536, 512, 6),
-                                           (33, 1536, 576, 7)])
+                                           (33, 1536, 576, 7), (4099, 1536, 512, 9)])
 def test_generic_shapes(M, Nq, Nkv, seed):
     """Tiny, ragged (partial 512-chunks, Nkv % 8 != 0, M not a multiple of
     the 4 rows per block) and largest supported widths."""
