@@ -41,6 +41,7 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned v4u32 __attribute__((ext_vector_type(4)));
 
 constexpr int kBlk = 128;            // K-block = weight scale block = quant group
 constexpr int kStageKb = 4;          // K-blocks staged in LDS at a time
@@ -364,6 +365,216 @@ int device_cu_count() {
     return cached[dev];
 }
 
+// ---------------------------------------------------------------------------
+// Decode variant (M <= 64, K/128 = kKB known at compile time).
+//
+// A block of 8 waves covers `subtiles_per_block` 16-row weight subtiles (one
+// per wave; the spare waves only help stage).  Phases:
+//  1. every thread loads its share of the activation tile (M x K bytes) into
+//     registers; then each weight wave starts its ring: the first kRing
+//     K-blocks of its subtile (32 bytes of one weight row per lane and
+//     K-block);
+//  2. the activation tile is written to LDS in fragment order (the compiler
+//     waits only for the activation loads: the ring loads were issued after
+//     them and loads complete in order), LDS writes are drained and the
+//     block meets at a plain s_barrier (no release fence, which would drain
+//     the ring too);
+//  3. K-block by K-block: MFMAs on the ring slot, scale FMAs, and the slot is
+//     refilled with K-block kb + kRing, so each wave computes while its later
+//     weight bytes are still arriving;
+//  4. the block's output tile goes through LDS and is written as contiguous
+//     row segments (2 * 16 * subtiles_per_block bytes per row) instead of
+//     32-byte pieces from every wave.
+// ---------------------------------------------------------------------------
+constexpr int kDecodeWaves = 8;
+constexpr int kRing = 6;  // weight K-blocks in flight per wave
+
+template <int kMT, int kKB>
+__global__ __launch_bounds__(kDecodeWaves * kWave) void block_scaled_fp8_gemm_decode_kernel(
+    GemmParams p, int subtiles_per_block) {
+    extern __shared__ uint4 s_dyn[];
+    uint4 *s_act = s_dyn;                                                   // [kb][mt][half][lane]
+    float *s_as = reinterpret_cast<float *>(s_dyn + kKB * kMT * 2 * kWave);  // [16 kb][64 rows]
+    uint16_t *s_out = reinterpret_cast<uint16_t *>(s_as + 2 * kDecodeWaves * kWave);  // [64 rows][cols of block]
+
+    constexpr int kRows = kMT * 16;
+    constexpr int kGranules = kRows * kKB * 8;                 // 16-byte pieces of the tile
+    constexpr int kPerThread = kGranules / (kDecodeWaves * kWave);
+    static_assert(kGranules % (kDecodeWaves * kWave) == 0, "tile must split evenly over the block");
+    constexpr int kRingN = kRing < kKB ? kRing : kKB;
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: scalar addressing
+    const int spb = subtiles_per_block;
+    const int64_t M = p.M, K = p.K;
+    const int64_t S = p.N / 16;
+    const int64_t st = static_cast<int64_t>(blockIdx.x) * spb + wave;
+    const bool active = wave < spb && st < S;
+    const int64_t n0 = st * 16;
+
+    // The prologue is straight-line code (every load unconditional, indices
+    // clamped into range) so that the compiler's wait counts stay exact: a
+    // branch around loads makes it drain all outstanding loads where the
+    // paths meet.
+    // -- 1. activation tile into registers (coalesced: consecutive threads,
+    //       consecutive 16-byte pieces of a row; rows at or beyond M repeat
+    //       row M-1, they only feed output columns that are never stored),
+    //       activation scales, then the weight ring --------------------------
+    // (a native vector type: a copy of the HIP uint4 struct from global
+    // memory would be kept in scratch)
+    v4u32 stage[kPerThread];
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+        const int g = threadIdx.x + i * kDecodeWaves * kWave;
+        const int64_t r = min<int64_t>(g / (kKB * 8), M - 1);
+        const int c = g % (kKB * 8);
+        stage[i] = *reinterpret_cast<const v4u32 *>(p.a + r * K + c * 16);
+    }
+    // wave w stages the scales of K-blocks w and w + 8 (slots past kKB are
+    // never read), lane = row
+    const int kb0 = wave, kb1 = wave + kDecodeWaves;
+    const int64_t ar = min<int64_t>(lane, M - 1);
+    const int kb0c = min(kb0, kKB - 1), kb1c = min(kb1, kKB - 1);
+    const float *as0p = p.a_scale_transposed ? p.a_scale + static_cast<int64_t>(kb0c) * M + ar : p.a_scale + ar * kKB + kb0c;
+    const float *as1p = p.a_scale_transposed ? p.a_scale + static_cast<int64_t>(kb1c) * M + ar : p.a_scale + ar * kKB + kb1c;
+    const float as0 = *as0p, as1 = *as1p;
+    __builtin_amdgcn_sched_barrier(0);  // ring loads stay behind the staging loads
+
+    // spare waves read their block's last subtile (L2 hits, never used)
+    const int64_t st_ld = min<int64_t>(st, min<int64_t>(static_cast<int64_t>(blockIdx.x) * spb + spb, S) - 1);
+    const uint8_t *wrow = p.w + (st_ld * 16 + (lane & 15)) * K + 32 * (lane >> 4);
+    v8i wf[kRingN];
+    float bs[kKB];
+#pragma unroll
+    for (int kb = 0; kb < kRingN; ++kb) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(wrow + kb * kBlk);
+        wf[kb] = join(src[0], src[1]);
+    }
+    const float *bs_row = p.w_scale + (st_ld * 16 / kBlk) * kKB;
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb)
+        bs[kb] = bs_row[kb];
+    __builtin_amdgcn_sched_barrier(0);  // LDS writes stay behind the ring loads
+
+    // -- 2. activation tile to LDS; drain LDS writes; plain barrier -----------
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+        const int g = threadIdx.x + i * kDecodeWaves * kWave;
+        const int r = g / (kKB * 8), c = g % (kKB * 8);
+        const int kb = c >> 3, j = c & 7;
+        reinterpret_cast<v4u32 *>(s_act)[((kb * kMT + (r >> 4)) * 2 + (j & 1)) * kWave + (j >> 1) * 16 + (r & 15)] =
+            stage[i];
+    }
+    s_as[kb0 * kWave + lane] = as0;
+    s_as[kb1 * kWave + lane] = as1;
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+    __builtin_amdgcn_s_barrier();
+
+    // -- 3. K-block loop (weight waves only; every wave reaches both barriers)
+    const int cols = 16 * spb;  // this block's output columns
+    if (active) {
+    v4f acc[kMT];
+#pragma unroll
+    for (int t = 0; t < kMT; ++t)
+        acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    uint4 lo[kMT], hi[kMT];
+    float as_m[kMT];
+#pragma unroll
+    for (int t = 0; t < kMT; ++t) {
+        lo[t] = s_act[(t * 2 + 0) * kWave + lane];
+        hi[t] = s_act[(t * 2 + 1) * kWave + lane];
+        as_m[t] = s_as[t * 16 + (lane & 15)];
+    }
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb) {
+        v4f part[kMT];
+        float sc[kMT];
+#pragma unroll
+        for (int t = 0; t < kMT; ++t) {
+            part[t] = mfma_e4m3_16x16x128(wf[kb % kRingN], join(lo[t], hi[t]));
+            sc[t] = as_m[t] * bs[kb];
+        }
+        if (kb + 1 < kKB) {
+#pragma unroll
+            for (int t = 0; t < kMT; ++t) {
+                lo[t] = s_act[(((kb + 1) * kMT + t) * 2 + 0) * kWave + lane];
+                hi[t] = s_act[(((kb + 1) * kMT + t) * 2 + 1) * kWave + lane];
+                as_m[t] = s_as[(kb + 1) * kWave + t * 16 + (lane & 15)];
+            }
+        }
+        // refill the slot just consumed with K-block kb + kRing
+        if (kb + kRingN < kKB) {
+            const uint4 *src = reinterpret_cast<const uint4 *>(wrow + (kb + kRingN) * kBlk);
+            wf[kb % kRingN] = join(src[0], src[1]);
+        }
+#pragma unroll
+        for (int t = 0; t < kMT; ++t) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[t][i] = fmaf(part[t][i], sc[t], acc[t][i]);
+            // see compute_chunk: keeps the FMAs of K-block kb ahead of the
+            // MFMAs of K-block kb + 1
+            asm volatile("" : "+v"(acc[t]), "+v"(lo[t].x), "+v"(lo[t].y), "+v"(lo[t].z), "+v"(lo[t].w),
+                         "+v"(hi[t].x), "+v"(hi[t].y), "+v"(hi[t].z), "+v"(hi[t].w), "+v"(as_m[t]));
+        }
+    }
+
+    // -- 4. output tile through LDS, contiguous row segments ----------------------
+#pragma unroll
+    for (int t = 0; t < kMT; ++t) {
+        const int m = t * 16 + (lane & 15);
+        *reinterpret_cast<uint2 *>(s_out + m * cols + wave * 16 + 4 * (lane >> 4)) =
+            make_uint2(pack2_bf16(acc[t][0], acc[t][1]), pack2_bf16(acc[t][2], acc[t][3]));
+    }
+    }  // active
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();        // every weight wave's tile is in LDS
+    const int64_t blk_n0 = static_cast<int64_t>(blockIdx.x) * spb * 16;
+    const int pieces_per_row = cols / 8;  // 16-byte pieces
+    // only columns of existing subtiles (< N) are read back; those were written
+    for (int pi = threadIdx.x; pi < M * pieces_per_row; pi += blockDim.x) {
+        const int m = pi / pieces_per_row, part = pi % pieces_per_row;
+        if (blk_n0 + part * 8 < p.N)
+            *reinterpret_cast<uint4 *>(p.out + m * p.N + blk_n0 + part * 8) =
+                *reinterpret_cast<const uint4 *>(s_out + m * cols + part * 8);
+    }
+}
+
+template <int kMT, int kKB>
+hipError_t launch_decode(const GemmParams &p, hipStream_t stream) {
+    const int64_t S = p.N / 16;
+    const int64_t cus = device_cu_count();
+    const int spb = static_cast<int>(std::min<int64_t>(kDecodeWaves, (S + cus - 1) / cus));
+    const int64_t blocks = (S + spb - 1) / spb;
+    if (blocks > 0x7FFFFFFF)
+        return hipErrorInvalidValue;
+    const size_t lds = static_cast<size_t>(kKB) * kMT * 2 * kWave * sizeof(uint4) +
+                       static_cast<size_t>(2 * kDecodeWaves) * kWave * sizeof(float) +
+                       static_cast<size_t>(kChunkRows) * 16 * kDecodeWaves * sizeof(uint16_t);
+    auto kern = block_scaled_fp8_gemm_decode_kernel<kMT, kKB>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+        if (e != hipSuccess)
+            return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kDecodeWaves * kWave), lds, stream, p, spb);
+    return hipGetLastError();
+}
+
+template <int kKB>
+hipError_t launch_decode_kb(const GemmParams &p, hipStream_t stream) {
+    if (p.M <= 16)
+        return launch_decode<1, kKB>(p, stream);
+    if (p.M <= 32)
+        return launch_decode<2, kKB>(p, stream);
+    if (p.M <= 48)
+        return launch_decode<3, kKB>(p, stream);
+    return launch_decode<4, kKB>(p, stream);
+}
+
 template <int kMT, int kKB>
 hipError_t launch_stream(const GemmParams &p, hipStream_t stream) {
     // one subtile per wave, at most 8 waves per block, at least one block per CU
@@ -415,6 +626,21 @@ hipError_t launch_mt(const GemmParams &p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_block_scaled_gemm(const GemmParams &p, hipStream_t stream) {
+    // Decode batches: weight ring per wave, activations resident in LDS.
+    if (p.M <= kChunkRows) {
+        switch (p.K / kBlk) {
+        case 4:
+            return launch_decode_kb<4>(p, stream);
+        case 8:
+            return launch_decode_kb<8>(p, stream);
+        case 12:
+            return launch_decode_kb<12>(p, stream);
+        case 16:
+            return launch_decode_kb<16>(p, stream);
+        default:
+            break;
+        }
+    }
     // Up to 256 rows: stream the weights once, activations through LDS.
     if (p.M <= 4 * kChunkRows) {
         switch (p.K / kBlk) {
