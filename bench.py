@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="skip the M=1 / M=8192 / M=256 extras")
     ap.add_argument("--kernel-loop", default="", help="only launch this kernel in a loop (profiling)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 64 MiB device copy in a loop (scales the HBM byte counters)")
     return ap.parse_args()
 
 
@@ -280,6 +282,21 @@ def sweep(torch, np, mi, W, wa, wb, dev, cold):
     return res
 
 
+def calibrate_copy(torch, steps):
+    """A plain device-to-device copy of a known size (64 MiB, rotating over
+    16 buffer pairs = 2 GiB so every copy streams from HBM).  Run under
+    rocprofv3 --pmc, FETCH_SIZE / WRITE_SIZE per copy divided by 64 MiB give
+    the factors that turn those counters into HBM bytes."""
+    dev = torch.device("cuda:0")
+    n = 64 << 20
+    srcs = [torch.empty(n, dtype=torch.uint8, device=dev).random_() for _ in range(16)]
+    dsts = [torch.empty(n, dtype=torch.uint8, device=dev) for _ in range(16)]
+    fns = [lambda i=i: dsts[i].copy_(srcs[i]) for i in range(16)]
+    us = time_eager(torch, fns, steps)
+    print(json.dumps({"calibrate_copy_bytes": n, "us_per_copy": round(us, 3),
+                      "GB/s(read+write)": round(2 * n / us / 1e3, 1)}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -289,6 +306,10 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.calibrate_copy:
+        calibrate_copy(torch, args.steps)
+        return
 
     import rmsnorm_fp8_block_amd as mi
     from rmsnorm_fp8_block_amd import workloads as W
@@ -354,11 +375,12 @@ def main():
              "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "source_sha": source_sha(src)}
         if flops:
             k["TFLOP/s"] = round(flops / us / 1e6, 2)
+        k["traffic"] = measured_traffic(name, k["source_sha"])
         kernels[name] = k
     dom = max(kernels, key=lambda n: kernels[n]["us"])
     dk = kernels[dom]
     roofline = {"bound": "hbm", "achieved": dk["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": dk["frac_hbm"], "traffic": measured_traffic(dom, dk["source_sha"]),
+                "frac": dk["frac_hbm"], "traffic": dk["traffic"],
                 "kernel": dom, "bytes_per_launch": dk["bytes"], "us_per_launch": dk["us"]}
 
     line = {
