@@ -27,11 +27,14 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE, "-I", CSRC,
 ]
+# device code: matrix-core results in ordinary VGPRs (the scale FMAs read
+# them right away; the accumulation-register form costs a copy per value)
+HIP_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    lang = ["-x", "hip"] if src.endswith(".hip") else []
+    lang = ["-x", "hip", *HIP_FLAGS] if src.endswith(".hip") else []
     cmd = [HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

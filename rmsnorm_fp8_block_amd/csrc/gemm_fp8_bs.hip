@@ -32,6 +32,7 @@
 // operands use the same one; both are loaded with the same lane/byte -> k
 // assignment.
 #include <algorithm>
+#include <atomic>
 
 #include "device.h"
 #include "launch.h"
@@ -155,23 +156,7 @@ __global__ __launch_bounds__(256) void block_scaled_fp8_gemm_kernel(GemmParams p
     }
 }
 
-// ---------------------------------------------------------------------------
-// Weight-streaming variant (M <= 256, K/128 = kKB known at compile time).
-// Each wave owns one 16-row weight subtile and loads all kKB K-blocks of it
-// with one burst of 16-byte loads (24 KB in flight per wave at K = 1536),
-// so the whole weight matrix is read from HBM once, in a single round trip
-// spread over every CU.  The activations are processed in chunks of up to
-// 64 rows: the block stages a chunk (in fragment order) and its scales in
-// LDS with direct global -> LDS loads, then every wave multiplies it with
-// the weight fragments it keeps in registers.
-//
-// Ordering: the first chunk's LDS loads are issued before the weight burst,
-// and before the barrier each wave waits only until those have landed
-// (loads complete in issue order), so the MFMAs start while the weight
-// K-blocks are still arriving.
-// ---------------------------------------------------------------------------
-constexpr int kStreamMaxWaves = 8;
-constexpr int kChunkRows = 64;
+constexpr int kChunkRows = 64;  // activation rows of the decode kernel
 
 // vmcnt-only waits (gfx9 encoding: vmcnt[3:0] + vmcnt[5:4] at bits 15:14,
 // expcnt 6:4 and lgkmcnt 11:8 left at their maxima = no wait)
@@ -181,174 +166,368 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((kVm & 15) | ((kVm >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int kMT, int kKB>
-__device__ __forceinline__ void stage_chunk(const GemmParams &p, int64_t m0, uint4 *s_act, float *s_as,
-                                           int wave, int waves, int lane) {
-    const int64_t M = p.M, K = p.K;
-    // Every block reads the same (small) activation rows.  Each block starts
-    // at a different slab so that, at any moment, the CUs ask for different
-    // cache lines instead of queueing on the same L2 channel.
-    constexpr int kSlabs = kKB * kMT * 2;
-    const int rot = static_cast<int>((blockIdx.x * 7u) % kSlabs);
-    // Slab i = (kb * kMT + mt) * 2 + h of the fragment layout is 64 lanes x
-    // 16 bytes; one global_load_lds_dwordx4 fills it, lane L fetching bytes
-    // [kb*128 + 32*(L/16) + 16*h, +16) of activation row m0 + mt*16 + L%16.
-    // Rows at or beyond M repeat row M-1: they only feed output columns that
-    // are never stored.
-    for (int j = wave; j < kSlabs; j += waves) {
-        const int i = (j + rot) % kSlabs;
-        const int h = i & 1, mt = (i >> 1) % kMT, kb = (i >> 1) / kMT;
-        const int64_t r = min<int64_t>(m0 + mt * 16 + (lane & 15), M - 1);
-        const uint8_t *src = p.a + r * K + kb * kBlk + 32 * (lane >> 4) + 16 * h;
-        __builtin_amdgcn_global_load_lds(src, s_act + i * kWave, 16, 0, 0);
+// ---------------------------------------------------------------------------
+// Wide variant (64 < M <= 256, K/128 = kKB known at compile time).
+//
+// A block of kWaves waves owns a slab of kNS 16-row weight subtiles and all
+// M activation rows; wave w computes rows [16 kMT w, 16 kMT (w + 1)) against
+// the whole slab.  With 8 waves, two share each SIMD, so one wave's waits
+// for LDS and for the barrier overlap the other's matrix-core work.
+// Weights, activations and scales reach LDS through direct global -> LDS
+// loads (no registers held for them), each in a ring of K-block stages:
+//  - weight stage kb (kNS x 2 KB, shared by all waves, which split its 1 KB
+//    slots between them),
+//  - activation stage kb (each wave loads its own kMT 16-row tiles),
+//  - scales of stage kb (per wave: one As per row, one Bs per subtile).
+// The weight ring is deeper than the activation ring: weights come from
+// HBM, activations are read by every block and sit in L2.
+// Per K-block kb: wait until this wave's loads of stage kb + 1 have landed
+// (exact vmcnt count, worked out at compile time from the issue order),
+// drain LDS reads, one plain s_barrier (all waves' parts of stage kb + 1 are
+// in LDS and every wave has stage kb in registers), refill the slots of
+// stage kb, read stage kb + 1 into the second register set, then the MFMAs
+// of stage kb.  The scale FMAs of an MFMA are issued two MFMAs later, in
+// the matrix core's shadow.
+// ---------------------------------------------------------------------------
+constexpr int kWideWaves = 8;  // 2 per SIMD
+
+constexpr int cmin(int a, int b) { return a < b ? a : b; }
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+template <int kKB, int kNS, int kMT, int kWaves>
+struct WidePlan {
+    static_assert(kNS % 2 == 0 && kNS >= 2 && kNS <= 6, "whole 2-slot subtiles; two fragment sets fit the registers");
+    static_assert(kWaves == 4 || kWaves == 8, "4 or 8 waves");
+    static_assert(kMT >= 1 && kMT * kWaves * 16 <= 256, "at most 256 rows");
+    static constexpr int kSlot = 1024;                         // 8 rows x 128 bytes
+    static constexpr int kWStage = kNS * 2 * kSlot;            // weight bytes per K-block
+    static constexpr int kAStage = kWaves * kMT * 2 * kSlot;   // activation bytes per K-block
+    static constexpr int kSStage = kWaves * 2 * kWave * 4;     // per wave: As (one per lane), Bs
+    static constexpr int kRA = cmin(kKB, 3);                   // activation stages
+    // weight stages: as many as the rest of the 160 KB allows, up to 6
+    static constexpr int kRW = cmin(kKB, cmin(6, (160 * 1024 - kRA * (kAStage + kSStage)) / kWStage));
+    // weight loads per wave per stage; when 2 kNS slots do not split evenly,
+    // the extra loads repeat a slot of the same row half (same bytes to the
+    // same place: harmless, and every wave then counts the same loads)
+    static constexpr int kNW = (2 * kNS + kWaves - 1) / kWaves;
+    static constexpr int kNA = 2 * kMT + 2;                    // activation, As and Bs loads
+    static constexpr int kWOff = 0;
+    static constexpr int kAOff = kWOff + kRW * kWStage;
+    static constexpr int kSOff = kAOff + kRA * kAStage;
+    static constexpr int kLds = kSOff + kRA * kSStage;
+    static_assert(kRW >= 2 && kRA >= 2, "a stage is waited for one iteration after it is issued");
+    static_assert(kLds <= 160 * 1024, "LDS per CU");
+
+    // Loads a wave has issued after the last load of stage s, at the point
+    // where stage s is waited for: after the prologue for s = 0, else in
+    // iteration s - 1 before its refill.  Issue order: prologue
+    // s = 0, 1, ...: activations(s) if s < kRA, then weights(s) if s < kRW;
+    // iteration it, after its barrier: activations(it + kRA), then
+    // weights(it + kRW).  Loads complete in order, so a wait for stage s
+    // also waits for everything issued before its last load: activations go
+    // first so that this never includes a weight stage beyond s (kRW <= kRA + 1)
+    // or, with a deeper weight ring, only the weights issued alongside.
+    static constexpr int vm_wait(int st) {
+        int issued = 0, last_w = -1, last_a = -1;
+        for (int s = 0; s < cmax(kRW, kRA); ++s) {
+            if (s < kRA && s < kKB) {
+                issued += kNA;
+                if (s == st) last_a = issued;
+            }
+            if (s < kRW && s < kKB) {
+                issued += kNW;
+                if (s == st) last_w = issued;
+            }
+        }
+        for (int it = 0; it + 1 < st; ++it) {
+            const int sw = it + kRW, sa = it + kRA;
+            if (sa < kKB) {
+                issued += kNA;
+                if (sa == st) last_a = issued;
+            }
+            if (sw < kKB) {
+                issued += kNW;
+                if (sw == st) last_w = issued;
+            }
+        }
+        return issued - cmax(last_w, last_a);
     }
-    // activation scales: one 4-byte direct load per K-block, lane = row
-    const int krot = static_cast<int>((blockIdx.x * 5u) % kKB);
-    for (int j = wave; j < kKB; j += waves) {
-        const int kb = (j + krot) % kKB;
-        const int64_t r = min<int64_t>(m0 + lane, M - 1);
-        const float *src = p.a_scale_transposed ? p.a_scale + static_cast<int64_t>(kb) * M + r
-                                                : p.a_scale + r * kKB + kb;
-        __builtin_amdgcn_global_load_lds(src, s_as + kb * kWave, 4, 0, 0);
-    }
+};
+
+__device__ __forceinline__ v8i join4(const v4u32 &lo, const v4u32 &hi) {
+    return __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// One 64-row chunk: each wave multiplies the staged activations with its
-// weight fragments and writes its 16 output columns of the chunk's rows.
-template <int kMT, int kKB>
-__device__ __forceinline__ void compute_chunk(const GemmParams &p, int64_t m0, int64_t n0, int lane,
-                                              const uint4 *s_act, const float *s_as,
-                                              const v8i (&wf)[kKB], const float (&bs)[kKB]) {
-    v4f acc[kMT];
-#pragma unroll
-    for (int t = 0; t < kMT; ++t)
-        acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    // Pipeline: the MFMAs of K-block kb+1 are issued before the scale FMAs
-    // of K-block kb (so the FMAs' wait for the matrix-core results overlaps
-    // the next MFMAs), and the activation fragments and scales are read from
-    // LDS two K-blocks ahead.  The empty asm statements pin that order: the
-    // compiler would otherwise be free to issue every MFMA first and keep all
-    // partial results live, which does not fit next to the weight burst.
-    auto frag = [&](int kb, int t, uint4 &lo, uint4 &hi, float &as) {
-        lo = s_act[((kb * kMT + t) * 2 + 0) * kWave + lane];
-        hi = s_act[((kb * kMT + t) * 2 + 1) * kWave + lane];
-        as = s_as[kb * kWave + t * 16 + (lane & 15)];
-    };
-    uint4 lo[kMT], hi[kMT];     // fragments of the next K-block to multiply
-    float as_m[kMT];
-    v4f part[kMT];              // MFMA results of the K-block being folded
-    float sc[kMT];
-#pragma unroll
-    for (int t = 0; t < kMT; ++t) {
-        uint4 l0, h0;
-        float a0;
-        frag(0, t, l0, h0, a0);
-        part[t] = mfma_e4m3_16x16x128(wf[0], join(l0, h0));
-        sc[t] = a0 * bs[0];
-    }
-    if (kKB > 1) {
-#pragma unroll
-        for (int t = 0; t < kMT; ++t)
-            frag(1, t, lo[t], hi[t], as_m[t]);
-    }
-#pragma unroll
-    for (int kb = 0; kb < kKB; ++kb) {
-        v4f next[kMT];
-        float nsc[kMT];
-        if (kb + 1 < kKB) {
-#pragma unroll
-            for (int t = 0; t < kMT; ++t) {
-                next[t] = mfma_e4m3_16x16x128(wf[kb + 1], join(lo[t], hi[t]));
-                nsc[t] = as_m[t] * bs[kb + 1];
-            }
-            if (kb + 2 < kKB) {
-#pragma unroll
-                for (int t = 0; t < kMT; ++t)
-                    frag(kb + 2, t, lo[t], hi[t], as_m[t]);
-            }
-        }
-#pragma unroll
-        for (int t = 0; t < kMT; ++t) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                acc[t][i] = fmaf(part[t][i], sc[t], acc[t][i]);
-            if (kb + 1 < kKB) {
-                part[t] = next[t];
-                sc[t] = nsc[t];
-            }
-            asm volatile("" : "+v"(acc[t]), "+v"(part[t]), "+v"(lo[t].x), "+v"(lo[t].y), "+v"(lo[t].z),
-                         "+v"(lo[t].w), "+v"(hi[t].x), "+v"(hi[t].y), "+v"(hi[t].z), "+v"(hi[t].w),
-                         "+v"(as_m[t]));
-        }
-    }
-#pragma unroll
-    for (int t = 0; t < kMT; ++t) {
-        const int64_t m = m0 + t * 16 + (lane & 15);
-        if (m < p.M) {
-            const int64_t n = n0 + 4 * (lane >> 4);
-            *reinterpret_cast<uint2 *>(p.out + m * p.N + n) =
-                make_uint2(pack2_bf16(acc[t][0], acc[t][1]), pack2_bf16(acc[t][2], acc[t][3]));
-        }
-    }
-}
+// Per-wave state of the wide kernel: load sources, accumulators and the
+// MFMA -> FMA pipeline.  Member functions instead of lambdas: the host pass
+// of the compiler drops a kernel's launch stub when the kernel calls a
+// lambda that issues direct global -> LDS loads.
+template <int kKB, int kNS, int kMT, int kWaves>
+struct WideWave {
+    using P = WidePlan<kKB, kNS, kMT, kWaves>;
+    static constexpr int kLag = 2;                // FMAs of MFMA n are issued after MFMA n + kLag
+    static constexpr int kRing = kLag + 2;        // partial results in flight
+    static constexpr int kSeq = kKB * kNS * kMT;  // MFMAs per wave
 
-template <int kMT, int kKB>
-__global__ __launch_bounds__(kStreamMaxWaves * kWave) void block_scaled_fp8_gemm_stream_kernel(
-    GemmParams p, int subtiles_per_block) {
+    uint8_t *lds;
+    int lane, wave;
+    const uint8_t *wbase[P::kNW];  // uniform: weight slot sources
+    int wslot[P::kNW];             // uniform: their LDS slots
+    uint32_t w_off;                // per lane
+    const uint8_t *a;
+    uint32_t a_off[kMT][2];        // per lane: m-tile j, row half g
+    uint32_t frag_lo, frag_hi;     // per lane: LDS offsets of its fragment halves inside a 2 KB tile
+    const float *a_scale;
+    int64_t s_stride;  // As elements between K-blocks
+    uint32_t s_off;
+    const float *w_scale;
+    uint32_t b_off;
+
+    v4f acc[kMT][kNS];
+    v4f part[kRing];   // MFMA n -> part[n % kRing]
+    float scl[kRing];  // its As * Bs
+
+    __device__ __forceinline__ void issue_w(int s) {
+        uint8_t *dst = lds + P::kWOff + (s % P::kRW) * P::kWStage;
+#pragma unroll
+        for (int i = 0; i < P::kNW; ++i)
+            __builtin_amdgcn_global_load_lds(wbase[i] + s * kBlk + w_off, dst + wslot[i] * P::kSlot, 16, 0, 0);
+    }
+
+    __device__ __forceinline__ void issue_a(int s) {
+        uint8_t *dst = lds + P::kAOff + (s % P::kRA) * P::kAStage + wave * kMT * 2 * P::kSlot;
+        const uint8_t *src = a + s * kBlk;
+#pragma unroll
+        for (int j = 0; j < kMT; ++j) {
+            __builtin_amdgcn_global_load_lds(src + a_off[j][0], dst + (2 * j) * P::kSlot, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(src + a_off[j][1], dst + (2 * j + 1) * P::kSlot, 16, 0, 0);
+        }
+        uint8_t *sdst = lds + P::kSOff + (s % P::kRA) * P::kSStage + wave * 2 * kWave * 4;
+        const uint8_t *ssrc = reinterpret_cast<const uint8_t *>(a_scale + s * s_stride);
+        __builtin_amdgcn_global_load_lds(ssrc + s_off, sdst, 4, 0, 0);
+        const uint8_t *bsrc = reinterpret_cast<const uint8_t *>(w_scale + s);
+        __builtin_amdgcn_global_load_lds(bsrc + b_off, sdst + kWave * 4, 4, 0, 0);
+    }
+
+    // The wait counts assume exactly this issue order (activations, then
+    // weights, stage by stage); the scheduling barriers keep the compiler
+    // from interleaving the groups.
+    __device__ __forceinline__ void prologue() {
+#pragma unroll
+        for (int s = 0; s < cmax(P::kRW, P::kRA); ++s) {
+            if (s < P::kRA && s < kKB)
+                issue_a(s);
+            __builtin_amdgcn_sched_barrier(0);
+            if (s < P::kRW && s < kKB)
+                issue_w(s);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    // fold MFMA n (sequence order: K-block, subtile, m-tile) into its accumulator
+    __device__ __forceinline__ void fold(int n) {
+        const int j = n % kMT, t = (n / kMT) % kNS, r = n % kRing;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            acc[j][t][i] = fmaf(part[r][i], scl[r], acc[j][t][i]);
+    }
+
+    // Fragments of one stage, in registers.  Two sets: the MFMAs of stage
+    // kb read set kb % 2 while the LDS reads of stage kb + 1 fill the other,
+    // so LDS latency hides behind a whole K-block of matrix-core work.
+    v8i af[2][kMT];
+    float asv[2][kMT];
+    v8i wfs[2][kNS];
+    float bss[2][kNS];
+
+    // Waits until stage st is in LDS for every wave (this wave's loads have
+    // landed, every wave has passed the barrier) -- which also means every
+    // wave has finished reading stage st - 1 into registers.
+    template <int st>
+    __device__ __forceinline__ void arrive() {
+        wait_vmcnt<P::vm_wait(st)>();
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are done
+        __builtin_amdgcn_s_barrier();
+    }
+
+    template <int st>
+    __device__ __forceinline__ void read_frags() {
+        constexpr int b = st & 1;
+        const uint8_t *ws = lds + P::kWOff + (st % P::kRW) * P::kWStage;
+        const uint8_t *as = lds + P::kAOff + (st % P::kRA) * P::kAStage + wave * kMT * 2 * P::kSlot;
+        const float *ss = reinterpret_cast<const float *>(lds + P::kSOff + (st % P::kRA) * P::kSStage) +
+                          wave * 2 * kWave;
+#pragma unroll
+        for (int j = 0; j < kMT; ++j) {
+            af[b][j] = join4(*reinterpret_cast<const v4u32 *>(as + (2 * j) * P::kSlot + frag_lo),
+                             *reinterpret_cast<const v4u32 *>(as + (2 * j) * P::kSlot + frag_hi));
+            asv[b][j] = ss[16 * j + (lane & 15)];
+        }
+#pragma unroll
+        for (int t = 0; t < kNS; ++t) {
+            wfs[b][t] = join4(*reinterpret_cast<const v4u32 *>(ws + (2 * t) * P::kSlot + frag_lo),
+                              *reinterpret_cast<const v4u32 *>(ws + (2 * t) * P::kSlot + frag_hi));
+            bss[b][t] = ss[kWave + t];  // same address in every lane: broadcast read
+        }
+    }
+
+    template <int kb>
+    __device__ __forceinline__ void kblock() {
+        if constexpr (kb + 1 < kKB) {
+            arrive<kb + 1>();
+            // the stages of K-block kb are in registers: refill their slots
+            if constexpr (kb + P::kRA < kKB)
+                issue_a(kb + P::kRA);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (kb + P::kRW < kKB)
+                issue_w(kb + P::kRW);
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags<kb + 1>();
+        }
+        constexpr int b = kb & 1;
+#pragma unroll
+        for (int t = 0; t < kNS; ++t) {
+#pragma unroll
+            for (int j = 0; j < kMT; ++j) {
+                const int n = (kb * kNS + t) * kMT + j;
+                part[n % kRing] = mfma_e4m3_16x16x128(wfs[b][t], af[b][j]);
+                scl[n % kRing] = asv[b][j] * bss[b][t];
+                if (n >= kLag) {
+                    fold(n - kLag);
+                    // the next MFMA reads af[] after this asm, so it stays
+                    // behind these FMAs (VALU work in the matrix core's shadow)
+                    v4f &folded = acc[(n - kLag) % kMT][((n - kLag) / kMT) % kNS];
+                    asm volatile("" : "+v"(af[b][(j + 1) % kMT]), "+v"(folded));
+                }
+            }
+        }
+        if constexpr (kb + 1 < kKB)
+            kblock<kb + 1>();
+    }
+};
+
+template <int kKB, int kNS, int kMT, int kWaves>
+__global__ __launch_bounds__(kWaves * kWave) void block_scaled_fp8_gemm_wide_kernel(GemmParams p) {
+    using W = WideWave<kKB, kNS, kMT, kWaves>;
     extern __shared__ uint4 s_dyn[];
-    uint4 *s_act = s_dyn;                                                   // [kb][mt][half][lane]
-    float *s_as = reinterpret_cast<float *>(s_dyn + kKB * kMT * 2 * kWave);  // [kb][64 rows]
-
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: scalar addressing
-    const int waves = blockDim.x / kWave;
+    W w;
+    w.lds = reinterpret_cast<uint8_t *>(s_dyn);
+    w.lane = threadIdx.x & (kWave - 1);
+    w.wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: LDS slot bases
+    const int lane = w.lane, wave = w.wave;
     const int64_t M = p.M, K = p.K;
-    const int64_t S = p.N / 16;  // 16-row weight subtiles
-    const int64_t st = static_cast<int64_t>(blockIdx.x) * subtiles_per_block + wave;
-    const bool active = wave < subtiles_per_block && st < S;
-    const int64_t n0 = st * 16;
+    const int64_t S = p.N / 16;
+    const int64_t st0 = static_cast<int64_t>(blockIdx.x) * kNS;
+    const int m_base = wave * 16 * kMT;
 
-    float bs[kKB];  // the subtile's weight scales (one 128-row block)
-    if (active) {
-        const float *bs_row = p.w_scale + (n0 / kBlk) * kKB;
-#pragma unroll
-        for (int kb = 0; kb < kKB; ++kb)
-            bs[kb] = bs_row[kb];
+    // LDS tiles.  A 16-row x 128-byte K-block tile of either operand takes
+    // 2 KB: rows 8g..8g+7 fill the 1 KB slot g, row r of the slot at 128 r,
+    // and its 16-byte chunk c sits at position c ^ f, f = r ^ g.  One direct
+    // load fills one slot: lane l fetches row l / 8, chunk (l % 8) ^ f, so
+    // each load reads 8 whole cache lines.  The MFMA fragment of lane L is
+    // row L % 16, chunks 2 (L / 16) and 2 (L / 16) + 1 (the same K order for
+    // both operands); with the XOR the 8 (or 16) lanes that read LDS together
+    // hit distinct banks.
+    {
+        const int rho = lane & 15, g = rho >> 3, r = rho & 7, q = lane >> 4;
+        w.frag_lo = static_cast<uint32_t>(g * 1024 + r * 128 + (((2 * q) ^ (r ^ g)) * 16));
+        w.frag_hi = static_cast<uint32_t>(g * 1024 + r * 128 + (((2 * q + 1) ^ (r ^ g)) * 16));
     }
-    stage_chunk<kMT, kKB>(p, 0, s_act, s_as, wave, waves, lane);
-    // The fences keep the program order of the memory operations: scales and
-    // staging loads, then the weight burst, then the wait.  Loads complete in
-    // issue order, so waiting until only the burst is outstanding means this
-    // wave's staging loads have landed in LDS.
-    asm volatile("" ::: "memory");
-    v8i wf[kKB];
-    if (active) {
-        const uint8_t *wrow = p.w + (n0 + (lane & 15)) * K + 32 * (lane >> 4);
+    const int lrow = lane >> 3, lchunk = lane & 7;  // this lane's part of one direct load
+    // Sources: a uniform base per load plus a 32-bit per-lane offset.
+    // Subtiles past the end of W repeat the last one and rows at or beyond M
+    // repeat row M - 1: their results are never stored.
+    // Weight slot (subtile, row half) = (slot / 2, slot % 2); this wave loads
+    // slots (wave + kWaves i) mod 2 kNS, all of row half wave % 2.
+    {
+        const int g = wave & 1;
+        w.w_off = static_cast<uint32_t>((8 * g + lrow) * K + 16 * (lchunk ^ lrow ^ g));
+    }
 #pragma unroll
-        for (int kb = 0; kb < kKB; ++kb) {
-            const uint4 *src = reinterpret_cast<const uint4 *>(wrow + kb * kBlk);
-            wf[kb] = join(src[0], src[1]);
+    for (int i = 0; i < W::P::kNW; ++i) {
+        const int slot = (wave + kWaves * i) % (2 * kNS);
+        const int64_t st = min<int64_t>(st0 + (slot >> 1), S - 1);
+        w.wslot[i] = slot;
+        w.wbase[i] = p.w + st * 16 * K;
+    }
+    w.a = p.a;
+#pragma unroll
+    for (int j = 0; j < kMT; ++j)
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            const int64_t r = min<int64_t>(m_base + 16 * j + 8 * g + lrow, M - 1);
+            w.a_off[j][g] = static_cast<uint32_t>(r * K + 16 * (lchunk ^ lrow ^ g));
         }
-        asm volatile("" ::: "memory");
-        wait_vmcnt<2 * kKB>();
-    } else {
-        wait_vmcnt<0>();
-    }
-    // A bare barrier: the LDS data is visible once every wave's own staging
-    // loads have landed (waited for above).  __syncthreads() would add a
-    // release fence that drains the whole weight burst first.
-    __builtin_amdgcn_s_barrier();
-    if (active)
-        compute_chunk<kMT, kKB>(p, 0, n0, lane, s_act, s_as, wf, bs);
+    // lane l: As of row m_base + l (rows past this wave's or past M repeat)
+    const int64_t srow = min<int64_t>(m_base + min(lane, 16 * kMT - 1), M - 1);
+    w.a_scale = p.a_scale;
+    w.s_off = static_cast<uint32_t>(4 * (p.a_scale_transposed ? srow : srow * kKB));
+    w.s_stride = p.a_scale_transposed ? M : 1;
+    // lane t < kNS: the 128x128 block-scale row of subtile t (other lanes
+    // repeat the last subtile)
+    const int64_t bst = min<int64_t>(st0 + min(lane, kNS - 1), S - 1);
+    w.w_scale = p.w_scale;
+    w.b_off = static_cast<uint32_t>(4 * ((bst * 16) / kBlk) * kKB);
 
-    for (int64_t m0 = kChunkRows; m0 < M; m0 += kChunkRows) {
-        __syncthreads();  // every wave is done reading the previous chunk
-        stage_chunk<kMT, kKB>(p, m0, s_act, s_as, wave, waves, lane);
-        wait_vmcnt<0>();
-        __syncthreads();
-        if (active)
-            compute_chunk<kMT, kKB>(p, m0, n0, lane, s_act, s_as, wf, bs);
+    w.prologue();
+#pragma unroll
+    for (int j = 0; j < kMT; ++j)
+#pragma unroll
+        for (int t = 0; t < kNS; ++t)
+            w.acc[j][t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    w.template arrive<0>();
+    w.template read_frags<0>();
+    w.template kblock<0>();
+#pragma unroll
+    for (int n = W::kSeq - W::kLag; n < W::kSeq; ++n)
+        w.fold(n);
+
+    // Output: lane holds out[m_base + 16j + L%16][16 (st0 + t) + 4 (L/16) + i].
+    // The wave's tile (16 kMT rows x 16 kNS columns, bf16) goes through LDS
+    // so that every row leaves as contiguous 16-byte pieces (8-byte pieces
+    // scattered over 16 rows per store make partial cache-line writes), with
+    // non-temporal stores (measured: cheaper than plain ones here).
+    // The rings are free once every wave has passed this barrier.
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    constexpr int kCols = 16 * kNS;
+    static_assert(kWaves * 16 * kMT * kCols * 2 <= W::P::kLds, "output tiles fit in the rings' LDS");
+    static_assert((16 * kMT * 2 * kNS) % kWave == 0, "whole pieces per lane");
+    uint16_t *tile = reinterpret_cast<uint16_t *>(w.lds) + wave * (16 * kMT) * kCols;
+#pragma unroll
+    for (int j = 0; j < kMT; ++j)
+#pragma unroll
+        for (int t = 0; t < kNS; ++t)
+            *reinterpret_cast<uint2 *>(tile + (16 * j + (lane & 15)) * kCols + 16 * t + 4 * (lane >> 4)) =
+                make_uint2(pack2_bf16(w.acc[j][t][0], w.acc[j][t][1]), pack2_bf16(w.acc[j][t][2], w.acc[j][t][3]));
+    constexpr int kPieces = 2 * kNS;  // 16-byte pieces per row
+#pragma unroll
+    for (int i = 0; i < (16 * kMT * kPieces) / kWave; ++i) {
+        const int pc = lane + i * kWave;
+        const int row = pc / kPieces, col = 8 * (pc % kPieces);
+        const int64_t m = m_base + row;
+        const v4u32 v = *reinterpret_cast<const v4u32 *>(tile + row * kCols + col);
+        if (m < M && st0 + col / 16 < S)  // streaming store: the output is not read back here
+            __builtin_nontemporal_store(v, reinterpret_cast<v4u32 *>(p.out + m * p.N + st0 * 16 + col));
     }
+}
+
+// The dynamic-LDS limit is a per-device function attribute: remember, per
+// kernel instance, on which devices it has been raised.
+template <typename Kern>
+hipError_t allow_dynamic_lds(Kern kern, size_t lds, std::atomic<uint64_t> &done) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t{1} << dev) : 0;
+    if (bit && (done.load(std::memory_order_acquire) & bit))
+        return hipSuccess;
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(lds));
+    if (e == hipSuccess && bit)
+        done.fetch_or(bit, std::memory_order_acq_rel);
+    return e;
 }
 
 int device_cu_count() {
@@ -512,7 +691,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void block_scaled_fp8_gemm_de
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 acc[t][i] = fmaf(part[t][i], sc[t], acc[t][i]);
-            // see compute_chunk: keeps the FMAs of K-block kb ahead of the
+            // keeps the FMAs of K-block kb ahead of the
             // MFMAs of K-block kb + 1
             asm volatile("" : "+v"(acc[t]), "+v"(lo[t].x), "+v"(lo[t].y), "+v"(lo[t].z), "+v"(lo[t].w),
                          "+v"(hi[t].x), "+v"(hi[t].y), "+v"(hi[t].z), "+v"(hi[t].w), "+v"(as_m[t]));
@@ -552,14 +731,10 @@ hipError_t launch_decode(const GemmParams &p, hipStream_t stream) {
                        static_cast<size_t>(2 * kDecodeWaves) * kWave * sizeof(float) +
                        static_cast<size_t>(kChunkRows) * 16 * kDecodeWaves * sizeof(uint16_t);
     auto kern = block_scaled_fp8_gemm_decode_kernel<kMT, kKB>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-        if (e != hipSuccess)
-            return e;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    const hipError_t e = allow_dynamic_lds(kern, lds, lds_set);
+    if (e != hipSuccess)
+        return e;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kDecodeWaves * kWave), lds, stream, p, spb);
     return hipGetLastError();
 }
@@ -575,41 +750,45 @@ hipError_t launch_decode_kb(const GemmParams &p, hipStream_t stream) {
     return launch_decode<4, kKB>(p, stream);
 }
 
-template <int kMT, int kKB>
-hipError_t launch_stream(const GemmParams &p, hipStream_t stream) {
-    // one subtile per wave, at most 8 waves per block, at least one block per CU
-    const int64_t S = p.N / 16;
-    const int64_t cus = device_cu_count();
-    int spb = static_cast<int>(std::min<int64_t>(kStreamMaxWaves, (S + cus - 1) / cus));
-    const int64_t blocks = (S + spb - 1) / spb;
-    if (blocks > 0x7FFFFFFF)
+template <int kKB, int kNS, int kMT, int kWaves>
+hipError_t launch_wide(const GemmParams &p, hipStream_t stream) {
+    using P = WidePlan<kKB, kNS, kMT, kWaves>;
+    const int64_t blocks = (p.N / 16 + kNS - 1) / kNS;
+    if (blocks > 0x7FFFFFFF || p.M > kWaves * 16 * kMT)
         return hipErrorInvalidValue;
-    const int waves = std::max(4, spb);  // spare waves only help stage the activations
-    const size_t lds = static_cast<size_t>(kKB) * kMT * 2 * kWave * sizeof(uint4) +
-                       static_cast<size_t>(kKB) * kWave * sizeof(float);
-    auto kern = block_scaled_fp8_gemm_stream_kernel<kMT, kKB>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-        if (e != hipSuccess)
-            return e;
-        attr_set = true;
-    }
-    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(waves * kWave), lds, stream, p, spb);
+    auto kern = block_scaled_fp8_gemm_wide_kernel<kKB, kNS, kMT, kWaves>;
+    static std::atomic<uint64_t> lds_set{0};
+    const hipError_t e = allow_dynamic_lds(kern, P::kLds, lds_set);
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kWaves * kWave), P::kLds, stream, p);
     return hipGetLastError();
 }
 
+template <int kKB, int kMT>
+hipError_t launch_wide_ns(const GemmParams &p, hipStream_t stream) {
+    // subtiles per block: the smallest even count that covers N with one
+    // block per CU; beyond 6 per CU (registers: two fragment sets) the grid
+    // simply has more blocks than CUs
+    const int64_t per_cu = (p.N / 16 + device_cu_count() - 1) / device_cu_count();
+    if (per_cu <= 2)
+        return launch_wide<kKB, 2, kMT, kWideWaves>(p, stream);
+    if (per_cu <= 4)
+        return launch_wide<kKB, 4, kMT, kWideWaves>(p, stream);
+    return launch_wide<kKB, 6, kMT, kWideWaves>(p, stream);
+}
+
 template <int kKB>
-hipError_t launch_stream_kb(const GemmParams &p, hipStream_t stream) {
-    // m-tiles per 64-row chunk: only the M <= 48 cases stage less than 4
-    if (p.M <= 16)
-        return launch_stream<1, kKB>(p, stream);
-    if (p.M <= 32)
-        return launch_stream<2, kKB>(p, stream);
-    if (p.M <= 48)
-        return launch_stream<3, kKB>(p, stream);
-    return launch_stream<4, kKB>(p, stream);
+hipError_t launch_wide_kb(const GemmParams &p, hipStream_t stream) {
+    // kWideWaves x 16 kMT rows cover M (at most 256)
+    if (p.M <= kWideWaves * 16)
+        return launch_wide_ns<kKB, 1>(p, stream);
+    if constexpr (kWideWaves * 32 >= 256)
+        return launch_wide_ns<kKB, 2>(p, stream);
+    else if (p.M <= kWideWaves * 32)
+        return launch_wide_ns<kKB, 2>(p, stream);
+    else
+        return launch_wide_ns<kKB, 256 / (16 * kWideWaves)>(p, stream);
 }
 
 template <int kMT>
@@ -641,17 +820,17 @@ hipError_t launch_block_scaled_gemm(const GemmParams &p, hipStream_t stream) {
             break;
         }
     }
-    // Up to 256 rows: stream the weights once, activations through LDS.
+    // Up to 256 rows: weight slab per block, everything staged through LDS.
     if (p.M <= 4 * kChunkRows) {
         switch (p.K / kBlk) {
         case 4:
-            return launch_stream_kb<4>(p, stream);
+            return launch_wide_kb<4>(p, stream);
         case 8:
-            return launch_stream_kb<8>(p, stream);
+            return launch_wide_kb<8>(p, stream);
         case 12:
-            return launch_stream_kb<12>(p, stream);
+            return launch_wide_kb<12>(p, stream);
         case 16:
-            return launch_stream_kb<16>(p, stream);
+            return launch_wide_kb<16>(p, stream);
         default:
             break;
         }

@@ -76,6 +76,33 @@ def test_gemm_random_vs_oracle(M, N, K, seed):
     assert np.array_equal(again, outs[0])
 
 
+@pytest.mark.parametrize("M,N,K,seed", [(65, 384, 512, 21), (129, 1280, 1024, 22), (100, 1536, 1536, 23),
+                                        (256, 16640, 1536, 24), (72, 32768, 512, 25), (200, 12288, 1536, 26),
+                                        (256, 8192, 2048, 27), (256, 24576, 1536, 28)])
+def test_gemm_wide_shapes_sampled(M, N, K, seed):
+    """64 < M <= 256 at widths that give 2, 4, 6 and 8 weight subtiles per
+    block, with a ragged last block (N = 16640: 1040 subtiles in blocks of 6).
+    The oracle runs on the first, the last and two random 128-column blocks."""
+    dev = gpu_or_skip()
+    a, As, w, Bs = random_operands(M, N, K, seed)
+    nb = N // 128
+    r = np.random.default_rng(seed)
+    blocks = np.unique(np.concatenate([[0, nb - 1], r.choice(nb, size=min(2, nb), replace=False)]))
+    cols = (blocks[:, None] * 128 + np.arange(128)[None, :]).reshape(-1)
+    ref = oracle.block_scaled_fp8_gemm(a, As.reshape(-1), False, w[cols], Bs[blocks])
+    mag = (np.abs(oracle.e4m3_decode_array(a)) * np.repeat(As.astype(np.float64), 128, axis=1)) @ \
+        (np.abs(oracle.e4m3_decode_array(w[cols])) * np.kron(Bs[blocks].astype(np.float64), np.ones((128, 128)))).T
+    outs = []
+    for t in (False, True):
+        out = run_gemm(a, As, w, Bs, t, dev)
+        got = bf16_to_f64(out)[:, cols]
+        assert_gemm_close(got, ref, f"M{M} N{N} K{K} t{t}")
+        err = np.abs(got - ref)
+        assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 2.0 ** -12 * mag), f"M{M} N{N} K{K} t{t}"
+        outs.append(host_bf16_bits(out))
+    assert np.array_equal(outs[0], outs[1]), "row- and column-major As must give identical bits"
+
+
 def test_one_hot_weights_closed_form():
     """W row n = 1.0 at column k_n, Bs = 1: out[m, n] = bf16(dec(a[m, k_n]) *
     As[m, k_n / 128]) exactly."""
