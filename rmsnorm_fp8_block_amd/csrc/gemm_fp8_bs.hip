@@ -156,7 +156,8 @@ __global__ __launch_bounds__(256) void block_scaled_fp8_gemm_kernel(GemmParams p
     }
 }
 
-constexpr int kChunkRows = 64;  // activation rows of the decode kernel
+constexpr int kChunkRows = 64;      // activation rows the decode kernel can hold
+constexpr int kDecodeMaxRows = 32;  // batches it is used for (measured crossover)
 
 // vmcnt-only waits (gfx9 encoding: vmcnt[3:0] + vmcnt[5:4] at bits 15:14,
 // expcnt 6:4 and lgkmcnt 11:8 left at their maxima = no wait)
@@ -189,7 +190,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 // of stage kb.  The scale FMAs of an MFMA are issued two MFMAs later, in
 // the matrix core's shadow.
 // ---------------------------------------------------------------------------
-constexpr int kWideWaves = 8;  // 2 per SIMD
+constexpr int kWideWaves = 4;  // 1 per SIMD
 
 constexpr int cmin(int a, int b) { return a < b ? a : b; }
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
@@ -713,9 +714,9 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void block_scaled_fp8_gemm_de
     // only columns of existing subtiles (< N) are read back; those were written
     for (int pi = threadIdx.x; pi < M * pieces_per_row; pi += blockDim.x) {
         const int m = pi / pieces_per_row, part = pi % pieces_per_row;
-        if (blk_n0 + part * 8 < p.N)
-            *reinterpret_cast<uint4 *>(p.out + m * p.N + blk_n0 + part * 8) =
-                *reinterpret_cast<const uint4 *>(s_out + m * cols + part * 8);
+        if (blk_n0 + part * 8 < p.N)  // streaming store: the output is not read back here
+            __builtin_nontemporal_store(*reinterpret_cast<const v4u32 *>(s_out + m * cols + part * 8),
+                                        reinterpret_cast<v4u32 *>(p.out + m * p.N + blk_n0 + part * 8));
     }
 }
 
@@ -805,8 +806,9 @@ hipError_t launch_mt(const GemmParams &p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_block_scaled_gemm(const GemmParams &p, hipStream_t stream) {
-    // Decode batches: weight ring per wave, activations resident in LDS.
-    if (p.M <= kChunkRows) {
+    // Small decode batches over wide weights (more than 4 subtiles per CU):
+    // weight ring per wave, activations resident in LDS.
+    if (p.M <= kDecodeMaxRows && p.N / 16 > 4 * static_cast<int64_t>(device_cu_count())) {
         switch (p.K / kBlk) {
         case 4:
             return launch_decode_kb<4>(p, stream);
@@ -820,7 +822,8 @@ hipError_t launch_block_scaled_gemm(const GemmParams &p, hipStream_t stream) {
             break;
         }
     }
-    // Up to 256 rows: weight slab per block, everything staged through LDS.
+    // Up to 256 rows: weight slab per block, everything streamed through
+    // LDS rings.
     if (p.M <= 4 * kChunkRows) {
         switch (p.K / kBlk) {
         case 4:
