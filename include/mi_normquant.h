@@ -134,6 +134,32 @@ mi_status mi_block_scaled_fp8_gemm(
     hipStream_t stream);
 
 /*
+ * mi_block_scaled_fp8_gemm_pair
+ *
+ * [PR53540] "Purpose": the attention wq_b and the indexer wq_b both consume
+ * the same pre-quantised (q_fp8, scale) pair.  This computes both consumers
+ * in one call: out1 = the block-scaled GEMM of the pair with (w1, w1_scale),
+ * out2 = the same with (w2, w2_scale), each exactly as
+ * mi_block_scaled_fp8_gemm defines it (bit-identical results).  One launch
+ * streams both weights and stages the shared activations once per compute
+ * unit; shapes the fused kernel does not cover (M > 64, or K / 128 not in
+ * {4, 8, 12, 16}) are run as two launches of mi_block_scaled_fp8_gemm on the
+ * same stream.
+ *
+ * a_fp8, a_scale, a_scale_transposed, M, K: as in mi_block_scaled_fp8_gemm.
+ * w1_fp8, w1_scale, out1_bf16, N1: first consumer ([N1, K], [N1/128, K/128],
+ *                    [M, N1]); w2_fp8, w2_scale, out2_bf16, N2: second.
+ * N1 % 128 == 0, N2 % 128 == 0, N1 > 0, N2 > 0; the same alignment rules.
+ * The two outputs must not overlap each other or any input.
+ */
+mi_status mi_block_scaled_fp8_gemm_pair(
+    const uint8_t *a_fp8, const float *a_scale, int a_scale_transposed,
+    const uint8_t *w1_fp8, const float *w1_scale, uint16_t *out1_bf16, int64_t N1,
+    const uint8_t *w2_fp8, const float *w2_scale, uint16_t *out2_bf16, int64_t N2,
+    int64_t M, int64_t K,
+    hipStream_t stream);
+
+/*
  * mi_negotiate_scale_layout
  *
  * [D56433] item 4: the producer writes one scale buffer for several

@@ -12,10 +12,12 @@ from ._binding import (  # noqa: F401
     MiError,
     lib,
     mi_block_scaled_fp8_gemm,
+    mi_block_scaled_fp8_gemm_pair,
     mi_fused_dual_rmsnorm_group_quant,
     mi_negotiate_scale_layout,
     mi_status_string,
     prepare_block_scaled_fp8_gemm,
+    prepare_block_scaled_fp8_gemm_pair,
     prepare_fused_dual_rmsnorm_group_quant,
     scale_is_transposed,
 )

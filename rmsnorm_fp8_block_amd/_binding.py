@@ -22,6 +22,7 @@ MI_OK, MI_ERR_NULL, MI_ERR_SHAPE, MI_ERR_STRIDE, MI_ERR_ALIGN, MI_ERR_HIP = rang
 EXPORTED = (
     "mi_fused_dual_rmsnorm_group_quant",
     "mi_block_scaled_fp8_gemm",
+    "mi_block_scaled_fp8_gemm_pair",
     "mi_negotiate_scale_layout",
     "mi_status_string",
 )
@@ -50,6 +51,8 @@ def lib() -> ctypes.CDLL:
             p, i64, p, i64, p, p, ctypes.c_float, i64, i64, i64, c_int, p, p, p, p]
         L.mi_block_scaled_fp8_gemm.restype = c_int
         L.mi_block_scaled_fp8_gemm.argtypes = [p, p, c_int, p, p, p, i64, i64, i64, p]
+        L.mi_block_scaled_fp8_gemm_pair.restype = c_int
+        L.mi_block_scaled_fp8_gemm_pair.argtypes = [p, p, c_int, p, p, p, i64, p, p, p, i64, i64, i64, p]
         L.mi_negotiate_scale_layout.restype = c_int
         L.mi_negotiate_scale_layout.argtypes = [ctypes.POINTER(c_int), c_int]
         L.mi_status_string.restype = ctypes.c_char_p
@@ -176,6 +179,48 @@ def mi_block_scaled_fp8_gemm(a: torch.Tensor, a_scale: torch.Tensor,
     return out
 
 
+def _check_gemm_operands(a, a_scale, w, w_scale):
+    for name, t, dt in (("a", a, torch.uint8), ("w", w, torch.uint8),
+                        ("w_scale", w_scale, torch.float32), ("a_scale", a_scale, torch.float32)):
+        if t.dtype != dt or t.dim() != 2:
+            raise ValueError(f"{name}: expected a 2-D {dt} tensor")
+    if not (a.is_contiguous() and w.is_contiguous() and w_scale.is_contiguous()):
+        raise ValueError("a, w and w_scale must be contiguous")
+    M, K = a.shape
+    N = w.shape[0]
+    if w.shape[1] != K or tuple(a_scale.shape) != (M, K // GROUP) or \
+            tuple(w_scale.shape) != (N // GROUP, K // GROUP):
+        raise ValueError("shape mismatch between a, a_scale, w, w_scale")
+    return M, N, K
+
+
+def _gemm_out(out, M, N, device):
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=device)
+    if out.dtype != torch.bfloat16 or not out.is_contiguous() or tuple(out.shape) != (M, N):
+        raise ValueError("out must be a contiguous bf16 [M, N] tensor")
+    return out
+
+
+def mi_block_scaled_fp8_gemm_pair(a: torch.Tensor, a_scale: torch.Tensor,
+                                  w1: torch.Tensor, w1_scale: torch.Tensor,
+                                  w2: torch.Tensor, w2_scale: torch.Tensor,
+                                  out1: torch.Tensor | None = None,
+                                  out2: torch.Tensor | None = None):
+    """Both consumers of one pre-quantised pair on the current stream:
+    returns (bf16 [M, N1], bf16 [M, N2]), each equal to
+    mi_block_scaled_fp8_gemm(a, a_scale, w_i, w_i_scale)."""
+    M, N1, K = _check_gemm_operands(a, a_scale, w1, w1_scale)
+    _, N2, K2 = _check_gemm_operands(a, a_scale, w2, w2_scale)
+    out1 = _gemm_out(out1, M, N1, a.device)
+    out2 = _gemm_out(out2, M, N2, a.device)
+    status = lib().mi_block_scaled_fp8_gemm_pair(
+        _ptr(a), _ptr(a_scale), int(scale_is_transposed(a_scale)), _ptr(w1), _ptr(w1_scale), _ptr(out1), N1,
+        _ptr(w2), _ptr(w2_scale), _ptr(out2), N2, M, K, _stream(a))
+    _check("mi_block_scaled_fp8_gemm_pair", status)
+    return out1, out2
+
+
 def mi_negotiate_scale_layout(consumer_wants_transposed) -> bool | None:
     """True / False when every consumer wants column-major / row-major
     scales, None when they disagree (do not share one quantised pair)."""
@@ -231,3 +276,15 @@ def prepare_block_scaled_fp8_gemm(a, a_scale, w, w_scale, out) -> PreparedCall:
     args = (_ptr(a), _ptr(a_scale), int(scale_is_transposed(a_scale)), _ptr(w), _ptr(w_scale),
             _ptr(out), M, N, K)
     return PreparedCall("mi_block_scaled_fp8_gemm", args, (a, a_scale, w, w_scale, out), a.device)
+
+
+def prepare_block_scaled_fp8_gemm_pair(a, a_scale, w1, w1_scale, out1, w2, w2_scale, out2) -> PreparedCall:
+    """Marshal the arguments of mi_block_scaled_fp8_gemm_pair once."""
+    M, K = a.shape
+    N1, N2 = w1.shape[0], w2.shape[0]
+    if tuple(a_scale.shape) != (M, K // GROUP) or tuple(out1.shape) != (M, N1) or tuple(out2.shape) != (M, N2):
+        raise ValueError("shape mismatch")
+    args = (_ptr(a), _ptr(a_scale), int(scale_is_transposed(a_scale)), _ptr(w1), _ptr(w1_scale), _ptr(out1), N1,
+            _ptr(w2), _ptr(w2_scale), _ptr(out2), N2, M, K)
+    return PreparedCall("mi_block_scaled_fp8_gemm_pair", args,
+                        (a, a_scale, w1, w1_scale, out1, w2, w2_scale, out2), a.device)

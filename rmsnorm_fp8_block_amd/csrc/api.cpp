@@ -77,6 +77,41 @@ extern "C" mi_status mi_block_scaled_fp8_gemm(
     return mi::launch_block_scaled_gemm(p, stream) == hipSuccess ? MI_OK : MI_ERR_HIP;
 }
 
+extern "C" mi_status mi_block_scaled_fp8_gemm_pair(
+    const uint8_t *a_fp8, const float *a_scale, int a_scale_transposed,
+    const uint8_t *w1_fp8, const float *w1_scale, uint16_t *out1_bf16, int64_t N1,
+    const uint8_t *w2_fp8, const float *w2_scale, uint16_t *out2_bf16, int64_t N2,
+    int64_t M, int64_t K,
+    hipStream_t stream) {
+    if (M < 0 || N1 <= 0 || N2 <= 0 || K <= 0 || (N1 % MI_GROUP) != 0 || (N2 % MI_GROUP) != 0 ||
+        (K % MI_GROUP) != 0)
+        return MI_ERR_SHAPE;
+    if (M == 0)
+        return MI_OK;
+    if (!a_fp8 || !a_scale || !w1_fp8 || !w1_scale || !out1_bf16 || !w2_fp8 || !w2_scale || !out2_bf16)
+        return MI_ERR_NULL;
+    if (!aligned16(a_fp8) || !aligned16(w1_fp8) || !aligned16(out1_bf16) || !aligned16(w2_fp8) ||
+        !aligned16(out2_bf16) || (reinterpret_cast<uintptr_t>(a_scale) & 3) ||
+        (reinterpret_cast<uintptr_t>(w1_scale) & 3) || (reinterpret_cast<uintptr_t>(w2_scale) & 3))
+        return MI_ERR_ALIGN;
+
+    mi::GemmParams p;
+    p.a = a_fp8;
+    p.a_scale = a_scale;
+    p.a_scale_transposed = a_scale_transposed ? 1 : 0;
+    p.w = w1_fp8;
+    p.w_scale = w1_scale;
+    p.out = out1_bf16;
+    p.M = M;
+    p.N = N1;
+    p.K = K;
+    p.w2 = w2_fp8;
+    p.w_scale2 = w2_scale;
+    p.out2 = out2_bf16;
+    p.N2 = N2;
+    return mi::launch_block_scaled_gemm_pair(p, stream) == hipSuccess ? MI_OK : MI_ERR_HIP;
+}
+
 extern "C" int mi_negotiate_scale_layout(const int *consumer_wants_transposed, int n) {
     if (!consumer_wants_transposed || n <= 0)
         return -1;

@@ -195,9 +195,28 @@ constexpr int kWideWaves = 4;  // 1 per SIMD
 constexpr int cmin(int a, int b) { return a < b ? a : b; }
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
+// 16-row weight subtile st of the (one or two) consumers: the subtiles of
+// p.w come first, then those of p.w2.  All fields uniform when st is.
+struct SubTile {
+    const uint8_t *w;   // first weight row of the subtile
+    const float *ws;    // its row of 128x128 block scales
+    uint16_t *out;      // output of its consumer
+    int64_t n0;         // its first output column
+    int64_t ldo;        // row stride of that output
+};
+
+__device__ __forceinline__ SubTile subtile(const GemmParams &p, int64_t st) {
+    const int64_t S1 = p.N / 16, KB = p.K / kBlk;
+    if (st < S1)
+        return {p.w + st * 16 * p.K, p.w_scale + (st * 16 / kBlk) * KB, p.out, st * 16, p.N};
+    const int64_t l = st - S1;
+    return {p.w2 + l * 16 * p.K, p.w_scale2 + (l * 16 / kBlk) * KB, p.out2, l * 16, p.N2};
+}
+
 template <int kKB, int kNS, int kMT, int kWaves>
 struct WidePlan {
-    static_assert(kNS % 2 == 0 && kNS >= 2 && kNS <= 6, "whole 2-slot subtiles; two fragment sets fit the registers");
+    static_assert(kNS % 2 == 0 && kNS >= 2 && kNS <= (kMT == 1 ? 8 : 6),
+                  "whole 2-slot subtiles; two fragment sets fit the registers");
     static_assert(kWaves == 4 || kWaves == 8, "4 or 8 waves");
     static_assert(kMT >= 1 && kMT * kWaves * 16 <= 256, "at most 256 rows");
     static constexpr int kSlot = 1024;                         // 8 rows x 128 bytes
@@ -281,8 +300,7 @@ struct WideWave {
     const float *a_scale;
     int64_t s_stride;  // As elements between K-blocks
     uint32_t s_off;
-    const float *w_scale;
-    uint32_t b_off;
+    const float *bsrc;  // per lane: block-scale row of subtile lane (lanes >= kNS repeat the last)
 
     v4f acc[kMT][kNS];
     v4f part[kRing];   // MFMA n -> part[n % kRing]
@@ -306,8 +324,7 @@ struct WideWave {
         uint8_t *sdst = lds + P::kSOff + (s % P::kRA) * P::kSStage + wave * 2 * kWave * 4;
         const uint8_t *ssrc = reinterpret_cast<const uint8_t *>(a_scale + s * s_stride);
         __builtin_amdgcn_global_load_lds(ssrc + s_off, sdst, 4, 0, 0);
-        const uint8_t *bsrc = reinterpret_cast<const uint8_t *>(w_scale + s);
-        __builtin_amdgcn_global_load_lds(bsrc + b_off, sdst + kWave * 4, 4, 0, 0);
+        __builtin_amdgcn_global_load_lds(bsrc + s, sdst + kWave * 4, 4, 0, 0);
     }
 
     // The wait counts assume exactly this issue order (activations, then
@@ -417,7 +434,7 @@ __global__ __launch_bounds__(kWaves * kWave) void block_scaled_fp8_gemm_wide_ker
     w.wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: LDS slot bases
     const int lane = w.lane, wave = w.wave;
     const int64_t M = p.M, K = p.K;
-    const int64_t S = p.N / 16;
+    const int64_t S = (p.N + p.N2) / 16;  // subtiles of both consumers
     const int64_t st0 = static_cast<int64_t>(blockIdx.x) * kNS;
     const int m_base = wave * 16 * kMT;
 
@@ -447,9 +464,8 @@ __global__ __launch_bounds__(kWaves * kWave) void block_scaled_fp8_gemm_wide_ker
 #pragma unroll
     for (int i = 0; i < W::P::kNW; ++i) {
         const int slot = (wave + kWaves * i) % (2 * kNS);
-        const int64_t st = min<int64_t>(st0 + (slot >> 1), S - 1);
         w.wslot[i] = slot;
-        w.wbase[i] = p.w + st * 16 * K;
+        w.wbase[i] = subtile(p, min<int64_t>(st0 + (slot >> 1), S - 1)).w;
     }
     w.a = p.a;
 #pragma unroll
@@ -466,9 +482,7 @@ __global__ __launch_bounds__(kWaves * kWave) void block_scaled_fp8_gemm_wide_ker
     w.s_stride = p.a_scale_transposed ? M : 1;
     // lane t < kNS: the 128x128 block-scale row of subtile t (other lanes
     // repeat the last subtile)
-    const int64_t bst = min<int64_t>(st0 + min(lane, kNS - 1), S - 1);
-    w.w_scale = p.w_scale;
-    w.b_off = static_cast<uint32_t>(4 * ((bst * 16) / kBlk) * kKB);
+    w.bsrc = subtile(p, min<int64_t>(st0 + min(lane, kNS - 1), S - 1)).ws;
 
     w.prologue();
 #pragma unroll
@@ -506,10 +520,12 @@ __global__ __launch_bounds__(kWaves * kWave) void block_scaled_fp8_gemm_wide_ker
     for (int i = 0; i < (16 * kMT * kPieces) / kWave; ++i) {
         const int pc = lane + i * kWave;
         const int row = pc / kPieces, col = 8 * (pc % kPieces);
-        const int64_t m = m_base + row;
+        const int64_t m = m_base + row, st = st0 + col / 16;
         const v4u32 v = *reinterpret_cast<const v4u32 *>(tile + row * kCols + col);
-        if (m < M && st0 + col / 16 < S)  // streaming store: the output is not read back here
-            __builtin_nontemporal_store(v, reinterpret_cast<v4u32 *>(p.out + m * p.N + st0 * 16 + col));
+        if (m < M && st < S) {  // streaming store: the output is not read back here
+            const SubTile sub = subtile(p, st);
+            __builtin_nontemporal_store(v, reinterpret_cast<v4u32 *>(sub.out + m * sub.ldo + sub.n0 + col % 16));
+        }
     }
 }
 
@@ -754,7 +770,7 @@ hipError_t launch_decode_kb(const GemmParams &p, hipStream_t stream) {
 template <int kKB, int kNS, int kMT, int kWaves>
 hipError_t launch_wide(const GemmParams &p, hipStream_t stream) {
     using P = WidePlan<kKB, kNS, kMT, kWaves>;
-    const int64_t blocks = (p.N / 16 + kNS - 1) / kNS;
+    const int64_t blocks = ((p.N + p.N2) / 16 + kNS - 1) / kNS;
     if (blocks > 0x7FFFFFFF || p.M > kWaves * 16 * kMT)
         return hipErrorInvalidValue;
     auto kern = block_scaled_fp8_gemm_wide_kernel<kKB, kNS, kMT, kWaves>;
@@ -768,14 +784,18 @@ hipError_t launch_wide(const GemmParams &p, hipStream_t stream) {
 
 template <int kKB, int kMT>
 hipError_t launch_wide_ns(const GemmParams &p, hipStream_t stream) {
-    // subtiles per block: the smallest even count that covers N with one
-    // block per CU; beyond 6 per CU (registers: two fragment sets) the grid
-    // simply has more blocks than CUs
-    const int64_t per_cu = (p.N / 16 + device_cu_count() - 1) / device_cu_count();
+    // subtiles per block: the smallest even count that covers N (+ N2) with
+    // one block per CU; beyond 6 per CU (8 with one 16-row tile per wave)
+    // the grid simply has more blocks than CUs (registers: two fragment sets)
+    const int64_t per_cu = ((p.N + p.N2) / 16 + device_cu_count() - 1) / device_cu_count();
     if (per_cu <= 2)
         return launch_wide<kKB, 2, kMT, kWideWaves>(p, stream);
     if (per_cu <= 4)
         return launch_wide<kKB, 4, kMT, kWideWaves>(p, stream);
+    if constexpr (kMT == 1) {
+        if (per_cu > 6)
+            return launch_wide<kKB, 8, kMT, kWideWaves>(p, stream);
+    }
     return launch_wide<kKB, 6, kMT, kWideWaves>(p, stream);
 }
 
@@ -846,6 +866,40 @@ hipError_t launch_block_scaled_gemm(const GemmParams &p, hipStream_t stream) {
     if (p.M <= 48)
         return launch_mt<3>(p, stream);
     return launch_mt<4>(p, stream);
+}
+
+hipError_t launch_block_scaled_gemm_pair(const GemmParams &p, hipStream_t stream) {
+    // decode batches: one launch over the subtiles of both weights, sharing
+    // the activation stages
+    if (p.M <= kChunkRows) {
+        switch (p.K / kBlk) {
+        case 4:
+            return launch_wide_kb<4>(p, stream);
+        case 8:
+            return launch_wide_kb<8>(p, stream);
+        case 12:
+            return launch_wide_kb<12>(p, stream);
+        case 16:
+            return launch_wide_kb<16>(p, stream);
+        default:
+            break;
+        }
+    }
+    GemmParams a = p, b = p;
+    a.w2 = nullptr;
+    a.w_scale2 = nullptr;
+    a.out2 = nullptr;
+    a.N2 = 0;
+    b.w = p.w2;
+    b.w_scale = p.w_scale2;
+    b.out = p.out2;
+    b.N = p.N2;
+    b.w2 = nullptr;
+    b.w_scale2 = nullptr;
+    b.out2 = nullptr;
+    b.N2 = 0;
+    const hipError_t e = launch_block_scaled_gemm(a, stream);
+    return e != hipSuccess ? e : launch_block_scaled_gemm(b, stream);
 }
 
 }  // namespace mi

@@ -37,9 +37,17 @@ struct GemmParams {
     int64_t M;
     int64_t N;
     int64_t K;
+    // optional second consumer of the same activations (N2 == 0: none);
+    // its 16-row subtiles follow those of w in one subtile index space
+    const uint8_t *w2 = nullptr;
+    const float *w_scale2 = nullptr;
+    uint16_t *out2 = nullptr;
+    int64_t N2 = 0;
 };
 
 hipError_t launch_normquant(const NormQuantParams &p, hipStream_t stream);
 hipError_t launch_block_scaled_gemm(const GemmParams &p, hipStream_t stream);
+// both consumers (p.N2 > 0) in one launch where the shape allows, else two
+hipError_t launch_block_scaled_gemm_pair(const GemmParams &p, hipStream_t stream);
 
 }  // namespace mi

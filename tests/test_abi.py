@@ -100,6 +100,26 @@ def test_gemm_validation(L):
     assert gemm(L, As=ctypes.c_void_p(0x1002)) == B.MI_ERR_ALIGN
 
 
+def gemm_pair(L, **kw):
+    a = dict(a=FAKE, As=FAKE, t=0, w1=FAKE, Bs1=FAKE, out1=FAKE, N1=24576, w2=FAKE, Bs2=FAKE, out2=FAKE,
+             N2=8192, M=4, K=1536)
+    a.update(kw)
+    return L.mi_block_scaled_fp8_gemm_pair(a["a"], a["As"], a["t"], a["w1"], a["Bs1"], a["out1"], a["N1"],
+                                           a["w2"], a["Bs2"], a["out2"], a["N2"], a["M"], a["K"], NULL)
+
+
+def test_gemm_pair_validation(L):
+    assert gemm_pair(L, M=-1) == B.MI_ERR_SHAPE
+    for k, v in (("N1", 1000), ("N2", 1000), ("K", 1000), ("N1", 0), ("N2", 0)):
+        assert gemm_pair(L, **{k: v}) == B.MI_ERR_SHAPE, k
+    assert gemm_pair(L, M=0) == B.MI_OK
+    for k in ("a", "As", "w1", "Bs1", "out1", "w2", "Bs2", "out2"):
+        assert gemm_pair(L, **{k: NULL}) == B.MI_ERR_NULL, k
+    for k, v in (("a", 0x1008), ("w1", 0x1004), ("w2", 0x1004), ("out1", 0x1002), ("out2", 0x1002),
+                 ("As", 0x1002), ("Bs1", 0x1002), ("Bs2", 0x1002)):
+        assert gemm_pair(L, **{k: ctypes.c_void_p(v)}) == B.MI_ERR_ALIGN, k
+
+
 def test_negotiate_scale_layout(L):
     assert mi.mi_negotiate_scale_layout([1, 1]) is True
     assert mi.mi_negotiate_scale_layout([0, 0, 0]) is False

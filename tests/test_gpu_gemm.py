@@ -202,3 +202,35 @@ def test_producer_and_two_consumers(M, transpose):
         got = bf16_to_f64(out)[:, cols]
         fro, mx = assert_gemm_close(got, gref, f"{name} M{M} t{transpose}")
         print(f"{name} M={M} transpose={transpose}: rel fro {fro:.2e} max {mx:.2e}")
+
+
+@pytest.mark.parametrize("M,N1,N2,K,seed", [(1, 24576, 8192, 1536, 31), (16, 24576, 8192, 1536, 32),
+                                            (64, 24576, 8192, 1536, 33), (40, 1280, 384, 512, 34),
+                                            (64, 3200, 1664, 1024, 35), (100, 1280, 640, 1536, 36),
+                                            (256, 2048, 1024, 2048, 37), (7, 384, 128, 896, 38),
+                                            (64, 12800, 6400, 1536, 39)])
+def test_gemm_pair_equals_two_gemms(M, N1, N2, K, seed):
+    """The two-consumer entry point returns, bit for bit, what two calls of
+    the single GEMM return (fused launch for M <= 64 and K/128 in {4, 8, 12,
+    16}, including 6-subtile slabs that straddle the two weights at
+    N1 = 12800; two launches
+    otherwise), and matches the oracle on sampled column blocks of both."""
+    dev = gpu_or_skip()
+    a, As, w1, Bs1 = random_operands(M, N1, K, seed)
+    _, _, w2, Bs2 = random_operands(M, N2, K, seed + 100)
+    da = dev_u8(a, dev)
+    for t in (False, True):
+        das = dev_f32(As.T.copy(), dev).T if t else dev_f32(As, dev)
+        dw1, dbs1, dw2, dbs2 = dev_u8(w1, dev), dev_f32(Bs1, dev), dev_u8(w2, dev), dev_f32(Bs2, dev)
+        o1, o2 = mi.mi_block_scaled_fp8_gemm_pair(da, das, dw1, dbs1, dw2, dbs2)
+        s1 = mi.mi_block_scaled_fp8_gemm(da, das, dw1, dbs1)
+        s2 = mi.mi_block_scaled_fp8_gemm(da, das, dw2, dbs2)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bf16_bits(o1), host_bf16_bits(s1)), f"out1 M{M} t{t}"
+        assert np.array_equal(host_bf16_bits(o2), host_bf16_bits(s2)), f"out2 M{M} t{t}"
+        for w, Bs, o, name in ((w1, Bs1, o1, "out1"), (w2, Bs2, o2, "out2")):
+            nb = w.shape[0] // 128
+            blocks = np.unique([0, nb - 1, nb // 2])
+            cols = (blocks[:, None] * 128 + np.arange(128)[None, :]).reshape(-1)
+            ref = oracle.block_scaled_fp8_gemm(a, As.reshape(-1), False, w[cols], Bs[blocks])
+            assert_gemm_close(bf16_to_f64(o)[:, cols], ref, f"{name} M{M} N{w.shape[0]} t{t}")
