@@ -62,6 +62,13 @@ def lib() -> ctypes.CDLL:
             p, p, ctypes.c_int, p, p, p, i64, i64, i64]
         L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_num_threads.argtypes = []
+        L.oracle_group_quant.restype = None
+        L.oracle_group_quant.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                         ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        L.oracle_rmsnorm_group_quant.restype = None
+        L.oracle_rmsnorm_group_quant.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float,
+                                                 ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                                 ctypes.c_void_p, ctypes.c_void_p]
         _lib = L
     return _lib
 
@@ -145,6 +152,44 @@ def dual_rmsnorm_group_quant(q: np.ndarray, kv: np.ndarray,
     if want_ratio:
         res["ratio"] = ratio
         res["y"] = y
+    return res
+
+
+def group_quant(x: np.ndarray, transpose_scale: bool, want_ratio: bool = False):
+    """Per-1x128 dynamic FP8 quant of a 2-D bf16 view ``x`` [M, N] (no
+    normalisation).  Returns a dict with ``q`` (uint8 [M, N]), ``scale``
+    (float32, M*N/128 values in the requested layout) and, when asked,
+    ``ratio`` (float64 x / s)."""
+    x, xs = _row_view(x, np.uint16)
+    M, N = x.shape
+    assert N % GROUP == 0
+    out_q = np.zeros((M, N), np.uint8)
+    out_s = np.zeros(M * (N // GROUP), np.float32)
+    ratio = np.zeros((M, N), np.float64) if want_ratio else None
+    lib().oracle_group_quant(_ptr(x), xs, M, N, int(bool(transpose_scale)), _ptr(out_q), _ptr(out_s), _ptr(ratio))
+    res = {"q": out_q, "scale": out_s}
+    if want_ratio:
+        res["ratio"] = ratio
+    return res
+
+
+def rmsnorm_group_quant(x: np.ndarray, gamma: np.ndarray, eps: float, transpose_scale: bool,
+                        want_ratio: bool = False):
+    """Single-input RMSNorm + per-1x128 FP8 group quant of a 2-D bf16 view
+    ``x`` [M, N] with bf16 ``gamma`` [N].  Same outputs as group_quant."""
+    x, xs = _row_view(x, np.uint16)
+    M, N = x.shape
+    assert N % GROUP == 0
+    gamma = np.ascontiguousarray(gamma, dtype=np.uint16)
+    assert gamma.shape == (N,)
+    out_q = np.zeros((M, N), np.uint8)
+    out_s = np.zeros(M * (N // GROUP), np.float32)
+    ratio = np.zeros((M, N), np.float64) if want_ratio else None
+    lib().oracle_rmsnorm_group_quant(_ptr(x), xs, _ptr(gamma), ctypes.c_float(eps), M, N,
+                                     int(bool(transpose_scale)), _ptr(out_q), _ptr(out_s), _ptr(ratio))
+    res = {"q": out_q, "scale": out_s}
+    if want_ratio:
+        res["ratio"] = ratio
     return res
 
 

@@ -25,7 +25,9 @@
  *  [D56433]   PRHub report of vLLM PR #56433 "Fix AITER preshuffled FP8
  *             block-scale kernel", "实现拆解" items 2 and 4.
  *  [D27289]   PRHub digest of SGLang PR #27289 (fp8 scale transpose copy),
- *             "功能与动机" and the aiter_w8a8_block_fp8_linear excerpt.
+ *             "功能与动机", "实现拆解" item 2 (fused_rms_fp8_group_quant with
+ *             transpose_scale) and the aiter_w8a8_block_fp8_linear excerpt
+ *             (its branch B: aiter_per1x128_quant of a bf16 input).
  *
  * Readings taken where the pages are silent (each also listed in the design
  * notes of the repository):
@@ -41,6 +43,7 @@
  *    As in the layout the caller states and Bs row-major [N/128, K/128].
  */
 #include <math.h>
+#include <stdlib.h>
 #include <stdint.h>
 #include <stddef.h>
 
@@ -239,6 +242,81 @@ void oracle_dual_rmsnorm_group_quant(
                 out_q[m * Nq + i] = oracle_e4m3_encode(c);
             }
         }
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * One row of per-1x128 group quantisation of exact values y[0..N): for each
+ * group g of 128 consecutive columns, s = max(fp32(max|y| / 448), 1e-12f)
+ * and code = e4m3(clamp(y / s, +-448)); the scale goes to element (m, g) of
+ * the [M, G] scale array in the requested layout.
+ * ------------------------------------------------------------------------- */
+static void quantise_row(const double *y, int64_t m, int64_t M, int64_t N, int transpose_scale,
+                         uint8_t *out_q, float *out_scale, double *out_ratio)
+{
+    const int64_t G = N / ORACLE_GROUP;
+    for (int64_t g = 0; g < G; ++g) {
+        double amax = 0.0;
+        for (int j = 0; j < ORACLE_GROUP; ++j)
+            if (fabs(y[g * ORACLE_GROUP + j]) > amax)
+                amax = fabs(y[g * ORACLE_GROUP + j]);
+        float s = to_f32(amax / ORACLE_E4M3_MAX);
+        if (s < ORACLE_SCALE_FLOOR)
+            s = ORACLE_SCALE_FLOOR;
+        out_scale[transpose_scale ? g * M + m : m * G + g] = s;
+        for (int j = 0; j < ORACLE_GROUP; ++j) {
+            int64_t i = g * ORACLE_GROUP + j;
+            double ratio = y[i] / (double)s;
+            if (out_ratio)
+                out_ratio[m * N + i] = ratio;
+            double c = ratio;
+            if (c > ORACLE_E4M3_MAX)
+                c = ORACLE_E4M3_MAX;
+            if (c < -ORACLE_E4M3_MAX)
+                c = -ORACLE_E4M3_MAX;
+            out_q[m * N + i] = oracle_e4m3_encode(c);
+        }
+    }
+}
+
+/* Per-1x128 dynamic FP8 quantisation of a bf16 activation [M, N] with no
+ * normalisation: [D27289] aiter_w8a8_block_fp8_linear excerpt, branch B
+ * (aiter_per1x128_quant with transpose_scale); [PR53540] "Purpose", step 2
+ * of the pipeline the fused kernel replaces.  y = x exactly. */
+void oracle_group_quant(const uint16_t *x, int64_t row_stride, int64_t M, int64_t N,
+                        int transpose_scale, uint8_t *out_q, float *out_scale, double *out_ratio)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        double *y = (double *)malloc(sizeof(double) * (size_t)N);
+        for (int64_t i = 0; i < N; ++i)
+            y[i] = oracle_bf16_decode(x[m * row_stride + i]);
+        quantise_row(y, m, M, N, transpose_scale, out_q, out_scale, out_ratio);
+        free(y);
+    }
+}
+
+/* Single-input RMSNorm + per-1x128 FP8 group quantisation: [D27289]
+ * "实现拆解" item 2 (fused_rms_fp8_group_quant with transpose_scale).
+ * y = x * gamma / sqrt(mean(x^2) + eps), exact (fp64), quantised as above. */
+void oracle_rmsnorm_group_quant(const uint16_t *x, int64_t row_stride, const uint16_t *gamma,
+                                float eps, int64_t M, int64_t N, int transpose_scale,
+                                uint8_t *out_q, float *out_scale, double *out_ratio)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t *xr = x + m * row_stride;
+        double ssq = 0.0;
+        for (int64_t i = 0; i < N; ++i) {
+            double v = oracle_bf16_decode(xr[i]);
+            ssq += v * v;
+        }
+        double rstd = 1.0 / sqrt(ssq / (double)N + (double)eps);
+        double *y = (double *)malloc(sizeof(double) * (size_t)N);
+        for (int64_t i = 0; i < N; ++i)
+            y[i] = oracle_bf16_decode(xr[i]) * rstd * oracle_bf16_decode(gamma[i]);
+        quantise_row(y, m, M, N, transpose_scale, out_q, out_scale, out_ratio);
+        free(y);
     }
 }
 
