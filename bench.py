@@ -65,6 +65,11 @@ def algorithmic_bytes_normquant(M, Nq=1536, Nkv=512):
     return M * (2 * Nq + 2 * Nkv + Nq + 4 * G + 2 * Nkv) + 2 * (Nq + Nkv)
 
 
+def algorithmic_bytes_single(M, N, normalize):
+    """Single-input quant: read x (+ gamma), write codes and scales."""
+    return M * N * 2 + M * N + M * (N // 128) * 4 + (N * 2 if normalize else 0)
+
+
 def algorithmic_bytes_gemm(M, N, K):
     """Weight codes + weight scales + activation codes + activation scales +
     bf16 output, each moved once."""
@@ -221,7 +226,8 @@ def cpu_baseline(np, W, M, layout, wa, wb):
 
 def sweep(torch, np, mi, W, wa, wb, dev, cold):
     """Extra figures of the metric: norm-quant at M=1 (us/call) and M=8192
-    (GB/s, both layouts); the GEMMs at M=256 (TFLOP/s, % of FP8 MFMA peak)."""
+    (GB/s, both layouts); the single-input quantisations at [8192, 1536] and
+    [256, 7168] (GB/s); the GEMMs at M=256 (TFLOP/s, % of FP8 MFMA peak)."""
     res = {}
     gq = bf16_dev(torch, np, W.gammas()[0], dev)
     gk = bf16_dev(torch, np, W.gammas()[1], dev)
@@ -263,6 +269,28 @@ def sweep(torch, np, mi, W, wa, wb, dev, cold):
         del g, fns
         torch.cuda.empty_cache()
     del bufp
+    # single-input forms: RMSNorm + quant and the norm-less quant, column-major scales
+    for M, N in ((8192, 1536), (256, 7168)):
+        x0, gam = W.single_input(M, N)
+        xd0 = bf16_dev(torch, np, x0, dev)
+        gd = bf16_dev(torch, np, gam, dev)
+        for normalize in (True, False):
+            nbytes = algorithmic_bytes_single(M, N, normalize)
+            nsets = max(1, COLD_BYTES // nbytes + 1) if cold else 1
+            fns = []
+            for i in range(nsets):
+                xd = xd0 if i == 0 else xd0.clone()
+                oq = torch.empty((M, N), dtype=torch.uint8, device=dev)
+                osc = torch.empty(M * (N // 128), dtype=torch.float32, device=dev)
+                fns.append(mi.prepare_rmsnorm_group_quant(xd, gd, W.EPS, True, oq, osc) if normalize
+                           else mi.prepare_group_quant_1x128(xd, True, oq, osc))
+            g = make_graph(torch, fns)
+            us = time_graph(torch, g, len(fns), max(1, 200 // len(fns)))
+            gbs = nbytes / us / 1e3
+            res[f"{'rmsnorm_quant' if normalize else 'quant_1x128'}_M{M}_N{N}_col"] = {
+                "us": round(us, 3), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+            del g, fns
+            torch.cuda.empty_cache()
     # GEMMs at M = 256
     M = 256
     a = torch.randint(0, 0x78, (M, 1536), dtype=torch.uint8, device=dev)

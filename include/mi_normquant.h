@@ -57,6 +57,8 @@ typedef enum {
 /* Largest supported widths of the fused norm-quant (one row per wavefront). */
 #define MI_MAX_NQ 4096
 #define MI_MAX_NKV 2048
+/* Largest row width of the single-input quantisations below. */
+#define MI_MAX_N_SINGLE 8192
 
 /*
  * mi_fused_dual_rmsnorm_group_quant
@@ -100,6 +102,60 @@ mi_status mi_fused_dual_rmsnorm_group_quant(
     float eps, int64_t M, int64_t Nq, int64_t Nkv,
     int transpose_scale,
     uint8_t *out_q_fp8, float *out_scale, uint16_t *out_kv,
+    hipStream_t stream);
+
+/*
+ * mi_rmsnorm_group_quant
+ *
+ * [D27289] "实现拆解" item 2: the single-input form of the fused operation,
+ * RMSNorm of one activation followed by the per-1x128 FP8 group quantisation
+ * of the normalised values, with the scale layout chosen by
+ * `transpose_scale`.  Per row m, with the formulas of
+ * mi_fused_dual_rmsnorm_group_quant's q path:
+ *   rstd   = 1 / sqrt(sum_i x_i^2 / N + eps)              (fp32 accumulation)
+ *   y_i    = x_i * rstd * gamma_i
+ *   s_g    = max(max_{i in g} |y_i| / 448, 1e-12)
+ *   code_i = e4m3fn_rne(clamp(y_i / s_g, -448, 448))
+ * The q outputs of mi_fused_dual_rmsnorm_group_quant for the same q rows are
+ * bit-identical to this call's.
+ *
+ * x, x_row_stride  [M, N] bf16, row m at x + m*x_row_stride (elements),
+ *                  x_row_stride >= N; no alignment required.
+ * gamma            [N] bf16 RMSNorm weight.
+ * eps              added to the mean of squares.
+ * M, N             M >= 0; N % 128 == 0, 128 <= N <= MI_MAX_N_SINGLE.
+ * transpose_scale  0: out_scale[m*G + g]; 1: out_scale[g*M + m], G = N/128.
+ * out_fp8          [M, N] e4m3fn codes, contiguous.
+ * out_scale        M*G fp32 values in the layout above.
+ */
+mi_status mi_rmsnorm_group_quant(
+    const uint16_t *x, int64_t x_row_stride, const uint16_t *gamma,
+    float eps, int64_t M, int64_t N, int transpose_scale,
+    uint8_t *out_fp8, float *out_scale,
+    hipStream_t stream);
+
+/*
+ * mi_group_quant_1x128
+ *
+ * [D27289] aiter_w8a8_block_fp8_linear excerpt, branch B: the dynamic
+ * per-1x128 FP8 quantisation of a bf16 activation (aiter_per1x128_quant
+ * with transpose_scale) that the block-scaled GEMM consumes; [PR53540]
+ * "Purpose": the second step of the unfused pipeline (quantising the bf16
+ * RMSNorm output).  No normalisation: per row m and group g,
+ *   s_g    = max(fp32(max_{i in g} |x_i| / 448), 1e-12)
+ *   code_i = e4m3fn_rne(clamp(x_i / s_g, -448, 448))
+ * Both are correctly rounded: the scale is one IEEE division, and each code
+ * is the single RNE rounding of the exact quotient (ties, which bf16 inputs
+ * hit often, included), so results are reproducible bit for bit by any
+ * exact implementation.
+ *
+ * x, x_row_stride, M, N, transpose_scale, out_fp8, out_scale: as in
+ * mi_rmsnorm_group_quant.
+ */
+mi_status mi_group_quant_1x128(
+    const uint16_t *x, int64_t x_row_stride,
+    int64_t M, int64_t N, int transpose_scale,
+    uint8_t *out_fp8, float *out_scale,
     hipStream_t stream);
 
 /*

@@ -21,6 +21,8 @@ MI_OK, MI_ERR_NULL, MI_ERR_SHAPE, MI_ERR_STRIDE, MI_ERR_ALIGN, MI_ERR_HIP = rang
 
 EXPORTED = (
     "mi_fused_dual_rmsnorm_group_quant",
+    "mi_rmsnorm_group_quant",
+    "mi_group_quant_1x128",
     "mi_block_scaled_fp8_gemm",
     "mi_block_scaled_fp8_gemm_pair",
     "mi_negotiate_scale_layout",
@@ -49,6 +51,10 @@ def lib() -> ctypes.CDLL:
         L.mi_fused_dual_rmsnorm_group_quant.restype = c_int
         L.mi_fused_dual_rmsnorm_group_quant.argtypes = [
             p, i64, p, i64, p, p, ctypes.c_float, i64, i64, i64, c_int, p, p, p, p]
+        L.mi_rmsnorm_group_quant.restype = c_int
+        L.mi_rmsnorm_group_quant.argtypes = [p, i64, p, ctypes.c_float, i64, i64, c_int, p, p, p]
+        L.mi_group_quant_1x128.restype = c_int
+        L.mi_group_quant_1x128.argtypes = [p, i64, i64, i64, c_int, p, p, p]
         L.mi_block_scaled_fp8_gemm.restype = c_int
         L.mi_block_scaled_fp8_gemm.argtypes = [p, p, c_int, p, p, p, i64, i64, i64, p]
         L.mi_block_scaled_fp8_gemm_pair.restype = c_int
@@ -130,9 +136,54 @@ def mi_fused_dual_rmsnorm_group_quant(q: torch.Tensor, kv: torch.Tensor,
         M, Nq, Nkv, int(bool(transpose_scale)), _ptr(out_q), _ptr(out_scale), _ptr(out_kv),
         _stream(q))
     _check("mi_fused_dual_rmsnorm_group_quant", status)
+    return out_q, _scale_view(out_scale, M, G, transpose_scale), out_kv
+
+
+def _quant_outputs(M: int, N: int, out_q, out_scale, device):
+    G = N // GROUP
+    if out_q is None:
+        out_q = torch.empty((M, N), dtype=torch.uint8, device=device)
+    if out_scale is None:
+        out_scale = torch.empty(M * G, dtype=torch.float32, device=device)
+    if not out_q.is_contiguous():
+        raise ValueError("out_q must be contiguous")
+    if out_q.numel() < M * N or out_scale.numel() < M * G:
+        raise ValueError("output buffers too small")
+    return out_q, out_scale
+
+
+def _scale_view(out_scale: torch.Tensor, M: int, G: int, transpose_scale: bool) -> torch.Tensor:
     flat = out_scale.reshape(-1)[:M * G]
-    scale = flat.as_strided((M, G), (1, M)) if transpose_scale else flat.view(M, G)
-    return out_q, scale, out_kv
+    return flat.as_strided((M, G), (1, M)) if transpose_scale else flat.view(M, G)
+
+
+def mi_rmsnorm_group_quant(x: torch.Tensor, gamma: torch.Tensor, eps: float, transpose_scale: bool,
+                           out_q: torch.Tensor | None = None, out_scale: torch.Tensor | None = None):
+    """Single-input RMSNorm + per-1x128 FP8 group quant on the current
+    stream.  ``x`` [M, N] bf16 with unit inner stride; returns ``(x_fp8,
+    scale)`` laid out as in :func:`mi_fused_dual_rmsnorm_group_quant`."""
+    xs = _rows(x, "x", torch.bfloat16)
+    M, N = x.shape
+    if gamma.dtype != torch.bfloat16 or not gamma.is_contiguous() or gamma.numel() != N:
+        raise ValueError("gamma must be a contiguous bf16 tensor of the row width")
+    out_q, out_scale = _quant_outputs(M, N, out_q, out_scale, x.device)
+    status = lib().mi_rmsnorm_group_quant(_ptr(x), xs, _ptr(gamma), ctypes.c_float(eps), M, N,
+                                          int(bool(transpose_scale)), _ptr(out_q), _ptr(out_scale), _stream(x))
+    _check("mi_rmsnorm_group_quant", status)
+    return out_q, _scale_view(out_scale, M, N // GROUP, transpose_scale)
+
+
+def mi_group_quant_1x128(x: torch.Tensor, transpose_scale: bool,
+                         out_q: torch.Tensor | None = None, out_scale: torch.Tensor | None = None):
+    """Per-1x128 dynamic FP8 quant of a bf16 activation (no normalisation)
+    on the current stream; returns ``(x_fp8, scale)``."""
+    xs = _rows(x, "x", torch.bfloat16)
+    M, N = x.shape
+    out_q, out_scale = _quant_outputs(M, N, out_q, out_scale, x.device)
+    status = lib().mi_group_quant_1x128(_ptr(x), xs, M, N, int(bool(transpose_scale)), _ptr(out_q),
+                                        _ptr(out_scale), _stream(x))
+    _check("mi_group_quant_1x128", status)
+    return out_q, _scale_view(out_scale, M, N // GROUP, transpose_scale)
 
 
 def scale_is_transposed(a_scale: torch.Tensor) -> bool:
@@ -264,6 +315,25 @@ def prepare_fused_dual_rmsnorm_group_quant(q, kv, gamma_q, gamma_kv, eps, transp
             M, Nq, Nkv, int(bool(transpose_scale)), _ptr(out_q), _ptr(out_scale), _ptr(out_kv))
     return PreparedCall("mi_fused_dual_rmsnorm_group_quant", args,
                         (q, kv, gamma_q, gamma_kv, out_q, out_scale, out_kv), q.device)
+
+
+def prepare_rmsnorm_group_quant(x, gamma, eps, transpose_scale, out_q, out_scale) -> PreparedCall:
+    """Marshal the arguments of mi_rmsnorm_group_quant once (outputs required)."""
+    xs = _rows(x, "x", torch.bfloat16)
+    M, N = x.shape
+    _quant_outputs(M, N, out_q, out_scale, x.device)
+    args = (_ptr(x), xs, _ptr(gamma), ctypes.c_float(eps), M, N, int(bool(transpose_scale)), _ptr(out_q),
+            _ptr(out_scale))
+    return PreparedCall("mi_rmsnorm_group_quant", args, (x, gamma, out_q, out_scale), x.device)
+
+
+def prepare_group_quant_1x128(x, transpose_scale, out_q, out_scale) -> PreparedCall:
+    """Marshal the arguments of mi_group_quant_1x128 once (outputs required)."""
+    xs = _rows(x, "x", torch.bfloat16)
+    M, N = x.shape
+    _quant_outputs(M, N, out_q, out_scale, x.device)
+    args = (_ptr(x), xs, M, N, int(bool(transpose_scale)), _ptr(out_q), _ptr(out_scale))
+    return PreparedCall("mi_group_quant_1x128", args, (x, out_q, out_scale), x.device)
 
 
 def prepare_block_scaled_fp8_gemm(a, a_scale, w, w_scale, out) -> PreparedCall:

@@ -48,6 +48,54 @@ extern "C" mi_status mi_fused_dual_rmsnorm_group_quant(
     return mi::launch_normquant(p, stream) == hipSuccess ? MI_OK : MI_ERR_HIP;
 }
 
+namespace {
+
+mi_status single_input_quant(const uint16_t *x, int64_t x_row_stride, const uint16_t *gamma, float eps,
+                             int64_t M, int64_t N, int transpose_scale, uint8_t *out_fp8,
+                             float *out_scale, bool normalize, hipStream_t stream) {
+    if (M < 0 || N < MI_GROUP || N > MI_MAX_N_SINGLE || (N % MI_GROUP) != 0)
+        return MI_ERR_SHAPE;
+    if (M == 0)
+        return MI_OK;
+    if (!x || (normalize && !gamma) || !out_fp8 || !out_scale)
+        return MI_ERR_NULL;
+    if (x_row_stride < N)
+        return MI_ERR_STRIDE;
+
+    mi::NormQuantParams p = {};
+    p.q = x;
+    p.q_stride = x_row_stride;
+    p.gamma_q = gamma;
+    p.eps = eps;
+    p.inv_nq = static_cast<float>(1.0 / static_cast<double>(N));
+    p.M = M;
+    p.Nq = static_cast<int>(N);
+    p.transpose_scale = transpose_scale ? 1 : 0;
+    p.out_q = out_fp8;
+    p.out_scale = out_scale;
+    return mi::launch_group_quant(p, normalize, stream) == hipSuccess ? MI_OK : MI_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" mi_status mi_rmsnorm_group_quant(
+    const uint16_t *x, int64_t x_row_stride, const uint16_t *gamma,
+    float eps, int64_t M, int64_t N, int transpose_scale,
+    uint8_t *out_fp8, float *out_scale,
+    hipStream_t stream) {
+    return single_input_quant(x, x_row_stride, gamma, eps, M, N, transpose_scale, out_fp8, out_scale, true,
+                              stream);
+}
+
+extern "C" mi_status mi_group_quant_1x128(
+    const uint16_t *x, int64_t x_row_stride,
+    int64_t M, int64_t N, int transpose_scale,
+    uint8_t *out_fp8, float *out_scale,
+    hipStream_t stream) {
+    return single_input_quant(x, x_row_stride, nullptr, 0.0f, M, N, transpose_scale, out_fp8, out_scale, false,
+                              stream);
+}
+
 extern "C" mi_status mi_block_scaled_fp8_gemm(
     const uint8_t *a_fp8, const float *a_scale, int a_scale_transposed,
     const uint8_t *w_fp8, const float *w_scale,

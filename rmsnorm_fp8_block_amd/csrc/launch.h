@@ -46,6 +46,9 @@ struct GemmParams {
 };
 
 hipError_t launch_normquant(const NormQuantParams &p, hipStream_t stream);
+// one input (kv unused): RMSNorm + group quant (normalize) or the group
+// quant of q itself (gamma_q, eps unused)
+hipError_t launch_group_quant(const NormQuantParams &p, bool normalize, hipStream_t stream);
 hipError_t launch_block_scaled_gemm(const GemmParams &p, hipStream_t stream);
 // both consumers (p.N2 > 0) in one launch where the shape allows, else two
 hipError_t launch_block_scaled_gemm_pair(const GemmParams &p, hipStream_t stream);

@@ -124,29 +124,52 @@ __device__ __forceinline__ float rstd_from_ssq(float ssq, float inv_n, float eps
     return r * (1.5f - (0.5f * x) * r * r);
 }
 
+// x / s rounded to fp32 "to odd" (an inexact quotient takes whichever of its
+// two fp32 neighbours has an odd last bit), so that the e4m3 RNE convert of
+// the result equals the single RNE rounding of the exact quotient: fp32
+// carries more than two bits beyond e4m3's precision, and no e4m3 rounding
+// midpoint has an odd last fp32 bit.  q0 = x * (1/s) is within about 1.5
+// fp32 ULP; one remainder step (the FMA remainder x - q*s is exact this close
+// to the quotient) makes it faithful; the sign of the second remainder says
+// on which side of it the exact quotient lies.
+__device__ __forceinline__ float div_round_to_odd(float x, float s, float inv) {
+    const float q0 = x * inv;
+    const float q1 = fmaf(fmaf(-q0, s, x), inv, q0);
+    const float r1 = fmaf(-q1, s, x);
+    uint32_t b = __float_as_uint(q1);
+    if (r1 != 0.0f && (b & 1u) == 0u)
+        b += ((r1 > 0.0f) == (q1 > 0.0f)) ? 1u : 0xFFFFFFFFu;  // one ULP towards the quotient
+    return __uint_as_float(b);
+}
+
 // One row.  With z = x * gamma (exact in fp32: a product of two bf16 values)
 // and r = rstd, the normalised value is y = z * r; the group scale is
 // s = max(max|z| * r / 448, 1e-12) and the quantised value y / s is formed
 // as z * (r / s), so the row's rstd is applied once per group instead of
-// once per element.
-template <int kQ, int kKv, bool kVec, bool kFull>
+// once per element.  kNorm == false: the per-1x128 quantisation of x itself
+// (z = x, r = 1, no gamma); there x and s are exact, and scales and codes
+// are the correctly rounded ones.  kKv == 0: no second input.
+template <int kQ, int kKv, bool kVec, bool kFull, bool kNorm>
 __device__ __forceinline__ void process_row(const NormQuantParams &a, int64_t m, int lane,
-                                            const uint4 (&xq)[kQ], const uint4 (&xk)[kKv],
-                                            const GammaSlice (&gq)[kQ], const GammaSlice (&gk)[kKv]) {
+                                            const uint4 (&xq)[kQ], const uint4 (&xk)[kKv > 0 ? kKv : 1],
+                                            const GammaSlice (&gq)[kQ], const GammaSlice (&gk)[kKv > 0 ? kKv : 1]) {
     // -- sums of squares (fp32) and reciprocal RMS -----------------------------
-    float part_q[kQ], part_k[kKv];
+    float rq = 1.0f;
+    if constexpr (kNorm) {
+        float part_q[kQ];
 #pragma unroll
-    for (int c = 0; c < kQ; ++c)
-        part_q[c] = sumsq8(xq[c]);
+        for (int c = 0; c < kQ; ++c)
+            part_q[c] = sumsq8(xq[c]);
+        rq = rstd_from_ssq(wave_sum(fold_sum<kQ>(part_q)), a.inv_nq, a.eps);
+    }
+
+    // -- kv: y = (x * gamma) * rstd, rounded to bf16 ---------------------------
+    if constexpr (kKv > 0) {
+    float part_k[kKv];
 #pragma unroll
     for (int c = 0; c < kKv; ++c)
         part_k[c] = sumsq8(xk[c]);
-    const float ssq_q = wave_sum(fold_sum<kQ>(part_q));
-    const float ssq_k = wave_sum(fold_sum<kKv>(part_k));
-    const float rq = rstd_from_ssq(ssq_q, a.inv_nq, a.eps);
-    const float rk = rstd_from_ssq(ssq_k, a.inv_nkv, a.eps);
-
-    // -- kv: y = (x * gamma) * rstd, rounded to bf16 ---------------------------
+    const float rk = rstd_from_ssq(wave_sum(fold_sum<kKv>(part_k)), a.inv_nkv, a.eps);
     uint16_t *kout = a.out_kv + m * a.Nkv;
 #pragma unroll
     for (int c = 0; c < kKv; ++c) {
@@ -172,6 +195,7 @@ __device__ __forceinline__ void process_row(const NormQuantParams &a, int64_t m,
                     kout[col + j] = static_cast<uint16_t>(w[j / 2] >> (16 * (j & 1)));
         }
     }
+    }  // kKv > 0
 
     // -- q: group amax, scale, e4m3fn codes -------------------------------------
     const int G = a.Nq / kGroup;
@@ -182,19 +206,26 @@ __device__ __forceinline__ void process_row(const NormQuantParams &a, int64_t m,
         if (!kFull && c * kChunk >= a.Nq)
             break;  // uniform across the wave
         float z[8];
-        times_gamma8(xq[c], gq[c], z);
+        if constexpr (kNorm)
+            times_gamma8(xq[c], gq[c], z);
+        else
+            unpack8_bf16(xq[c], z);
         float amax = 0.0f;
 #pragma unroll
         for (int j = 0; j < 8; ++j)
             amax = fmaxf(amax, fabsf(z[j]));
         // 16 lanes x 8 elements = one 128-element group
         amax = row16_max(amax);
-        const float s = fmaxf((amax * rq) * kInvE4m3Max, kScaleFloor);
+        // without the norm, amax is an exact bf16 value and one correctly
+        // rounded division gives the scale bit for bit (once per group)
+        const float s = kNorm ? fmaxf((amax * rq) * kInvE4m3Max, kScaleFloor)
+                              : fmaxf(amax / kE4m3Max, kScaleFloor);
         const float inv = rq * __builtin_amdgcn_rcpf(s);
         float r[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-            r[j] = __builtin_amdgcn_fmed3f(z[j] * inv, -kE4m3Max, kE4m3Max);
+            r[j] = __builtin_amdgcn_fmed3f(kNorm ? z[j] * inv : div_round_to_odd(z[j], s, inv), -kE4m3Max,
+                                           kE4m3Max);
         const uint32_t lo = pack4_e4m3(r[0], r[1], r[2], r[3]);
         const uint32_t hi = pack4_e4m3(r[4], r[5], r[6], r[7]);
         if (kFull || col < a.Nq) {  // Nq % 128 == 0: a lane's 8 codes are all in range
@@ -223,8 +254,9 @@ __device__ __forceinline__ void process_row(const NormQuantParams &a, int64_t m,
 // output row is 16-byte aligned and Nkv % 8 == 0.  kRows: consecutive rows
 // per wave; all their loads are issued together, gammas once per wave.
 // kFull: Nq == 512 * kQ and Nkv == 512 * kKv (no bounds tests).
-template <int kQ, int kKv, bool kVec, int kRows, bool kFull>
+template <int kQ, int kKv, bool kVec, int kRows, bool kFull, bool kNorm>
 __global__ __launch_bounds__(256) void fused_dual_rmsnorm_group_quant_kernel(NormQuantParams a) {
+    constexpr int kKvA = kKv > 0 ? kKv : 1;  // array extents
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: scalar row addressing
     const int waves_per_block = blockDim.x / kWave;
@@ -234,33 +266,39 @@ __global__ __launch_bounds__(256) void fused_dual_rmsnorm_group_quant_kernel(Nor
         return;
 
     // -- all loads first: gammas, then every row's data ------------------------
-    uint4 gq_raw[kQ], gk_raw[kKv];
+    uint4 gq_raw[kQ], gk_raw[kKvA];
+    if constexpr (kNorm) {
 #pragma unroll
-    for (int c = 0; c < kQ; ++c)
-        gq_raw[c] = load8<kVec, kFull>(a.gamma_q, c * kChunk + lane * 8, a.Nq);
+        for (int c = 0; c < kQ; ++c)
+            gq_raw[c] = load8<kVec, kFull>(a.gamma_q, c * kChunk + lane * 8, a.Nq);
+    }
 #pragma unroll
     for (int c = 0; c < kKv; ++c)
         gk_raw[c] = load8<kVec, kFull>(a.gamma_kv, c * kChunk + lane * 8, a.Nkv);
-    uint4 xq[kRows][kQ], xk[kRows][kKv];
+    uint4 xq[kRows][kQ], xk[kRows][kKvA];
 #pragma unroll
     for (int r = 0; r < kRows; ++r) {
         const int64_t m = row0 + r;
         if (m >= a.M)
             break;
         const uint16_t *qrow = a.q + m * a.q_stride;
-        const uint16_t *krow = a.kv + m * a.kv_stride;
 #pragma unroll
         for (int c = 0; c < kQ; ++c)
             xq[r][c] = load8<kVec, kFull>(qrow, c * kChunk + lane * 8, a.Nq);
+        if constexpr (kKv > 0) {
+            const uint16_t *krow = a.kv + m * a.kv_stride;
 #pragma unroll
-        for (int c = 0; c < kKv; ++c)
-            xk[r][c] = load8<kVec, kFull>(krow, c * kChunk + lane * 8, a.Nkv);
+            for (int c = 0; c < kKv; ++c)
+                xk[r][c] = load8<kVec, kFull>(krow, c * kChunk + lane * 8, a.Nkv);
+        }
     }
     // gammas prepared once per wave, shared by its rows
-    GammaSlice gq[kQ], gk[kKv];
+    GammaSlice gq[kQ], gk[kKvA];
+    if constexpr (kNorm) {
 #pragma unroll
-    for (int c = 0; c < kQ; ++c)
-        gq[c] = prepare_gamma(gq_raw[c]);
+        for (int c = 0; c < kQ; ++c)
+            gq[c] = prepare_gamma(gq_raw[c]);
+    }
 #pragma unroll
     for (int c = 0; c < kKv; ++c)
         gk[c] = prepare_gamma(gk_raw[c]);
@@ -270,18 +308,18 @@ __global__ __launch_bounds__(256) void fused_dual_rmsnorm_group_quant_kernel(Nor
         const int64_t m = row0 + r;
         if (m >= a.M)
             break;
-        process_row<kQ, kKv, kVec, kFull>(a, m, lane, xq[r], xk[r], gq, gk);
+        process_row<kQ, kKv, kVec, kFull, kNorm>(a, m, lane, xq[r], xk[r], gq, gk);
     }
 }
 
-template <int kQ, int kKv, bool kVec, int kRows, bool kFull = false>
+template <int kQ, int kKv, bool kVec, int kRows, bool kFull = false, bool kNorm = true>
 hipError_t launch_variant(const NormQuantParams &p, hipStream_t stream) {
     const int64_t waves = (p.M + kRows - 1) / kRows;
     const int waves_per_block = waves >= 4 ? 4 : static_cast<int>(waves);
     const int64_t blocks = (waves + waves_per_block - 1) / waves_per_block;
     if (blocks > 0x7FFFFFFF)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((fused_dual_rmsnorm_group_quant_kernel<kQ, kKv, kVec, kRows, kFull>),
+    hipLaunchKernelGGL((fused_dual_rmsnorm_group_quant_kernel<kQ, kKv, kVec, kRows, kFull, kNorm>),
                        dim3(static_cast<unsigned>(blocks)), dim3(waves_per_block * kWave), 0, stream, p);
     return hipGetLastError();
 }
@@ -303,6 +341,25 @@ hipError_t launch_normquant(const NormQuantParams &p, hipStream_t stream) {
     if (qch <= 8 && kch <= 4)
         return vec ? launch_variant<8, 4, true, 1>(p, stream) : launch_variant<8, 4, false, 1>(p, stream);
     return hipErrorInvalidValue;
+}
+
+template <bool kNorm>
+hipError_t launch_single_kind(const NormQuantParams &p, hipStream_t stream) {
+    const bool vec = aligned16(p.q) && (!kNorm || aligned16(p.gamma_q)) && aligned16(p.out_q) &&
+                     (p.q_stride % 8) == 0;
+    const int qch = (p.Nq + kChunk - 1) / kChunk;
+    if (vec && p.Nq == 3 * kChunk)  // 1536: the MLA q latent
+        return launch_variant<3, 0, true, 1, true, kNorm>(p, stream);
+    if (vec && p.Nq == 14 * kChunk)  // 7168: a DeepSeek hidden row
+        return launch_variant<14, 0, true, 1, true, kNorm>(p, stream);
+    if (qch <= 16)
+        return vec ? launch_variant<16, 0, true, 1, false, kNorm>(p, stream)
+                   : launch_variant<16, 0, false, 1, false, kNorm>(p, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_group_quant(const NormQuantParams &p, bool normalize, hipStream_t stream) {
+    return normalize ? launch_single_kind<true>(p, stream) : launch_single_kind<false>(p, stream);
 }
 
 }  // namespace mi

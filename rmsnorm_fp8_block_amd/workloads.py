@@ -133,6 +133,24 @@ def producer_activations(M: int, seed: int = 5, rows: int = 256) -> NormQuantCas
     return NormQuantCase(f"producer_M{M}", q, kv, gq, gk, layouts=(0, 1), buffer=buf)
 
 
+def single_input(M: int, N: int = NQ, seed: int = 6, pad: int = 0, frac: float = 0.01,
+                 mult: float = 50.0):
+    """Input of the single-input quantisations: a [M, N] bf16 view of a
+    [M, N + pad] buffer (pad > 0: a strided view, like a column slice of a
+    wider projection output), N(0,1) with a Bernoulli(frac) subset scaled by
+    ``mult`` and, in every row m, the group (m mod G) set to zero; plus a
+    seeded bf16 gamma [N] near 1.  Returns (x, gamma)."""
+    r = rng(seed)
+    G = N // GROUP
+    x32 = r.standard_normal((M, N + pad), dtype=np.float32)
+    x32[r.random((M, N + pad)) < frac] *= np.float32(mult)
+    for m in range(M):
+        g = m % G
+        x32[m, g * GROUP:(g + 1) * GROUP] = 0.0
+    gamma = f32_to_bf16_bits((1.0 + 0.1 * r.standard_normal(N)).astype(np.float32))
+    return f32_to_bf16_bits(x32)[:, :N], gamma
+
+
 @dataclass
 class BlockFp8Weight:
     """A weight [N, K] as e4m3fn codes plus fp32 scales [N/128, K/128]

@@ -77,14 +77,15 @@ def e4m3_midpoint_distance(ratio: np.ndarray) -> np.ndarray:
     return d / np.maximum(a, 2.0 ** -12)
 
 
-def compare_normquant(got_q, got_scale_buf, got_kv, ref, label=""):
-    """Assert the parity bar and return a dict of statistics.
+def compare_quant(got_q, got_scale_buf, ref, label="", scale_rtol=SCALE_RTOL):
+    """Assert the parity bar on codes and scales; return statistics.
 
     Codes: within 1 e4m3 ULP everywhere; every differing code must sit where
     the oracle's exact y/s is within MIDPOINT_WINDOW of a rounding midpoint
     (away from a midpoint the code is unique and must match); and, on inputs
     large enough for the fraction to mean something (>= 10^4 codes), at
-    least 99.9 % identical."""
+    least 99.9 % identical.  Scales: relative error <= scale_rtol (0: equal
+    bit for bit)."""
     rq = ref["q"]
     assert got_q.shape == rq.shape
     assert not np.any((got_q & 0x7F) == 0x7F), f"{label}: NaN code"
@@ -99,12 +100,20 @@ def compare_normquant(got_q, got_scale_buf, got_kv, ref, label=""):
     if d.size >= 10_000:
         assert exact >= CODE_EXACT_FRACTION, f"{label}: only {exact:.5f} of codes exact"
     rs = ref["scale"]
+    if scale_rtol == 0:
+        assert np.array_equal(got_scale_buf, rs), f"{label}: scales not bit-exact"
     rel = np.abs(got_scale_buf.astype(np.float64) / rs.astype(np.float64) - 1.0)
-    assert rel.max() <= SCALE_RTOL, f"{label}: scale rel err {rel.max():.3e}"
+    assert rel.max() <= scale_rtol, f"{label}: scale rel err {rel.max():.3e}"
+    return {"code_exact": exact, "code_mismatches": n_mis, "scale_max_rel": float(rel.max())}
+
+
+def compare_normquant(got_q, got_scale_buf, got_kv, ref, label=""):
+    """compare_quant on the q outputs, and kv within 1 bf16 ULP."""
+    stats = compare_quant(got_q, got_scale_buf, ref, label)
     dk = np.abs(bf16_ord(got_kv) - bf16_ord(ref["kv"]))
     assert dk.max() <= 1, f"{label}: kv off by {dk.max()} bf16 ULP"
-    return {"code_exact": exact, "code_mismatches": n_mis, "scale_max_rel": float(rel.max()),
-            "kv_exact": float((dk == 0).mean())}
+    stats["kv_exact"] = float((dk == 0).mean())
+    return stats
 
 
 def gemm_error(out: np.ndarray, ref: np.ndarray):

@@ -79,6 +79,30 @@ def test_normquant_validation(L):
     assert nq(L, ks=511) == B.MI_ERR_STRIDE
 
 
+def single(L, normalize, **kw):
+    a = dict(x=FAKE, xs=7168, g=FAKE, eps=1e-6, M=4, N=7168, t=0, oq=FAKE, os_=FAKE)
+    a.update(kw)
+    if normalize:
+        return L.mi_rmsnorm_group_quant(a["x"], a["xs"], a["g"], ctypes.c_float(a["eps"]), a["M"], a["N"], a["t"],
+                                        a["oq"], a["os_"], NULL)
+    return L.mi_group_quant_1x128(a["x"], a["xs"], a["M"], a["N"], a["t"], a["oq"], a["os_"], NULL)
+
+
+@pytest.mark.parametrize("normalize", [True, False])
+def test_single_input_quant_validation(L, normalize):
+    assert single(L, normalize, M=-1) == B.MI_ERR_SHAPE
+    for n in (0, 100, 1500, 8192 + 128):
+        assert single(L, normalize, N=n, xs=max(n, 1)) == B.MI_ERR_SHAPE, n
+    assert single(L, normalize, M=0) == B.MI_OK
+    assert single(L, normalize, M=0, x=NULL) == B.MI_OK
+    for k in ("x", "oq", "os_"):
+        assert single(L, normalize, **{k: NULL}) == B.MI_ERR_NULL, k
+    # gamma is read only by the normalising form
+    want = B.MI_ERR_NULL if normalize else B.MI_ERR_STRIDE
+    assert single(L, normalize, g=NULL, xs=100) == want
+    assert single(L, normalize, xs=7167) == B.MI_ERR_STRIDE
+
+
 def gemm(L, **kw):
     a = dict(a=FAKE, As=FAKE, t=0, w=FAKE, Bs=FAKE, out=FAKE, M=4, N=1024, K=1536)
     a.update(kw)
