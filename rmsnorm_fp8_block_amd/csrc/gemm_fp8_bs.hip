@@ -11,26 +11,30 @@
 // PRHub digest of SGLang PR #27289, and the explicit As major order of the
 // PRHub report of vLLM PR #56433 (item 2).
 //
-// Mapping onto CDNA4:
+// Mapping onto CDNA4, common to every kernel here:
 //  - v_mfma_f32_16x16x128_f8f6f4 (e4m3 x e4m3): one instruction covers one
 //    whole 128-deep K-block of a 16 (n) x 16 (m) output tile, so the block's
 //    partial sum leaves the matrix core once per K-block and is folded into
 //    the fp32 accumulator with As[m, kb] * Bs[nb, kb] (one FMA per value);
-//  - the weight is the MFMA "A" operand (rows = n): each lane streams 32
-//    contiguous bytes of one weight row per K-block straight from HBM into
-//    registers; a weight byte is used by exactly one wave;
-//  - the activation is the MFMA "B" operand (columns = m): a block stages
-//    its M-tile for 4 K-blocks at a time in LDS, already in fragment order
-//    (each lane's 32 bytes split in two 16-byte halves, lane-contiguous, so
-//    the ds_read_b128 of a wave hits consecutive banks);
-//  - each lane holds outputs (n = 4*(lane/16) + i, m = lane % 16), i < 4, so
-//    one lane writes 4 consecutive bf16 (8 bytes) of one output row;
-//  - a block is 4 waves = 64 weight rows x up to 64 activation rows; blocks
-//    are renumbered so that the M-tiles of one N-tile run on the same XCD
-//    and share the weight tile through its L2.
+//  - the weight is the MFMA "A" operand (rows = n), the activation the "B"
+//    operand (columns = m); every weight byte is read from HBM once;
+//  - each lane holds outputs (n = 4*(lane/16) + i, m = lane % 16), i < 4.
 // The K order inside one MFMA is irrelevant to the result as long as both
 // operands use the same one; both are loaded with the same lane/byte -> k
-// assignment.
+// assignment, so every kernel gives the same bits.
+//
+// At decode and small-batch sizes the GEMM streams the weight from HBM
+// (M <= 256: at most ~380 flop per weight byte); the kernels differ in how
+// they keep that stream going:
+//  - decode (M <= 32 over weights of more than 4 subtiles per CU): 8 waves
+//    per block, each streams its own 16-row weight subtile through a ring of
+//    registers while the activation tile sits in LDS;
+//  - wide (M <= 256, and both consumers of one activation in one launch):
+//    a slab of weight subtiles per block, all M rows, weights / activations
+//    / scales streamed through LDS rings by direct global -> LDS loads;
+//  - v0 (any other shape): 64-row weight tiles, activations staged through
+//    LDS 4 K-blocks at a time, blocks renumbered so the M-tiles of one N-tile
+//    share the weight tile through one XCD's L2.
 #include <algorithm>
 #include <atomic>
 
@@ -168,12 +172,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // ---------------------------------------------------------------------------
-// Wide variant (64 < M <= 256, K/128 = kKB known at compile time).
+// Wide variant (M <= 256, K/128 = kKB known at compile time).
 //
-// A block of kWaves waves owns a slab of kNS 16-row weight subtiles and all
-// M activation rows; wave w computes rows [16 kMT w, 16 kMT (w + 1)) against
-// the whole slab.  With 8 waves, two share each SIMD, so one wave's waits
-// for LDS and for the barrier overlap the other's matrix-core work.
+// A block of kWaves waves (4: one per SIMD) owns a slab of kNS 16-row weight
+// subtiles, of one weight or straddling the two weights of a pair launch,
+// and all M activation rows; wave w computes rows [16 kMT w, 16 kMT (w + 1))
+// against the whole slab.
 // Weights, activations and scales reach LDS through direct global -> LDS
 // loads (no registers held for them), each in a ring of K-block stages:
 //  - weight stage kb (kNS x 2 KB, shared by all waves, which split its 1 KB

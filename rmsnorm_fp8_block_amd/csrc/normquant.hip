@@ -131,7 +131,8 @@ __device__ __forceinline__ float rstd_from_ssq(float ssq, float inv_n, float eps
 // midpoint has an odd last fp32 bit.  q0 = x * (1/s) is within about 1.5
 // fp32 ULP; one remainder step (the FMA remainder x - q*s is exact this close
 // to the quotient) makes it faithful; the sign of the second remainder says
-// on which side of it the exact quotient lies.
+// on which side of it the exact quotient lies.  The sign is taken from x
+// (s > 0): the remainder step turns a -0 quotient into +0.
 __device__ __forceinline__ float div_round_to_odd(float x, float s, float inv) {
     const float q0 = x * inv;
     const float q1 = fmaf(fmaf(-q0, s, x), inv, q0);
@@ -139,7 +140,59 @@ __device__ __forceinline__ float div_round_to_odd(float x, float s, float inv) {
     uint32_t b = __float_as_uint(q1);
     if (r1 != 0.0f && (b & 1u) == 0u)
         b += ((r1 > 0.0f) == (q1 > 0.0f)) ? 1u : 0xFFFFFFFFu;  // one ULP towards the quotient
-    return __uint_as_float(b);
+    return __builtin_copysignf(__uint_as_float(b), x);
+}
+
+// Chunk c (512 elements, 4 groups) of row m: group amax, scale, e4m3fn codes.
+// x: this lane's 8 elements; g: their gamma (unused without the norm);
+// rq: the row's rstd (1 without the norm).
+template <bool kVec, bool kFull, bool kNorm>
+__device__ __forceinline__ void quant_chunk(const NormQuantParams &a, int64_t m, int lane, int c,
+                                            const uint4 &x, const GammaSlice &g, float rq) {
+    const int G = a.Nq / kGroup;
+    uint8_t *qout = a.out_q + m * a.Nq;
+    const int col = c * kChunk + lane * 8;
+    float z[8];
+    if constexpr (kNorm)
+        times_gamma8(x, g, z);
+    else
+        unpack8_bf16(x, z);
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        amax = fmaxf(amax, fabsf(z[j]));
+    // 16 lanes x 8 elements = one 128-element group
+    amax = row16_max(amax);
+    // without the norm, amax is an exact bf16 value and one correctly
+    // rounded division gives the scale bit for bit (once per group)
+    const float s = kNorm ? fmaxf((amax * rq) * kInvE4m3Max, kScaleFloor)
+                          : fmaxf(amax / kE4m3Max, kScaleFloor);
+    const float inv = rq * __builtin_amdgcn_rcpf(s);
+    float r[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        r[j] = __builtin_amdgcn_fmed3f(kNorm ? z[j] * inv : div_round_to_odd(z[j], s, inv), -kE4m3Max,
+                                       kE4m3Max);
+    const uint32_t lo = pack4_e4m3(r[0], r[1], r[2], r[3]);
+    const uint32_t hi = pack4_e4m3(r[4], r[5], r[6], r[7]);
+    if (kFull || col < a.Nq) {  // Nq % 128 == 0: a lane's 8 codes are all in range
+        if (kFull) {
+            store_streaming(qout + col, lo, hi);
+        } else if (kVec) {
+            *reinterpret_cast<uint2 *>(qout + col) = make_uint2(lo, hi);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                qout[col + j] = static_cast<uint8_t>((j < 4 ? lo : hi) >> (8 * (j & 3)));
+        }
+    }
+
+    const int grp = c * (kChunk / kGroup) + lane / 16;
+    if ((lane & 15) == 0 && (kFull || grp < G)) {
+        const int64_t at = a.transpose_scale ? static_cast<int64_t>(grp) * a.M + m
+                                             : m * G + grp;
+        a.out_scale[at] = s;
+    }
 }
 
 // One row.  With z = x * gamma (exact in fp32: a product of two bf16 values)
@@ -198,54 +251,11 @@ __device__ __forceinline__ void process_row(const NormQuantParams &a, int64_t m,
     }  // kKv > 0
 
     // -- q: group amax, scale, e4m3fn codes -------------------------------------
-    const int G = a.Nq / kGroup;
-    uint8_t *qout = a.out_q + m * a.Nq;
 #pragma unroll
     for (int c = 0; c < kQ; ++c) {
-        const int col = c * kChunk + lane * 8;
         if (!kFull && c * kChunk >= a.Nq)
             break;  // uniform across the wave
-        float z[8];
-        if constexpr (kNorm)
-            times_gamma8(xq[c], gq[c], z);
-        else
-            unpack8_bf16(xq[c], z);
-        float amax = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            amax = fmaxf(amax, fabsf(z[j]));
-        // 16 lanes x 8 elements = one 128-element group
-        amax = row16_max(amax);
-        // without the norm, amax is an exact bf16 value and one correctly
-        // rounded division gives the scale bit for bit (once per group)
-        const float s = kNorm ? fmaxf((amax * rq) * kInvE4m3Max, kScaleFloor)
-                              : fmaxf(amax / kE4m3Max, kScaleFloor);
-        const float inv = rq * __builtin_amdgcn_rcpf(s);
-        float r[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            r[j] = __builtin_amdgcn_fmed3f(kNorm ? z[j] * inv : div_round_to_odd(z[j], s, inv), -kE4m3Max,
-                                           kE4m3Max);
-        const uint32_t lo = pack4_e4m3(r[0], r[1], r[2], r[3]);
-        const uint32_t hi = pack4_e4m3(r[4], r[5], r[6], r[7]);
-        if (kFull || col < a.Nq) {  // Nq % 128 == 0: a lane's 8 codes are all in range
-            if (kFull) {
-                store_streaming(qout + col, lo, hi);
-            } else if (kVec) {
-                *reinterpret_cast<uint2 *>(qout + col) = make_uint2(lo, hi);
-            } else {
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    qout[col + j] = static_cast<uint8_t>((j < 4 ? lo : hi) >> (8 * (j & 3)));
-            }
-        }
-
-        const int grp = c * (kChunk / kGroup) + lane / 16;
-        if ((lane & 15) == 0 && (kFull || grp < G)) {
-            const int64_t at = a.transpose_scale ? static_cast<int64_t>(grp) * a.M + m
-                                                 : m * G + grp;
-            a.out_scale[at] = s;
-        }
+        quant_chunk<kVec, kFull, kNorm>(a, m, lane, c, xq[c], gq[c], rq);
     }
 }
 
@@ -312,6 +322,68 @@ __global__ __launch_bounds__(256) void fused_dual_rmsnorm_group_quant_kernel(Nor
     }
 }
 
+// Single input, one row split over kSplit waves of a 4-wave block (for few
+// rows of many chunks, so that the grid still covers the chip).  Wave part p
+// of a row takes chunks p, p + kSplit, ... (at most kC of them).  With the
+// norm, each wave reduces its chunks' sums of squares, the kSplit wave sums
+// meet in LDS and are added in part order, so every wave of the row
+// derives the same rstd.
+template <int kC, int kSplit, bool kVec, bool kNorm>
+__global__ __launch_bounds__(256) void split_row_group_quant_kernel(NormQuantParams a) {
+    constexpr int kRowsPerBlock = 4 / kSplit;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int part = wave % kSplit;
+    const int64_t m =
+        static_cast<int64_t>(xcd_contiguous_block(blockIdx.x, gridDim.x)) * kRowsPerBlock + wave / kSplit;
+    const bool live = m < a.M;  // uniform per wave
+    if (!kNorm && !live)
+        return;  // no barrier below without the norm
+    const int nch = (a.Nq + kChunk - 1) / kChunk;
+
+    uint4 x[kC], graw[kC];
+    if (live) {
+        const uint16_t *row = a.q + m * a.q_stride;
+#pragma unroll
+        for (int i = 0; i < kC; ++i) {
+            const int col = (part + kSplit * i) * kChunk + lane * 8;
+            if constexpr (kNorm)
+                graw[i] = load8<kVec>(a.gamma_q, col, a.Nq);
+            x[i] = load8<kVec>(row, col, a.Nq);  // zeros past the row
+        }
+    }
+    float rq = 1.0f;
+    if constexpr (kNorm) {
+        __shared__ float wave_ssq[4];
+        float part_ssq[kC];
+#pragma unroll
+        for (int i = 0; i < kC; ++i)
+            part_ssq[i] = live ? sumsq8(x[i]) : 0.0f;
+        const float w = wave_sum(fold_sum<kC>(part_ssq));
+        if (lane == 0)
+            wave_ssq[wave] = w;
+        __syncthreads();
+        const int first = wave - part;
+        float ssq = wave_ssq[first];
+#pragma unroll
+        for (int j = 1; j < kSplit; ++j)
+            ssq += wave_ssq[first + j];
+        rq = rstd_from_ssq(ssq, a.inv_nq, a.eps);
+    }
+    if (!live)
+        return;
+#pragma unroll
+    for (int i = 0; i < kC; ++i) {
+        const int c = part + kSplit * i;
+        if (c >= nch)
+            break;  // uniform across the wave
+        GammaSlice g;
+        if constexpr (kNorm)
+            g = prepare_gamma(graw[i]);
+        quant_chunk<kVec, false, kNorm>(a, m, lane, c, x[i], g, rq);
+    }
+}
+
 template <int kQ, int kKv, bool kVec, int kRows, bool kFull = false, bool kNorm = true>
 hipError_t launch_variant(const NormQuantParams &p, hipStream_t stream) {
     const int64_t waves = (p.M + kRows - 1) / kRows;
@@ -321,6 +393,15 @@ hipError_t launch_variant(const NormQuantParams &p, hipStream_t stream) {
         return hipErrorInvalidValue;
     hipLaunchKernelGGL((fused_dual_rmsnorm_group_quant_kernel<kQ, kKv, kVec, kRows, kFull, kNorm>),
                        dim3(static_cast<unsigned>(blocks)), dim3(waves_per_block * kWave), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <int kC, int kSplit, bool kVec, bool kNorm>
+hipError_t launch_split(const NormQuantParams &p, hipStream_t stream) {
+    constexpr int kRowsPerBlock = 4 / kSplit;
+    const int64_t blocks = (p.M + kRowsPerBlock - 1) / kRowsPerBlock;
+    hipLaunchKernelGGL((split_row_group_quant_kernel<kC, kSplit, kVec, kNorm>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -343,11 +424,20 @@ hipError_t launch_normquant(const NormQuantParams &p, hipStream_t stream) {
     return hipErrorInvalidValue;
 }
 
+// Below this many rows, one wave per row leaves CUs idle for wide rows.
+constexpr int64_t kSplitBelowRows = 2048;
+
 template <bool kNorm>
 hipError_t launch_single_kind(const NormQuantParams &p, hipStream_t stream) {
     const bool vec = aligned16(p.q) && (!kNorm || aligned16(p.gamma_q)) && aligned16(p.out_q) &&
                      (p.q_stride % 8) == 0;
     const int qch = (p.Nq + kChunk - 1) / kChunk;
+    // few rows of 4 or more chunks: split each row over 2 or 4 waves
+    if (p.M < kSplitBelowRows && qch >= 4) {
+        if (qch >= 8)
+            return vec ? launch_split<4, 4, true, kNorm>(p, stream) : launch_split<4, 4, false, kNorm>(p, stream);
+        return vec ? launch_split<4, 2, true, kNorm>(p, stream) : launch_split<4, 2, false, kNorm>(p, stream);
+    }
     if (vec && p.Nq == 3 * kChunk)  // 1536: the MLA q latent
         return launch_variant<3, 0, true, 1, true, kNorm>(p, stream);
     if (vec && p.Nq == 14 * kChunk)  // 7168: a DeepSeek hidden row

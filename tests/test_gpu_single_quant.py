@@ -91,10 +91,13 @@ def test_workload_parity(name, normalize):
 @pytest.mark.parametrize("normalize", [True, False], ids=["rmsnorm_quant", "quant"])
 @pytest.mark.parametrize("M,N,pad,seed", [(1, 128, 0, 21), (3, 256, 0, 22), (7, 640, 0, 23),
                                           (5, 8192, 0, 24), (33, 1024, 8, 25), (4099, 1536, 0, 26),
-                                          (9, 7168, 128, 27), (2, 4096, 0, 28)])
+                                          (9, 7168, 128, 27), (2, 4096, 0, 28), (3, 2048, 0, 30),
+                                          (1500, 7168, 0, 31), (2047, 2560, 8, 32), (2048, 3584, 0, 33)])
 def test_generic_shapes(M, N, pad, seed, normalize):
     """Tiny, ragged (partial 512-element chunks, rows not a multiple of the
-    4 rows per block), strided and largest widths, both layouts."""
+    rows per block), strided and largest widths, both layouts; below 2048
+    rows, rows of 4 or more chunks are split over 2 or 4 waves (2048 x 3584
+    is just above that, on one wave per row)."""
     dev = gpu_or_skip()
     x, gamma = W.single_input(M, N, seed=seed, pad=pad)
     for t in (0, 1):
