@@ -291,6 +291,36 @@ def sweep(torch, np, mi, W, wa, wb, dev, cold):
                 "us": round(us, 3), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
             del g, fns
             torch.cuda.empty_cache()
+    # tensor-parallel shards: rank r holds N/TP rows of W_a and W_b; the pair
+    # launch at decode sizes, the W_a shard alone at M = 256
+    for tp in (2, 4, 8):
+        na, nb = wa.codes.shape[0] // tp, wb.codes.shape[0] // tp
+        wac0, was = torch.from_numpy(wa.codes[:na]).to(dev), torch.from_numpy(wa.scale[:na // 128]).to(dev)
+        wbc0, wbs = torch.from_numpy(wb.codes[:nb]).to(dev), torch.from_numpy(wb.scale[:nb // 128]).to(dev)
+        for M in (1, 16, 64, 256):
+            a = torch.randint(0, 0x78, (M, 1536), dtype=torch.uint8, device=dev)
+            asc = (torch.rand((12, M), dtype=torch.float32, device=dev) + 0.5).T   # column-major
+            per = (algorithmic_bytes_gemm_pair(M, na, nb, 1536) if M <= 64
+                   else algorithmic_bytes_gemm(M, na, 1536))
+            nsets = max(1, COLD_BYTES // per + 1) if cold else 1
+            fns = []
+            for i in range(nsets):
+                wac = wac0 if i == 0 else wac0.clone()
+                oa = torch.empty((M, na), dtype=torch.bfloat16, device=dev)
+                if M <= 64:
+                    wbc = wbc0 if i == 0 else wbc0.clone()
+                    ob = torch.empty((M, nb), dtype=torch.bfloat16, device=dev)
+                    fns.append(mi.prepare_block_scaled_fp8_gemm_pair(a, asc, wac, was, oa, wbc, wbs, ob))
+                else:
+                    fns.append(mi.prepare_block_scaled_fp8_gemm(a, asc, wac, was, oa))
+            g = make_graph(torch, fns)
+            us = time_graph(torch, g, len(fns), max(1, 200 // len(fns)))
+            key = f"tp{tp}_pair_M{M}" if M <= 64 else f"tp{tp}_W_a_M{M}"
+            res[key] = {"N": [na, nb] if M <= 64 else na, "us": round(us, 3), "GB/s": round(per / us / 1e3, 1),
+                        "frac_hbm": round(per / us / 1e3 / HBM_PEAK_GBS, 4)}
+            del g, fns
+        del wac0, wbc0
+        torch.cuda.empty_cache()
     # GEMMs at M = 256
     M = 256
     a = torch.randint(0, 0x78, (M, 1536), dtype=torch.uint8, device=dev)
