@@ -439,8 +439,14 @@ __global__ __launch_bounds__(kWaves * kWave) void block_scaled_fp8_gemm_wide_ker
     const int lane = w.lane, wave = w.wave;
     const int64_t M = p.M, K = p.K;
     const int64_t S = (p.N + p.N2) / 16;  // subtiles of both consumers
-    const int64_t st0 = static_cast<int64_t>(blockIdx.x) * kNS;
-    const int m_base = wave * 16 * kMT;
+    // block -> (slab, row chunk): a block covers kWaves x 16 kMT rows; when
+    // that is fewer than M, the row chunks of one slab get consecutive ids,
+    // renumbered onto one XCD so that they share the slab through its L2
+    constexpr int kBlockRows = kWaves * 16 * kMT;
+    const int nm = static_cast<int>((M + kBlockRows - 1) / kBlockRows);
+    const int b = nm > 1 ? xcd_contiguous_block(blockIdx.x, gridDim.x) : static_cast<int>(blockIdx.x);
+    const int64_t st0 = static_cast<int64_t>(b / nm) * kNS;
+    const int m_base = (b % nm) * kBlockRows + wave * 16 * kMT;
 
     // LDS tiles.  A 16-row x 128-byte K-block tile of either operand takes
     // 2 KB: rows 8g..8g+7 fill the 1 KB slot g, row r of the slot at 128 r,
@@ -511,7 +517,6 @@ __global__ __launch_bounds__(kWaves * kWave) void block_scaled_fp8_gemm_wide_ker
     __builtin_amdgcn_s_barrier();
     constexpr int kCols = 16 * kNS;
     static_assert(kWaves * 16 * kMT * kCols * 2 <= W::P::kLds, "output tiles fit in the rings' LDS");
-    static_assert((16 * kMT * 2 * kNS) % kWave == 0, "whole pieces per lane");
     uint16_t *tile = reinterpret_cast<uint16_t *>(w.lds) + wave * (16 * kMT) * kCols;
 #pragma unroll
     for (int j = 0; j < kMT; ++j)
@@ -520,9 +525,12 @@ __global__ __launch_bounds__(kWaves * kWave) void block_scaled_fp8_gemm_wide_ker
             *reinterpret_cast<uint2 *>(tile + (16 * j + (lane & 15)) * kCols + 16 * t + 4 * (lane >> 4)) =
                 make_uint2(pack2_bf16(w.acc[j][t][0], w.acc[j][t][1]), pack2_bf16(w.acc[j][t][2], w.acc[j][t][3]));
     constexpr int kPieces = 2 * kNS;  // 16-byte pieces per row
+    constexpr int kTilePieces = 16 * kMT * kPieces;
 #pragma unroll
-    for (int i = 0; i < (16 * kMT * kPieces) / kWave; ++i) {
+    for (int i = 0; i < (kTilePieces + kWave - 1) / kWave; ++i) {
         const int pc = lane + i * kWave;
+        if (kTilePieces % kWave != 0 && pc >= kTilePieces)
+            break;
         const int row = pc / kPieces, col = 8 * (pc % kPieces);
         const int64_t m = m_base + row, st = st0 + col / 16;
         const v4u32 v = *reinterpret_cast<const v4u32 *>(tile + row * kCols + col);
@@ -774,8 +782,9 @@ hipError_t launch_decode_kb(const GemmParams &p, hipStream_t stream) {
 template <int kKB, int kNS, int kMT, int kWaves>
 hipError_t launch_wide(const GemmParams &p, hipStream_t stream) {
     using P = WidePlan<kKB, kNS, kMT, kWaves>;
-    const int64_t blocks = ((p.N + p.N2) / 16 + kNS - 1) / kNS;
-    if (blocks > 0x7FFFFFFF || p.M > kWaves * 16 * kMT)
+    const int64_t nm = (p.M + kWaves * 16 * kMT - 1) / (kWaves * 16 * kMT);
+    const int64_t blocks = ((p.N + p.N2) / 16 + kNS - 1) / kNS * nm;
+    if (blocks > 0x7FFFFFFF || p.M > 256)
         return hipErrorInvalidValue;
     auto kern = block_scaled_fp8_gemm_wide_kernel<kKB, kNS, kMT, kWaves>;
     static std::atomic<uint64_t> lds_set{0};
@@ -803,17 +812,31 @@ hipError_t launch_wide_ns(const GemmParams &p, hipStream_t stream) {
     return launch_wide<kKB, 6, kMT, kWideWaves>(p, stream);
 }
 
+template <int kKB, int kNS>
+hipError_t launch_wide_split(const GemmParams &p, int64_t slabs, hipStream_t stream) {
+    // row chunks of 128 if that already gives a block per CU, else of 64
+    const int64_t chunks128 = (p.M + 127) / 128;
+    if (slabs * chunks128 >= device_cu_count())
+        return launch_wide<kKB, kNS, 2, kWideWaves>(p, stream);
+    return launch_wide<kKB, kNS, 1, kWideWaves>(p, stream);
+}
+
 template <int kKB>
 hipError_t launch_wide_kb(const GemmParams &p, hipStream_t stream) {
-    // kWideWaves x 16 kMT rows cover M (at most 256)
-    if (p.M <= kWideWaves * 16)
+    static_assert(kWideWaves == 4, "a block covers 64 kMT rows");
+    if (p.M <= 64)
         return launch_wide_ns<kKB, 1>(p, stream);
-    if constexpr (kWideWaves * 32 >= 256)
+    // With weight slabs for fewer than half the CUs, split the rows over
+    // blocks (each slab is then read once per row chunk, the repeats from
+    // L2) rather than leave CUs idle; otherwise one block holds all M rows
+    // (measured: splitting a grid that fills more than half the CUs loses).
+    const int64_t S = (p.N + p.N2) / 16, cus = device_cu_count();
+    const int64_t slabs = (S + 1) / 2;  // at 2 subtiles per block
+    if (2 * slabs < cus)
+        return launch_wide_split<kKB, 2>(p, slabs, stream);
+    if (p.M <= 128)
         return launch_wide_ns<kKB, 2>(p, stream);
-    else if (p.M <= kWideWaves * 32)
-        return launch_wide_ns<kKB, 2>(p, stream);
-    else
-        return launch_wide_ns<kKB, 256 / (16 * kWideWaves)>(p, stream);
+    return launch_wide_ns<kKB, 4>(p, stream);
 }
 
 template <int kMT>
