@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--M", type=int, default=64, help="tokens per step")
     ap.add_argument("--scale-layout", choices=("row", "col"), default="col")
+    ap.add_argument("--weight-layout", choices=("preferred", "row", "tiled"), default="preferred",
+                    help="weight byte order (preferred: what mi_preferred_weight_layout says)")
     ap.add_argument("--warm", action="store_true", help="reuse one buffer set (cache-warm numbers)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="skip the M=1 / M=8192 / M=256 extras")
@@ -175,9 +177,11 @@ def bf16_dev(torch, np, a, dev):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
 
 
-def build_sets(torch, np, mi, W, M, layout, wa, wb, nsets, dev):
+def build_sets(torch, np, mi, W, M, layout, wa, wb, nsets, dev, tiled):
     """``nsets`` independent buffer sets for the full step (device copies of
-    the same seeded inputs), each with its own outputs."""
+    the same seeded inputs), each with its own outputs.  ``tiled``: the
+    weights are stored in the library's tiled layout (the load-time
+    relayout, done here once, outside any timed region)."""
     case = W.producer_activations(M) if M <= 256 else W.strided_batch(M)
     buf0 = bf16_dev(torch, np, case.buffer, dev)
     gq = bf16_dev(torch, np, case.gamma_q, dev)
@@ -186,6 +190,12 @@ def build_sets(torch, np, mi, W, M, layout, wa, wb, nsets, dev):
     wa_s0 = torch.from_numpy(wa.scale).to(dev)
     wb_c0 = torch.from_numpy(wb.codes).to(dev)
     wb_s0 = torch.from_numpy(wb.scale).to(dev)
+    if tiled:
+        wa_c0, wb_c0 = mi.relayout_weight(wa_c0), mi.relayout_weight(wb_c0)
+
+    def copy_weight(w):
+        return mi.TiledWeight(w.data.clone(), w.N, w.K) if tiled else w.clone()
+
     G = W.NQ // 128
     sets = []
     for i in range(nsets):
@@ -195,8 +205,8 @@ def build_sets(torch, np, mi, W, M, layout, wa, wb, nsets, dev):
         osc = torch.empty(M * G, dtype=torch.float32, device=dev)
         okv = torch.empty((M, W.NKV), dtype=torch.bfloat16, device=dev)
         scale = osc.as_strided((M, G), (1, M)) if layout else osc.view(M, G)
-        wa_c = wa_c0 if i == 0 else wa_c0.clone()
-        wb_c = wb_c0 if i == 0 else wb_c0.clone()
+        wa_c = wa_c0 if i == 0 else copy_weight(wa_c0)
+        wb_c = wb_c0 if i == 0 else copy_weight(wb_c0)
         oa = torch.empty((M, wa.codes.shape[0]), dtype=torch.bfloat16, device=dev)
         ob = torch.empty((M, wb.codes.shape[0]), dtype=torch.bfloat16, device=dev)
         sets.append({
@@ -291,6 +301,34 @@ def sweep(torch, np, mi, W, wa, wb, dev, cold):
                 "us": round(us, 3), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
             del g, fns
             torch.cuda.empty_cache()
+    # both weights in the tiled load-time layout: the pair at M = 1 / 64, W_a at M = 256
+    wat0, wbt0 = mi.relayout_weight(torch.from_numpy(wa.codes).to(dev)), mi.relayout_weight(
+        torch.from_numpy(wb.codes).to(dev))
+    was_d, wbs_d = torch.from_numpy(wa.scale).to(dev), torch.from_numpy(wb.scale).to(dev)
+    NA, NB = wa.codes.shape[0], wb.codes.shape[0]
+    for M in (1, 64, 256):
+        a = torch.randint(0, 0x78, (M, 1536), dtype=torch.uint8, device=dev)
+        asc = (torch.rand((12, M), dtype=torch.float32, device=dev) + 0.5).T
+        per = algorithmic_bytes_gemm_pair(M, NA, NB, 1536) if M <= 64 else algorithmic_bytes_gemm(M, NA, 1536)
+        nsets = max(1, COLD_BYTES // per + 1) if cold else 1
+        fns = []
+        for i in range(nsets):
+            wat = wat0 if i == 0 else mi.TiledWeight(wat0.data.clone(), NA, 1536)
+            oa = torch.empty((M, NA), dtype=torch.bfloat16, device=dev)
+            if M <= 64:
+                wbt = wbt0 if i == 0 else mi.TiledWeight(wbt0.data.clone(), NB, 1536)
+                ob = torch.empty((M, NB), dtype=torch.bfloat16, device=dev)
+                fns.append(mi.prepare_block_scaled_fp8_gemm_pair(a, asc, wat, was_d, oa, wbt, wbs_d, ob))
+            else:
+                fns.append(mi.prepare_block_scaled_fp8_gemm(a, asc, wat, was_d, oa))
+        g = make_graph(torch, fns)
+        us = time_graph(torch, g, len(fns), max(1, 200 // len(fns)))
+        key = f"tiled_pair_M{M}" if M <= 64 else f"tiled_W_a_M{M}"
+        res[key] = {"us": round(us, 3), "GB/s": round(per / us / 1e3, 1),
+                    "frac_hbm": round(per / us / 1e3 / HBM_PEAK_GBS, 4)}
+        del g, fns
+    del wat0, wbt0
+    torch.cuda.empty_cache()
     # tensor-parallel shards: rank r holds N/TP rows of W_a and W_b; the pair
     # launch at decode sizes, the W_a shard alone at M = 256
     for tp in (2, 4, 8):
@@ -390,7 +428,12 @@ def main():
     step_bytes = (algorithmic_bytes_normquant(M)
                   + algorithmic_bytes_gemm_pair(M, W.W_A_SHAPE[0], W.W_B_SHAPE[0], W.NQ))
     nsets = 1 if args.warm else max(2, COLD_BYTES // step_bytes + 1)
-    sets = build_sets(torch, np, mi, W, M, layout, wa, wb, nsets, dev)
+    if args.weight_layout == "preferred":
+        prefs = {mi.mi_preferred_weight_layout(*W.W_A_SHAPE), mi.mi_preferred_weight_layout(*W.W_B_SHAPE)}
+        tiled = prefs == {1}
+    else:
+        tiled = args.weight_layout == "tiled"
+    sets = build_sets(torch, np, mi, W, M, layout, wa, wb, nsets, dev, tiled)
     torch.cuda.synchronize()
 
     if args.kernel_loop:
@@ -472,6 +515,7 @@ def main():
                         f"block-scaled FP8 GEMMs with W_a [24576,1536] and W_b [8192,1536] sharing "
                         f"the (q_fp8, scale) pair, both in one launch",
             "M": M, "scale_layout": "column-major" if layout else "row-major",
+            "weight_layout": "tiled (relaid out once at load time)" if tiled else "row-major",
             "cache": "warm" if args.warm else f"cold ({nsets} rotating buffer sets, "
                                               f"{nsets * step_bytes / 2**30:.2f} GiB)",
             "timing": "HIP graph of one step per buffer set, replayed; HIP events",

@@ -49,7 +49,9 @@ typedef enum {
                            is required, or above a documented limit */
     MI_ERR_STRIDE = 3,  /* a row stride is smaller than the row width */
     MI_ERR_ALIGN = 4,   /* a GEMM operand is not 16-byte aligned */
-    MI_ERR_HIP = 5      /* the HIP launch reported an error */
+    MI_ERR_HIP = 5,     /* the HIP launch reported an error */
+    MI_ERR_ALIAS = 6,   /* an output is the same buffer as an input */
+    MI_ERR_LAYOUT = 7   /* unknown layout value */
 } mi_status;
 
 /* Quantisation group: one fp32 scale per 1 x 128 consecutive q elements. */
@@ -210,6 +212,81 @@ mi_status mi_block_scaled_fp8_gemm(
  */
 mi_status mi_block_scaled_fp8_gemm_pair(
     const uint8_t *a_fp8, const float *a_scale, int a_scale_transposed,
+    const uint8_t *w1_fp8, const float *w1_scale, uint16_t *out1_bf16, int64_t N1,
+    const uint8_t *w2_fp8, const float *w2_scale, uint16_t *out2_bf16, int64_t N2,
+    int64_t M, int64_t K,
+    hipStream_t stream);
+
+/*
+ * Weight layouts and capabilities (load-time weight relayout).
+ *
+ * [D56433] "实现拆解" items 1-3: a block-scale GEMM kernel that wants its
+ * weight relaid out at load time declares it with a capability flag, the
+ * relayout is done once at load time, and code that reads a weight directly
+ * keeps the plain layout; the relayout is a permutation, not an involution,
+ * so applying it twice corrupts the weight ("功能与动机").  Here the layout
+ * is an explicit argument of every GEMM call (as the As order is), the
+ * relayout is out of place and invertible, and a caller learns from
+ * mi_gemm_capabilities / mi_preferred_weight_layout whether to relayout.
+ *
+ * MI_WEIGHT_TILED: the [N, K] e4m3fn weight as N/16 x K/128 tiles of
+ * 2048 bytes, tile (s, kb) at byte (s * (K/128) + kb) * 2048 (the tiles of
+ * one 16-row subtile are contiguous); inside a tile, byte
+ * g * 1024 + r * 128 + 16 * p + b (g < 2, r < 8, p < 8, b < 16) holds
+ * w[16 s + 8 g + r][128 kb + 16 (p ^ r ^ g) + b].  This is the image the
+ * GEMM keeps in LDS for a 16 x 128 weight tile (bank-conflict-free
+ * fragment reads), so each 1 KB half is one contiguous direct load.  The
+ * block scales (w_scale) are not relaid out.
+ */
+typedef enum {
+    MI_WEIGHT_ROW_MAJOR = 0,
+    MI_WEIGHT_TILED = 1
+} mi_weight_layout;
+
+#define MI_CAP_AS_ROW_MAJOR 1u   /* GEMMs read row-major activation scales */
+#define MI_CAP_AS_COL_MAJOR 2u   /* ... and column-major ones */
+#define MI_CAP_WEIGHT_TILED 4u   /* GEMMs read MI_WEIGHT_TILED weights */
+
+/* The capability flags of this library's GEMMs (a constant bit set). */
+unsigned mi_gemm_capabilities(void);
+
+/*
+ * mi_preferred_weight_layout: the layout to store an [N, K] weight in at
+ * load time for the GEMMs of this library (N % 128 == 0, K % 128 == 0), or
+ * -1 for an invalid shape.  A weight that other code reads directly must
+ * stay MI_WEIGHT_ROW_MAJOR whatever this returns; both layouts give
+ * bit-identical GEMM results.
+ */
+int mi_preferred_weight_layout(int64_t N, int64_t K);
+
+/*
+ * mi_relayout_weight: out-of-place permutation of an [N, K] e4m3fn weight
+ * between the two layouts: from_layout -> to_layout (MI_WEIGHT_ROW_MAJOR ->
+ * MI_WEIGHT_TILED, or back; equal layouts copy).  src and dst are device
+ * buffers of N*K bytes, 16-byte aligned, not overlapping (src == dst is
+ * rejected with MI_ERR_ALIAS).  N % 16 == 0 (GEMM weights: N % 128), K % 128
+ * == 0.  Enqueued on `stream`.
+ */
+mi_status mi_relayout_weight(const uint8_t *src, int from_layout, uint8_t *dst, int to_layout,
+                             int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * mi_block_scaled_fp8_gemm_ex / mi_block_scaled_fp8_gemm_pair_ex: as
+ * mi_block_scaled_fp8_gemm / mi_block_scaled_fp8_gemm_pair (which read
+ * MI_WEIGHT_ROW_MAJOR weights) with the weight layout as an argument (one
+ * layout for both weights of a pair).  Results are bit-identical for both
+ * layouts.  A weight passed with the wrong layout value is not detected: the
+ * result is wrong.
+ */
+mi_status mi_block_scaled_fp8_gemm_ex(
+    const uint8_t *a_fp8, const float *a_scale, int a_scale_transposed,
+    const uint8_t *w_fp8, int w_layout, const float *w_scale,
+    uint16_t *out_bf16,
+    int64_t M, int64_t N, int64_t K,
+    hipStream_t stream);
+
+mi_status mi_block_scaled_fp8_gemm_pair_ex(
+    const uint8_t *a_fp8, const float *a_scale, int a_scale_transposed, int w_layout,
     const uint8_t *w1_fp8, const float *w1_scale, uint16_t *out1_bf16, int64_t N1,
     const uint8_t *w2_fp8, const float *w2_scale, uint16_t *out2_bf16, int64_t N2,
     int64_t M, int64_t K,

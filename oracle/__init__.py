@@ -63,6 +63,10 @@ def lib() -> ctypes.CDLL:
         L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_num_threads.argtypes = []
         L.oracle_group_quant.restype = None
+        L.oracle_tile_weight.restype = None
+        L.oracle_tile_weight.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+        L.oracle_untile_weight.restype = None
+        L.oracle_untile_weight.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
         L.oracle_group_quant.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                          ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         L.oracle_rmsnorm_group_quant.restype = None
@@ -71,6 +75,25 @@ def lib() -> ctypes.CDLL:
                                                  ctypes.c_void_p, ctypes.c_void_p]
         _lib = L
     return _lib
+
+
+def tile_weight(w: np.ndarray) -> np.ndarray:
+    """The tiled byte order of an [N, K] uint8 weight (flat, N*K bytes)."""
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    N, K = w.shape
+    assert N % 16 == 0 and K % GROUP == 0
+    out = np.zeros(N * K, np.uint8)
+    lib().oracle_tile_weight(_ptr(w), N, K, _ptr(out))
+    return out
+
+
+def untile_weight(tiled: np.ndarray, N: int, K: int) -> np.ndarray:
+    """Inverse of tile_weight: flat tiled bytes -> [N, K] row-major."""
+    tiled = np.ascontiguousarray(tiled, dtype=np.uint8).reshape(-1)
+    assert tiled.size == N * K and N % 16 == 0 and K % GROUP == 0
+    out = np.zeros((N, K), np.uint8)
+    lib().oracle_untile_weight(_ptr(tiled), N, K, _ptr(out))
+    return out
 
 
 def _ptr(a: np.ndarray | None):

@@ -11,10 +11,13 @@ from ._binding import (  # noqa: F401
     EXPORTED,
     LIB_PATH,
     MiError,
+    TiledWeight,
     lib,
     mi_block_scaled_fp8_gemm,
     mi_block_scaled_fp8_gemm_pair,
     mi_fused_dual_rmsnorm_group_quant,
+    mi_gemm_capabilities,
+    mi_preferred_weight_layout,
     mi_group_quant_1x128,
     mi_rmsnorm_group_quant,
     mi_negotiate_scale_layout,
@@ -24,5 +27,8 @@ from ._binding import (  # noqa: F401
     prepare_fused_dual_rmsnorm_group_quant,
     prepare_group_quant_1x128,
     prepare_rmsnorm_group_quant,
+    relayout_weight,
     scale_is_transposed,
+    untile_weight,
+    weight_already_tiled,
 )

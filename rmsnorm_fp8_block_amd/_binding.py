@@ -17,14 +17,21 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmi_normquant.so")
 GROUP = 128
 
-MI_OK, MI_ERR_NULL, MI_ERR_SHAPE, MI_ERR_STRIDE, MI_ERR_ALIGN, MI_ERR_HIP = range(6)
+MI_OK, MI_ERR_NULL, MI_ERR_SHAPE, MI_ERR_STRIDE, MI_ERR_ALIGN, MI_ERR_HIP, MI_ERR_ALIAS, MI_ERR_LAYOUT = range(8)
+MI_WEIGHT_ROW_MAJOR, MI_WEIGHT_TILED = 0, 1
+MI_CAP_AS_ROW_MAJOR, MI_CAP_AS_COL_MAJOR, MI_CAP_WEIGHT_TILED = 1, 2, 4
 
 EXPORTED = (
     "mi_fused_dual_rmsnorm_group_quant",
     "mi_rmsnorm_group_quant",
     "mi_group_quant_1x128",
     "mi_block_scaled_fp8_gemm",
+    "mi_block_scaled_fp8_gemm_ex",
     "mi_block_scaled_fp8_gemm_pair",
+    "mi_block_scaled_fp8_gemm_pair_ex",
+    "mi_gemm_capabilities",
+    "mi_preferred_weight_layout",
+    "mi_relayout_weight",
     "mi_negotiate_scale_layout",
     "mi_status_string",
 )
@@ -59,6 +66,16 @@ def lib() -> ctypes.CDLL:
         L.mi_block_scaled_fp8_gemm.argtypes = [p, p, c_int, p, p, p, i64, i64, i64, p]
         L.mi_block_scaled_fp8_gemm_pair.restype = c_int
         L.mi_block_scaled_fp8_gemm_pair.argtypes = [p, p, c_int, p, p, p, i64, p, p, p, i64, i64, i64, p]
+        L.mi_block_scaled_fp8_gemm_ex.restype = c_int
+        L.mi_block_scaled_fp8_gemm_ex.argtypes = [p, p, c_int, p, c_int, p, p, i64, i64, i64, p]
+        L.mi_block_scaled_fp8_gemm_pair_ex.restype = c_int
+        L.mi_block_scaled_fp8_gemm_pair_ex.argtypes = [p, p, c_int, c_int, p, p, p, i64, p, p, p, i64, i64, i64, p]
+        L.mi_gemm_capabilities.restype = ctypes.c_uint
+        L.mi_gemm_capabilities.argtypes = []
+        L.mi_preferred_weight_layout.restype = c_int
+        L.mi_preferred_weight_layout.argtypes = [i64, i64]
+        L.mi_relayout_weight.restype = c_int
+        L.mi_relayout_weight.argtypes = [p, c_int, p, c_int, i64, i64, p]
         L.mi_negotiate_scale_layout.restype = c_int
         L.mi_negotiate_scale_layout.argtypes = [ctypes.POINTER(c_int), c_int]
         L.mi_status_string.restype = ctypes.c_char_p
@@ -198,51 +215,83 @@ def scale_is_transposed(a_scale: torch.Tensor) -> bool:
     raise ValueError(f"a_scale strides {a_scale.stride()} are neither row- nor column-major")
 
 
-def mi_block_scaled_fp8_gemm(a: torch.Tensor, a_scale: torch.Tensor,
-                             w: torch.Tensor, w_scale: torch.Tensor,
-                             out: torch.Tensor | None = None,
-                             a_scale_transposed: bool | None = None):
-    """Block-scaled FP8 GEMM on the current stream: ``a`` uint8 [M, K],
-    ``a_scale`` fp32 [M, K/128] (row- or column-major, read from its strides
-    unless ``a_scale_transposed`` is given and agrees), ``w`` uint8 [N, K],
-    ``w_scale`` fp32 [N/128, K/128].  Returns bf16 [M, N]."""
-    for name, t, dt in (("a", a, torch.uint8), ("w", w, torch.uint8),
-                        ("w_scale", w_scale, torch.float32), ("a_scale", a_scale, torch.float32)):
-        if t.dtype != dt or t.dim() != 2:
-            raise ValueError(f"{name}: expected a 2-D {dt} tensor")
-    if not (a.is_contiguous() and w.is_contiguous() and w_scale.is_contiguous()):
-        raise ValueError("a, w and w_scale must be contiguous")
-    M, K = a.shape
-    N = w.shape[0]
-    if w.shape[1] != K or tuple(a_scale.shape) != (M, K // GROUP) or \
-            tuple(w_scale.shape) != (N // GROUP, K // GROUP):
-        raise ValueError("shape mismatch between a, a_scale, w, w_scale")
-    layout = scale_is_transposed(a_scale)
-    if a_scale_transposed is not None and M > 1 and bool(a_scale_transposed) != layout:
-        raise ValueError("a_scale_transposed disagrees with the strides of a_scale")
-    if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
-    if out.dtype != torch.bfloat16 or not out.is_contiguous() or tuple(out.shape) != (M, N):
-        raise ValueError("out must be a contiguous bf16 [M, N] tensor")
-    status = lib().mi_block_scaled_fp8_gemm(
-        _ptr(a), _ptr(a_scale), int(layout), _ptr(w), _ptr(w_scale), _ptr(out), M, N, K, _stream(a))
-    _check("mi_block_scaled_fp8_gemm", status)
-    return out
+class TiledWeight:
+    """An [N, K] e4m3fn weight in the MI_WEIGHT_TILED byte order (see
+    include/mi_normquant.h): ``data`` is a flat uint8 device tensor of N*K
+    bytes.  Only :func:`relayout_weight` makes one, so a weight cannot be
+    relaid out twice through this binding (the relayout is a permutation,
+    not an involution)."""
+
+    def __init__(self, data: torch.Tensor, N: int, K: int):
+        self.data, self.N, self.K = data, int(N), int(K)
+
+    @property
+    def shape(self):
+        return (self.N, self.K)
+
+    @property
+    def device(self):
+        return self.data.device
+
+
+def weight_already_tiled(w) -> bool:
+    return isinstance(w, TiledWeight)
+
+
+def mi_gemm_capabilities() -> int:
+    return int(lib().mi_gemm_capabilities())
+
+
+def mi_preferred_weight_layout(N: int, K: int) -> int:
+    return int(lib().mi_preferred_weight_layout(N, K))
+
+
+def relayout_weight(w: torch.Tensor) -> TiledWeight:
+    """Row-major uint8 [N, K] weight -> a new TiledWeight (on w's stream)."""
+    if isinstance(w, TiledWeight):
+        raise TypeError("weight is already tiled: relaying it out again would permute it twice")
+    if w.dtype != torch.uint8 or w.dim() != 2 or not w.is_contiguous():
+        raise ValueError("w: expected a contiguous 2-D uint8 tensor")
+    N, K = w.shape
+    dst = torch.empty(N * K, dtype=torch.uint8, device=w.device)
+    status = lib().mi_relayout_weight(_ptr(w), MI_WEIGHT_ROW_MAJOR, _ptr(dst), MI_WEIGHT_TILED, N, K, _stream(w))
+    _check("mi_relayout_weight", status)
+    return TiledWeight(dst, N, K)
+
+
+def untile_weight(tw: TiledWeight) -> torch.Tensor:
+    """TiledWeight -> a new row-major uint8 [N, K] tensor."""
+    if not isinstance(tw, TiledWeight):
+        raise TypeError("expected a TiledWeight")
+    dst = torch.empty((tw.N, tw.K), dtype=torch.uint8, device=tw.device)
+    status = lib().mi_relayout_weight(_ptr(tw.data), MI_WEIGHT_TILED, _ptr(dst), MI_WEIGHT_ROW_MAJOR, tw.N, tw.K,
+                                      _stream(dst))
+    _check("mi_relayout_weight", status)
+    return dst
+
+
+def _weight_arg(w):
+    """(data tensor, layout, N, K) of a row-major tensor or a TiledWeight."""
+    if isinstance(w, TiledWeight):
+        return w.data, MI_WEIGHT_TILED, w.N, w.K
+    if w.dtype != torch.uint8 or w.dim() != 2 or not w.is_contiguous():
+        raise ValueError("w: expected a contiguous 2-D uint8 tensor or a TiledWeight")
+    return w, MI_WEIGHT_ROW_MAJOR, w.shape[0], w.shape[1]
 
 
 def _check_gemm_operands(a, a_scale, w, w_scale):
-    for name, t, dt in (("a", a, torch.uint8), ("w", w, torch.uint8),
-                        ("w_scale", w_scale, torch.float32), ("a_scale", a_scale, torch.float32)):
+    """Returns (M, N, K, weight data tensor, weight layout)."""
+    for name, t, dt in (("a", a, torch.uint8), ("w_scale", w_scale, torch.float32),
+                        ("a_scale", a_scale, torch.float32)):
         if t.dtype != dt or t.dim() != 2:
             raise ValueError(f"{name}: expected a 2-D {dt} tensor")
-    if not (a.is_contiguous() and w.is_contiguous() and w_scale.is_contiguous()):
-        raise ValueError("a, w and w_scale must be contiguous")
+    if not (a.is_contiguous() and w_scale.is_contiguous()):
+        raise ValueError("a and w_scale must be contiguous")
+    wd, wl, N, Kw = _weight_arg(w)
     M, K = a.shape
-    N = w.shape[0]
-    if w.shape[1] != K or tuple(a_scale.shape) != (M, K // GROUP) or \
-            tuple(w_scale.shape) != (N // GROUP, K // GROUP):
+    if Kw != K or tuple(a_scale.shape) != (M, K // GROUP) or tuple(w_scale.shape) != (N // GROUP, K // GROUP):
         raise ValueError("shape mismatch between a, a_scale, w, w_scale")
-    return M, N, K
+    return M, N, K, wd, wl
 
 
 def _gemm_out(out, M, N, device):
@@ -253,22 +302,43 @@ def _gemm_out(out, M, N, device):
     return out
 
 
-def mi_block_scaled_fp8_gemm_pair(a: torch.Tensor, a_scale: torch.Tensor,
-                                  w1: torch.Tensor, w1_scale: torch.Tensor,
-                                  w2: torch.Tensor, w2_scale: torch.Tensor,
+def mi_block_scaled_fp8_gemm(a: torch.Tensor, a_scale: torch.Tensor, w, w_scale: torch.Tensor,
+                             out: torch.Tensor | None = None,
+                             a_scale_transposed: bool | None = None):
+    """Block-scaled FP8 GEMM on the current stream: ``a`` uint8 [M, K],
+    ``a_scale`` fp32 [M, K/128] (row- or column-major, read from its strides
+    unless ``a_scale_transposed`` is given and agrees), ``w`` uint8 [N, K]
+    (row-major) or a :class:`TiledWeight`, ``w_scale`` fp32 [N/128, K/128].
+    Returns bf16 [M, N]."""
+    M, N, K, wd, wl = _check_gemm_operands(a, a_scale, w, w_scale)
+    layout = scale_is_transposed(a_scale)
+    if a_scale_transposed is not None and M > 1 and bool(a_scale_transposed) != layout:
+        raise ValueError("a_scale_transposed disagrees with the strides of a_scale")
+    out = _gemm_out(out, M, N, a.device)
+    status = lib().mi_block_scaled_fp8_gemm_ex(
+        _ptr(a), _ptr(a_scale), int(layout), _ptr(wd), wl, _ptr(w_scale), _ptr(out), M, N, K, _stream(a))
+    _check("mi_block_scaled_fp8_gemm_ex", status)
+    return out
+
+
+def mi_block_scaled_fp8_gemm_pair(a: torch.Tensor, a_scale: torch.Tensor, w1, w1_scale: torch.Tensor,
+                                  w2, w2_scale: torch.Tensor,
                                   out1: torch.Tensor | None = None,
                                   out2: torch.Tensor | None = None):
     """Both consumers of one pre-quantised pair on the current stream:
     returns (bf16 [M, N1], bf16 [M, N2]), each equal to
-    mi_block_scaled_fp8_gemm(a, a_scale, w_i, w_i_scale)."""
-    M, N1, K = _check_gemm_operands(a, a_scale, w1, w1_scale)
-    _, N2, K2 = _check_gemm_operands(a, a_scale, w2, w2_scale)
+    mi_block_scaled_fp8_gemm(a, a_scale, w_i, w_i_scale).  Both weights in
+    the same layout."""
+    M, N1, K, wd1, wl1 = _check_gemm_operands(a, a_scale, w1, w1_scale)
+    _, N2, _, wd2, wl2 = _check_gemm_operands(a, a_scale, w2, w2_scale)
+    if wl1 != wl2:
+        raise ValueError("both weights of a pair must have the same layout")
     out1 = _gemm_out(out1, M, N1, a.device)
     out2 = _gemm_out(out2, M, N2, a.device)
-    status = lib().mi_block_scaled_fp8_gemm_pair(
-        _ptr(a), _ptr(a_scale), int(scale_is_transposed(a_scale)), _ptr(w1), _ptr(w1_scale), _ptr(out1), N1,
-        _ptr(w2), _ptr(w2_scale), _ptr(out2), N2, M, K, _stream(a))
-    _check("mi_block_scaled_fp8_gemm_pair", status)
+    status = lib().mi_block_scaled_fp8_gemm_pair_ex(
+        _ptr(a), _ptr(a_scale), int(scale_is_transposed(a_scale)), wl1, _ptr(wd1), _ptr(w1_scale), _ptr(out1), N1,
+        _ptr(wd2), _ptr(w2_scale), _ptr(out2), N2, M, K, _stream(a))
+    _check("mi_block_scaled_fp8_gemm_pair_ex", status)
     return out1, out2
 
 
@@ -337,24 +407,26 @@ def prepare_group_quant_1x128(x, transpose_scale, out_q, out_scale) -> PreparedC
 
 
 def prepare_block_scaled_fp8_gemm(a, a_scale, w, w_scale, out) -> PreparedCall:
-    """Marshal the arguments of mi_block_scaled_fp8_gemm once; the As layout
-    is read from the strides of ``a_scale`` ([M, K/128])."""
-    M, K = a.shape
-    N = w.shape[0]
-    if tuple(a_scale.shape) != (M, K // GROUP) or tuple(out.shape) != (M, N):
+    """Marshal the arguments of mi_block_scaled_fp8_gemm_ex once; the As
+    layout is read from the strides of ``a_scale`` ([M, K/128]), the weight
+    layout from the type of ``w``."""
+    M, N, K, wd, wl = _check_gemm_operands(a, a_scale, w, w_scale)
+    if tuple(out.shape) != (M, N):
         raise ValueError("shape mismatch")
-    args = (_ptr(a), _ptr(a_scale), int(scale_is_transposed(a_scale)), _ptr(w), _ptr(w_scale),
+    args = (_ptr(a), _ptr(a_scale), int(scale_is_transposed(a_scale)), _ptr(wd), wl, _ptr(w_scale),
             _ptr(out), M, N, K)
-    return PreparedCall("mi_block_scaled_fp8_gemm", args, (a, a_scale, w, w_scale, out), a.device)
+    return PreparedCall("mi_block_scaled_fp8_gemm_ex", args, (a, a_scale, wd, w_scale, out), a.device)
 
 
 def prepare_block_scaled_fp8_gemm_pair(a, a_scale, w1, w1_scale, out1, w2, w2_scale, out2) -> PreparedCall:
-    """Marshal the arguments of mi_block_scaled_fp8_gemm_pair once."""
-    M, K = a.shape
-    N1, N2 = w1.shape[0], w2.shape[0]
-    if tuple(a_scale.shape) != (M, K // GROUP) or tuple(out1.shape) != (M, N1) or tuple(out2.shape) != (M, N2):
+    """Marshal the arguments of mi_block_scaled_fp8_gemm_pair_ex once."""
+    M, N1, K, wd1, wl1 = _check_gemm_operands(a, a_scale, w1, w1_scale)
+    _, N2, _, wd2, wl2 = _check_gemm_operands(a, a_scale, w2, w2_scale)
+    if wl1 != wl2:
+        raise ValueError("both weights of a pair must have the same layout")
+    if tuple(out1.shape) != (M, N1) or tuple(out2.shape) != (M, N2):
         raise ValueError("shape mismatch")
-    args = (_ptr(a), _ptr(a_scale), int(scale_is_transposed(a_scale)), _ptr(w1), _ptr(w1_scale), _ptr(out1), N1,
-            _ptr(w2), _ptr(w2_scale), _ptr(out2), N2, M, K)
-    return PreparedCall("mi_block_scaled_fp8_gemm_pair", args,
-                        (a, a_scale, w1, w1_scale, out1, w2, w2_scale, out2), a.device)
+    args = (_ptr(a), _ptr(a_scale), int(scale_is_transposed(a_scale)), wl1, _ptr(wd1), _ptr(w1_scale), _ptr(out1),
+            N1, _ptr(wd2), _ptr(w2_scale), _ptr(out2), N2, M, K)
+    return PreparedCall("mi_block_scaled_fp8_gemm_pair_ex", args,
+                        (a, a_scale, wd1, w1_scale, out1, wd2, w2_scale, out2), a.device)

@@ -96,12 +96,14 @@ extern "C" mi_status mi_group_quant_1x128(
                               stream);
 }
 
-extern "C" mi_status mi_block_scaled_fp8_gemm(
+extern "C" mi_status mi_block_scaled_fp8_gemm_ex(
     const uint8_t *a_fp8, const float *a_scale, int a_scale_transposed,
-    const uint8_t *w_fp8, const float *w_scale,
+    const uint8_t *w_fp8, int w_layout, const float *w_scale,
     uint16_t *out_bf16,
     int64_t M, int64_t N, int64_t K,
     hipStream_t stream) {
+    if (w_layout != MI_WEIGHT_ROW_MAJOR && w_layout != MI_WEIGHT_TILED)
+        return MI_ERR_LAYOUT;
     if (M < 0 || N <= 0 || K <= 0 || (N % MI_GROUP) != 0 || (K % MI_GROUP) != 0)
         return MI_ERR_SHAPE;
     if (M == 0)
@@ -122,15 +124,28 @@ extern "C" mi_status mi_block_scaled_fp8_gemm(
     p.M = M;
     p.N = N;
     p.K = K;
+    p.w_tiled = w_layout == MI_WEIGHT_TILED ? 1 : 0;
     return mi::launch_block_scaled_gemm(p, stream) == hipSuccess ? MI_OK : MI_ERR_HIP;
 }
 
-extern "C" mi_status mi_block_scaled_fp8_gemm_pair(
+extern "C" mi_status mi_block_scaled_fp8_gemm(
     const uint8_t *a_fp8, const float *a_scale, int a_scale_transposed,
+    const uint8_t *w_fp8, const float *w_scale,
+    uint16_t *out_bf16,
+    int64_t M, int64_t N, int64_t K,
+    hipStream_t stream) {
+    return mi_block_scaled_fp8_gemm_ex(a_fp8, a_scale, a_scale_transposed, w_fp8, MI_WEIGHT_ROW_MAJOR, w_scale,
+                                       out_bf16, M, N, K, stream);
+}
+
+extern "C" mi_status mi_block_scaled_fp8_gemm_pair_ex(
+    const uint8_t *a_fp8, const float *a_scale, int a_scale_transposed, int w_layout,
     const uint8_t *w1_fp8, const float *w1_scale, uint16_t *out1_bf16, int64_t N1,
     const uint8_t *w2_fp8, const float *w2_scale, uint16_t *out2_bf16, int64_t N2,
     int64_t M, int64_t K,
     hipStream_t stream) {
+    if (w_layout != MI_WEIGHT_ROW_MAJOR && w_layout != MI_WEIGHT_TILED)
+        return MI_ERR_LAYOUT;
     if (M < 0 || N1 <= 0 || N2 <= 0 || K <= 0 || (N1 % MI_GROUP) != 0 || (N2 % MI_GROUP) != 0 ||
         (K % MI_GROUP) != 0)
         return MI_ERR_SHAPE;
@@ -157,7 +172,52 @@ extern "C" mi_status mi_block_scaled_fp8_gemm_pair(
     p.w_scale2 = w2_scale;
     p.out2 = out2_bf16;
     p.N2 = N2;
+    p.w_tiled = w_layout == MI_WEIGHT_TILED ? 1 : 0;
     return mi::launch_block_scaled_gemm_pair(p, stream) == hipSuccess ? MI_OK : MI_ERR_HIP;
+}
+
+extern "C" mi_status mi_block_scaled_fp8_gemm_pair(
+    const uint8_t *a_fp8, const float *a_scale, int a_scale_transposed,
+    const uint8_t *w1_fp8, const float *w1_scale, uint16_t *out1_bf16, int64_t N1,
+    const uint8_t *w2_fp8, const float *w2_scale, uint16_t *out2_bf16, int64_t N2,
+    int64_t M, int64_t K,
+    hipStream_t stream) {
+    return mi_block_scaled_fp8_gemm_pair_ex(a_fp8, a_scale, a_scale_transposed, MI_WEIGHT_ROW_MAJOR, w1_fp8,
+                                            w1_scale, out1_bf16, N1, w2_fp8, w2_scale, out2_bf16, N2, M, K, stream);
+}
+
+extern "C" unsigned mi_gemm_capabilities(void) {
+    return MI_CAP_AS_ROW_MAJOR | MI_CAP_AS_COL_MAJOR | MI_CAP_WEIGHT_TILED;
+}
+
+extern "C" int mi_preferred_weight_layout(int64_t N, int64_t K) {
+    if (N <= 0 || K <= 0 || (N % MI_GROUP) != 0 || (K % MI_GROUP) != 0)
+        return -1;
+    return MI_WEIGHT_TILED;
+}
+
+extern "C" mi_status mi_relayout_weight(const uint8_t *src, int from_layout, uint8_t *dst, int to_layout,
+                                        int64_t N, int64_t K, hipStream_t stream) {
+    const auto known = [](int l) { return l == MI_WEIGHT_ROW_MAJOR || l == MI_WEIGHT_TILED; };
+    if (!known(from_layout) || !known(to_layout))
+        return MI_ERR_LAYOUT;
+    if (N < 0 || K < 0 || (N % 16) != 0 || (K % MI_GROUP) != 0)
+        return MI_ERR_SHAPE;
+    if (N == 0 || K == 0)
+        return MI_OK;
+    if (!src || !dst)
+        return MI_ERR_NULL;
+    if (src == dst)
+        return MI_ERR_ALIAS;
+    if (!aligned16(src) || !aligned16(dst))
+        return MI_ERR_ALIGN;
+    if (from_layout == to_layout)
+        return hipMemcpyAsync(dst, src, static_cast<size_t>(N * K), hipMemcpyDeviceToDevice, stream) == hipSuccess
+                   ? MI_OK
+                   : MI_ERR_HIP;
+    return mi::launch_weight_relayout(src, dst, N, K, to_layout == MI_WEIGHT_TILED, stream) == hipSuccess
+               ? MI_OK
+               : MI_ERR_HIP;
 }
 
 extern "C" int mi_negotiate_scale_layout(const int *consumer_wants_transposed, int n) {
@@ -184,6 +244,10 @@ extern "C" const char *mi_status_string(mi_status s) {
         return "MI_ERR_ALIGN: operand not 16-byte aligned";
     case MI_ERR_HIP:
         return "MI_ERR_HIP: kernel launch failed";
+    case MI_ERR_ALIAS:
+        return "MI_ERR_ALIAS: an output is the same buffer as an input";
+    case MI_ERR_LAYOUT:
+        return "MI_ERR_LAYOUT: unknown layout value";
     }
     return "unknown mi_status";
 }

@@ -60,6 +60,33 @@ __device__ __forceinline__ v8i join(const uint4 &lo, const uint4 &hi) {
     return r;
 }
 
+// Weight fragment of lane L for the register-path kernels: row L % 16 of a
+// 16-row subtile, chunks 2q and 2q + 1 (q = L / 16) of each K-block.
+//  row-major: at row * K + 32 q, K-blocks 128 bytes apart;
+//  tiled: the subtile's K-block tiles are 2 KB apart, and inside a tile
+//  chunk c of row 8 g + r sits at g * 1024 + r * 128 + 16 (c ^ r ^ g), so
+//  the two chunks are the aligned 32-byte pair at (2q) ^ (f & 6), f = r ^ g,
+//  in swapped order when f is odd.
+struct WeightFrag {
+    int64_t lane_off;  // from the subtile's first byte
+    int64_t kstride;   // between K-blocks
+    bool swap;         // halves in swapped order
+};
+
+__device__ __forceinline__ WeightFrag weight_frag(int lane, int64_t K, int tiled) {
+    const int rho = lane & 15, q = lane >> 4;
+    if (!tiled)
+        return {rho * K + 32 * q, kBlk, false};
+    const int g = rho >> 3, r = rho & 7, f = r ^ g;
+    return {g * 1024 + r * 128 + 16 * ((2 * q) ^ (f & 6)), 16 * kBlk, (f & 1) != 0};
+}
+
+__device__ __forceinline__ v8i load_weight_frag(const uint8_t *p, bool swap) {
+    const uint4 *src = reinterpret_cast<const uint4 *>(p);
+    const uint4 a = src[0], b = src[1];
+    return swap ? join(b, a) : join(a, b);
+}
+
 __device__ __forceinline__ v4f mfma_e4m3_16x16x128(const v8i &a, const v8i &b) {
     const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
     // format 0 = e4m3 for both operands; zero scale operands select the
@@ -83,7 +110,8 @@ __global__ __launch_bounds__(256) void block_scaled_fp8_gemm_kernel(GemmParams p
     const int64_t m0 = static_cast<int64_t>(b % mgrid) * (kMT * 16);
     const int64_t n0 = static_cast<int64_t>(b / mgrid) * kTileN + wave * 16;
 
-    const uint8_t *wrow = p.w + (n0 + (lane & 15)) * K + 32 * (lane >> 4);
+    const WeightFrag wfrag = weight_frag(lane, K, p.w_tiled);
+    const uint8_t *wrow = p.w + n0 * K + wfrag.lane_off;
     const float *bs_row = p.w_scale + (n0 / kBlk) * KB;
 
     v4f acc[kMT];
@@ -99,10 +127,8 @@ __global__ __launch_bounds__(256) void block_scaled_fp8_gemm_kernel(GemmParams p
         v8i wf[kStageKb];
 #pragma unroll
         for (int j = 0; j < kStageKb; ++j) {
-            if (j < kc) {
-                const uint4 *src = reinterpret_cast<const uint4 *>(wrow + static_cast<int64_t>(kb0 + j) * kBlk);
-                wf[j] = join(src[0], src[1]);
-            }
+            if (j < kc)
+                wf[j] = load_weight_frag(wrow + (kb0 + j) * wfrag.kstride, wfrag.swap);
         }
 
         __syncthreads();  // the previous stage's LDS reads are done
@@ -298,6 +324,7 @@ struct WideWave {
     const uint8_t *wbase[P::kNW];  // uniform: weight slot sources
     int wslot[P::kNW];             // uniform: their LDS slots
     uint32_t w_off;                // per lane
+    uint32_t w_kstride;            // uniform: bytes between K-blocks of a subtile
     const uint8_t *a;
     uint32_t a_off[kMT][2];        // per lane: m-tile j, row half g
     uint32_t frag_lo, frag_hi;     // per lane: LDS offsets of its fragment halves inside a 2 KB tile
@@ -314,7 +341,7 @@ struct WideWave {
         uint8_t *dst = lds + P::kWOff + (s % P::kRW) * P::kWStage;
 #pragma unroll
         for (int i = 0; i < P::kNW; ++i)
-            __builtin_amdgcn_global_load_lds(wbase[i] + s * kBlk + w_off, dst + wslot[i] * P::kSlot, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(wbase[i] + s * w_kstride + w_off, dst + wslot[i] * P::kSlot, 16, 0, 0);
     }
 
     __device__ __forceinline__ void issue_a(int s) {
@@ -467,9 +494,13 @@ __global__ __launch_bounds__(kWaves * kWave) void block_scaled_fp8_gemm_wide_ker
     // repeat row M - 1: their results are never stored.
     // Weight slot (subtile, row half) = (slot / 2, slot % 2); this wave loads
     // slots (wave + kWaves i) mod 2 kNS, all of row half wave % 2.
+    // A tiled weight holds each (subtile, K-block) tile as exactly this LDS
+    // image: a slot is 1 KB of contiguous bytes.
     {
         const int g = wave & 1;
-        w.w_off = static_cast<uint32_t>((8 * g + lrow) * K + 16 * (lchunk ^ lrow ^ g));
+        w.w_off = p.w_tiled ? static_cast<uint32_t>(g * 1024 + lane * 16)
+                            : static_cast<uint32_t>((8 * g + lrow) * K + 16 * (lchunk ^ lrow ^ g));
+        w.w_kstride = p.w_tiled ? 16 * kBlk : kBlk;
     }
 #pragma unroll
     for (int i = 0; i < W::P::kNW; ++i) {
@@ -650,14 +681,13 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void block_scaled_fp8_gemm_de
 
     // spare waves read their block's last subtile (L2 hits, never used)
     const int64_t st_ld = min<int64_t>(st, min<int64_t>(static_cast<int64_t>(blockIdx.x) * spb + spb, S) - 1);
-    const uint8_t *wrow = p.w + (st_ld * 16 + (lane & 15)) * K + 32 * (lane >> 4);
+    const WeightFrag wfrag = weight_frag(lane, K, p.w_tiled);
+    const uint8_t *wrow = p.w + st_ld * 16 * K + wfrag.lane_off;
     v8i wf[kRingN];
     float bs[kKB];
 #pragma unroll
-    for (int kb = 0; kb < kRingN; ++kb) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(wrow + kb * kBlk);
-        wf[kb] = join(src[0], src[1]);
-    }
+    for (int kb = 0; kb < kRingN; ++kb)
+        wf[kb] = load_weight_frag(wrow + kb * wfrag.kstride, wfrag.swap);
     const float *bs_row = p.w_scale + (st_ld * 16 / kBlk) * kKB;
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb)
@@ -711,10 +741,8 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void block_scaled_fp8_gemm_de
             }
         }
         // refill the slot just consumed with K-block kb + kRing
-        if (kb + kRingN < kKB) {
-            const uint4 *src = reinterpret_cast<const uint4 *>(wrow + (kb + kRingN) * kBlk);
-            wf[kb % kRingN] = join(src[0], src[1]);
-        }
+        if (kb + kRingN < kKB)
+            wf[kb % kRingN] = load_weight_frag(wrow + (kb + kRingN) * wfrag.kstride, wfrag.swap);
 #pragma unroll
         for (int t = 0; t < kMT; ++t) {
 #pragma unroll
@@ -893,6 +921,43 @@ hipError_t launch_block_scaled_gemm(const GemmParams &p, hipStream_t stream) {
     if (p.M <= 48)
         return launch_mt<3>(p, stream);
     return launch_mt<4>(p, stream);
+}
+
+namespace {
+
+// Row-major <-> tiled weight, one thread per 16-byte chunk of the tiled
+// image: a wave covers one 1 KB slot (8 rows x 128 bytes of one K-block),
+// contiguous on the tiled side, 8 whole 128-byte row pieces on the other.
+__global__ __launch_bounds__(256) void weight_relayout_kernel(const uint8_t *src, uint8_t *dst, int64_t N,
+                                                              int64_t K, int to_tiled) {
+    const int64_t chunks = N * K / 16;
+    const int64_t KB = K / kBlk;
+    for (int64_t o = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; o < chunks;
+         o += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        // o = ((st * KB + kb) * 2 + g) * 64 + r * 8 + pos
+        const int pos = static_cast<int>(o & 7), r = static_cast<int>((o >> 3) & 7),
+                  g = static_cast<int>((o >> 6) & 1);
+        const int64_t tile = o >> 7, st = tile / KB, kb = tile % KB;
+        const int c = pos ^ r ^ g;
+        const int64_t rm = ((st * 16 + 8 * g + r) * K + kb * kBlk) / 16 + c;  // row-major chunk
+        const uint4 *s = reinterpret_cast<const uint4 *>(src);
+        uint4 *d = reinterpret_cast<uint4 *>(dst);
+        if (to_tiled)
+            d[o] = s[rm];
+        else
+            d[rm] = s[o];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_weight_relayout(const uint8_t *src, uint8_t *dst, int64_t N, int64_t K, bool to_tiled,
+                                  hipStream_t stream) {
+    const int64_t chunks = N * K / 16;
+    const int64_t blocks = std::min<int64_t>((chunks + 255) / 256, 65536);
+    hipLaunchKernelGGL(weight_relayout_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, src, dst,
+                       N, K, to_tiled ? 1 : 0);
+    return hipGetLastError();
 }
 
 hipError_t launch_block_scaled_gemm_pair(const GemmParams &p, hipStream_t stream) {

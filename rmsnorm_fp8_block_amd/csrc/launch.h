@@ -43,9 +43,15 @@ struct GemmParams {
     const float *w_scale2 = nullptr;
     uint16_t *out2 = nullptr;
     int64_t N2 = 0;
+    // weight byte order of w (and w2): 0 row-major, 1 tiled (see
+    // mi_relayout_weight_tiled)
+    int w_tiled = 0;
 };
 
 hipError_t launch_normquant(const NormQuantParams &p, hipStream_t stream);
+// weight [N, K] row-major <-> tiled (to_tiled selects the direction)
+hipError_t launch_weight_relayout(const uint8_t *src, uint8_t *dst, int64_t N, int64_t K, bool to_tiled,
+                                  hipStream_t stream);
 // one input (kv unused): RMSNorm + group quant (normalize) or the group
 // quant of q itself (gamma_q, eps unused)
 hipError_t launch_group_quant(const NormQuantParams &p, bool normalize, hipStream_t stream);

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for s in range(6):
+    for s in range(8):
         assert mi.mi_status_string(s).startswith(("MI_OK", "MI_ERR"))
     assert mi.mi_status_string(99) == "unknown mi_status"
 
@@ -157,3 +157,52 @@ def test_binding_raises_on_error_status():
     with pytest.raises(mi.MiError) as e:
         B._check("x", B.MI_ERR_SHAPE)
     assert e.value.status == B.MI_ERR_SHAPE
+
+
+def relayout(L, **kw):
+    a = dict(src=FAKE, fl=0, dst=ctypes.c_void_p(0x2000), tl=1, N=256, K=1536)
+    a.update(kw)
+    return L.mi_relayout_weight(a["src"], a["fl"], a["dst"], a["tl"], a["N"], a["K"], NULL)
+
+
+def test_relayout_validation(L):
+    for k, v in (("fl", 2), ("tl", -1)):
+        assert relayout(L, **{k: v}) == B.MI_ERR_LAYOUT, k
+    for k, v in (("N", 8), ("K", 100), ("N", -16)):
+        assert relayout(L, **{k: v}) == B.MI_ERR_SHAPE, (k, v)
+    assert relayout(L, N=0) == B.MI_OK
+    for k in ("src", "dst"):
+        assert relayout(L, **{k: NULL}) == B.MI_ERR_NULL, k
+    assert relayout(L, dst=FAKE) == B.MI_ERR_ALIAS
+    assert relayout(L, dst=ctypes.c_void_p(0x2008)) == B.MI_ERR_ALIGN
+
+
+def test_gemm_ex_layout_validation(L):
+    st = L.mi_block_scaled_fp8_gemm_ex(FAKE, FAKE, 0, FAKE, 2, FAKE, FAKE, 4, 1024, 1536, NULL)
+    assert st == B.MI_ERR_LAYOUT
+    st = L.mi_block_scaled_fp8_gemm_pair_ex(FAKE, FAKE, 0, 5, FAKE, FAKE, FAKE, 256, FAKE, FAKE, FAKE, 256, 4, 1536,
+                                            NULL)
+    assert st == B.MI_ERR_LAYOUT
+    # a valid layout value goes on to the ordinary checks
+    st = L.mi_block_scaled_fp8_gemm_ex(FAKE, FAKE, 0, FAKE, 1, FAKE, FAKE, 4, 1000, 1536, NULL)
+    assert st == B.MI_ERR_SHAPE
+
+
+def test_capabilities_and_preferred_layout(L):
+    caps = mi.mi_gemm_capabilities()
+    assert caps == B.MI_CAP_AS_ROW_MAJOR | B.MI_CAP_AS_COL_MAJOR | B.MI_CAP_WEIGHT_TILED
+    assert mi.mi_preferred_weight_layout(24576, 1536) in (B.MI_WEIGHT_ROW_MAJOR, B.MI_WEIGHT_TILED)
+    for n, k in ((100, 1536), (256, 0), (-128, 128)):
+        assert mi.mi_preferred_weight_layout(n, k) == -1
+
+
+def test_binding_refuses_a_second_relayout():
+    """The relayout is a permutation, not an involution: a TiledWeight is
+    never relaid out again (checked before any device work)."""
+    import torch
+    tw = B.TiledWeight(torch.empty(0, dtype=torch.uint8), 128, 128)
+    assert mi.weight_already_tiled(tw)
+    with pytest.raises(TypeError):
+        mi.relayout_weight(tw)
+    with pytest.raises(TypeError):
+        mi.untile_weight(torch.empty((128, 128), dtype=torch.uint8))
