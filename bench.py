@@ -234,10 +234,12 @@ def cpu_baseline(np, W, M, layout, wa, wb):
                       f"{wa.codes.shape[0] + wb.codes.shape[0]} output columns ({dt:.1f} s wall)"}
 
 
-def sweep(torch, np, mi, W, wa, wb, dev, cold):
+def sweep(torch, np, mi, W, wa, wb, dev, cold, tiled):
     """Extra figures of the metric: norm-quant at M=1 (us/call) and M=8192
     (GB/s, both layouts); the single-input quantisations at [8192, 1536] and
-    [256, 7168] (GB/s); the GEMMs at M=256 (TFLOP/s, % of FP8 MFMA peak)."""
+    [256, 7168] (GB/s); the GEMMs at M=256 (TFLOP/s, % of FP8 MFMA peak) and at
+    tensor-parallel shard shapes, with the step's weight layout (``tiled``),
+    and the pair / W_a in both layouts, timed back to back."""
     res = {}
     gq = bf16_dev(torch, np, W.gammas()[0], dev)
     gk = bf16_dev(torch, np, W.gammas()[1], dev)
@@ -301,9 +303,17 @@ def sweep(torch, np, mi, W, wa, wb, dev, cold):
                 "us": round(us, 3), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
             del g, fns
             torch.cuda.empty_cache()
-    # both weights in the tiled load-time layout: the pair at M = 1 / 64, W_a at M = 256
-    wat0, wbt0 = mi.relayout_weight(torch.from_numpy(wa.codes).to(dev)), mi.relayout_weight(
-        torch.from_numpy(wb.codes).to(dev))
+    # weights in the given layout (tiled: the load-time relayout, done once here)
+    def dev_weight(codes, as_tiled):
+        w = torch.from_numpy(np.ascontiguousarray(codes)).to(dev)
+        return mi.relayout_weight(w) if as_tiled else w
+
+    def copy_weight(w):
+        return mi.TiledWeight(w.data.clone(), w.N, w.K) if isinstance(w, mi.TiledWeight) else w.clone()
+
+    # both weight layouts back to back at the same point of the run (timings
+    # drift with the position in a long run, so only adjacent figures are
+    # compared): the pair at M = 1 / 64 and W_a at M = 256
     was_d, wbs_d = torch.from_numpy(wa.scale).to(dev), torch.from_numpy(wb.scale).to(dev)
     NA, NB = wa.codes.shape[0], wb.codes.shape[0]
     for M in (1, 64, 256):
@@ -311,30 +321,32 @@ def sweep(torch, np, mi, W, wa, wb, dev, cold):
         asc = (torch.rand((12, M), dtype=torch.float32, device=dev) + 0.5).T
         per = algorithmic_bytes_gemm_pair(M, NA, NB, 1536) if M <= 64 else algorithmic_bytes_gemm(M, NA, 1536)
         nsets = max(1, COLD_BYTES // per + 1) if cold else 1
-        fns = []
-        for i in range(nsets):
-            wat = wat0 if i == 0 else mi.TiledWeight(wat0.data.clone(), NA, 1536)
-            oa = torch.empty((M, NA), dtype=torch.bfloat16, device=dev)
-            if M <= 64:
-                wbt = wbt0 if i == 0 else mi.TiledWeight(wbt0.data.clone(), NB, 1536)
-                ob = torch.empty((M, NB), dtype=torch.bfloat16, device=dev)
-                fns.append(mi.prepare_block_scaled_fp8_gemm_pair(a, asc, wat, was_d, oa, wbt, wbs_d, ob))
-            else:
-                fns.append(mi.prepare_block_scaled_fp8_gemm(a, asc, wat, was_d, oa))
-        g = make_graph(torch, fns)
-        us = time_graph(torch, g, len(fns), max(1, 200 // len(fns)))
-        key = f"tiled_pair_M{M}" if M <= 64 else f"tiled_W_a_M{M}"
-        res[key] = {"us": round(us, 3), "GB/s": round(per / us / 1e3, 1),
-                    "frac_hbm": round(per / us / 1e3 / HBM_PEAK_GBS, 4)}
-        del g, fns
-    del wat0, wbt0
-    torch.cuda.empty_cache()
+        for lay in ("rowmajor", "tiled"):
+            wat0 = dev_weight(wa.codes, lay == "tiled")
+            wbt0 = dev_weight(wb.codes, lay == "tiled") if M <= 64 else None
+            fns = []
+            for i in range(nsets):
+                wat = wat0 if i == 0 else copy_weight(wat0)
+                oa = torch.empty((M, NA), dtype=torch.bfloat16, device=dev)
+                if M <= 64:
+                    wbt = wbt0 if i == 0 else copy_weight(wbt0)
+                    ob = torch.empty((M, NB), dtype=torch.bfloat16, device=dev)
+                    fns.append(mi.prepare_block_scaled_fp8_gemm_pair(a, asc, wat, was_d, oa, wbt, wbs_d, ob))
+                else:
+                    fns.append(mi.prepare_block_scaled_fp8_gemm(a, asc, wat, was_d, oa))
+            g = make_graph(torch, fns)
+            us = time_graph(torch, g, len(fns), max(1, 200 // len(fns)))
+            key = f"{lay}_pair_M{M}" if M <= 64 else f"{lay}_W_a_M{M}"
+            res[key] = {"us": round(us, 3), "GB/s": round(per / us / 1e3, 1),
+                        "frac_hbm": round(per / us / 1e3 / HBM_PEAK_GBS, 4)}
+            del g, fns, wat0, wbt0
+            torch.cuda.empty_cache()
     # tensor-parallel shards: rank r holds N/TP rows of W_a and W_b; the pair
     # launch at decode sizes, the W_a shard alone at M = 256
     for tp in (2, 4, 8):
         na, nb = wa.codes.shape[0] // tp, wb.codes.shape[0] // tp
-        wac0, was = torch.from_numpy(wa.codes[:na]).to(dev), torch.from_numpy(wa.scale[:na // 128]).to(dev)
-        wbc0, wbs = torch.from_numpy(wb.codes[:nb]).to(dev), torch.from_numpy(wb.scale[:nb // 128]).to(dev)
+        wac0, was = dev_weight(wa.codes[:na], tiled), torch.from_numpy(wa.scale[:na // 128]).to(dev)
+        wbc0, wbs = dev_weight(wb.codes[:nb], tiled), torch.from_numpy(wb.scale[:nb // 128]).to(dev)
         for M in (1, 16, 64, 256):
             a = torch.randint(0, 0x78, (M, 1536), dtype=torch.uint8, device=dev)
             asc = (torch.rand((12, M), dtype=torch.float32, device=dev) + 0.5).T   # column-major
@@ -343,10 +355,10 @@ def sweep(torch, np, mi, W, wa, wb, dev, cold):
             nsets = max(1, COLD_BYTES // per + 1) if cold else 1
             fns = []
             for i in range(nsets):
-                wac = wac0 if i == 0 else wac0.clone()
+                wac = wac0 if i == 0 else copy_weight(wac0)
                 oa = torch.empty((M, na), dtype=torch.bfloat16, device=dev)
                 if M <= 64:
-                    wbc = wbc0 if i == 0 else wbc0.clone()
+                    wbc = wbc0 if i == 0 else copy_weight(wbc0)
                     ob = torch.empty((M, nb), dtype=torch.bfloat16, device=dev)
                     fns.append(mi.prepare_block_scaled_fp8_gemm_pair(a, asc, wac, was, oa, wbc, wbs, ob))
                 else:
@@ -365,13 +377,13 @@ def sweep(torch, np, mi, W, wa, wb, dev, cold):
     asc = torch.rand((M, 12), dtype=torch.float32, device=dev) + 0.5
     for name, wt in (("W_a", wa), ("W_b", wb)):
         N, K = wt.codes.shape
-        wc0 = torch.from_numpy(wt.codes).to(dev)
+        wc0 = dev_weight(wt.codes, tiled)
         ws = torch.from_numpy(wt.scale).to(dev)
         per = algorithmic_bytes_gemm(M, N, K)
         nsets = max(1, COLD_BYTES // per + 1) if cold else 1
         fns = []
         for i in range(nsets):
-            wc = wc0 if i == 0 else wc0.clone()
+            wc = wc0 if i == 0 else copy_weight(wc0)
             fns.append(mi.prepare_block_scaled_fp8_gemm(
                 a, asc, wc, ws, torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
         g = make_graph(torch, fns)
@@ -527,7 +539,7 @@ def main():
                    "cus": props.multi_processor_count},
     }
     if not args.no_sweep:
-        line["sweep"] = sweep(torch, np, mi, W, wa, wb, dev, cold=not args.warm)
+        line["sweep"] = sweep(torch, np, mi, W, wa, wb, dev, cold=not args.warm, tiled=tiled)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(np, W, M, layout, wa, wb)
     print(json.dumps(line), flush=True)
