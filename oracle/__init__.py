@@ -63,6 +63,13 @@ def lib() -> ctypes.CDLL:
         L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_num_threads.argtypes = []
         L.oracle_group_quant.restype = None
+        L.oracle_e8m0_decode.restype = ctypes.c_double
+        L.oracle_e8m0_decode.argtypes = [ctypes.c_uint8]
+        L.oracle_dual_rmsnorm_group_quant_e8m0.restype = None
+        L.oracle_dual_rmsnorm_group_quant_e8m0.argtypes = [
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_float, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         L.oracle_tile_weight.restype = None
         L.oracle_tile_weight.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
         L.oracle_untile_weight.restype = None
@@ -75,6 +82,41 @@ def lib() -> ctypes.CDLL:
                                                  ctypes.c_void_p, ctypes.c_void_p]
         _lib = L
     return _lib
+
+
+def e8m0_decode(e: int) -> float:
+    """Value of an e8m0 scale byte: 2^(e - 127) (255: NaN)."""
+    return lib().oracle_e8m0_decode(int(e))
+
+
+def e8m0_decode_array(e: np.ndarray) -> np.ndarray:
+    table = np.array([e8m0_decode(i) for i in range(256)], dtype=np.float64)
+    return table[np.asarray(e, dtype=np.uint8)]
+
+
+def dual_rmsnorm_group_quant_e8m0(q, kv, gamma_q, gamma_kv, eps, transpose_scale, want_ratio=False):
+    """The dual RMSNorm + per-1x128 group quant with e8m0 (power-of-two)
+    scales.  Returns a dict with ``q`` (uint8 codes [M, Nq]), ``scale``
+    (uint8 e8m0 bytes, M*Nq/128 in the requested layout), ``kv`` (uint16
+    bf16 [M, Nkv]) and, when asked, ``ratio`` (y * 2^-e, float64)."""
+    q, qs = _row_view(q, np.uint16)
+    kv, ks = _row_view(kv, np.uint16)
+    M, Nq = q.shape
+    Nkv = kv.shape[1]
+    assert kv.shape[0] == M and Nq % GROUP == 0
+    gamma_q = np.ascontiguousarray(gamma_q, dtype=np.uint16)
+    gamma_kv = np.ascontiguousarray(gamma_kv, dtype=np.uint16)
+    out_q = np.zeros((M, Nq), np.uint8)
+    out_s = np.zeros(M * (Nq // GROUP), np.uint8)
+    out_kv = np.zeros((M, Nkv), np.uint16)
+    ratio = np.zeros((M, Nq), np.float64) if want_ratio else None
+    lib().oracle_dual_rmsnorm_group_quant_e8m0(
+        _ptr(q), qs, _ptr(kv), ks, _ptr(gamma_q), _ptr(gamma_kv), ctypes.c_float(eps), M, Nq, Nkv,
+        int(bool(transpose_scale)), _ptr(out_q), _ptr(out_s), _ptr(out_kv), _ptr(ratio))
+    res = {"q": out_q, "scale": out_s, "kv": out_kv}
+    if want_ratio:
+        res["ratio"] = ratio
+    return res
 
 
 def tile_weight(w: np.ndarray) -> np.ndarray:

@@ -361,6 +361,85 @@ void oracle_block_scaled_fp8_gemm(
 }
 
 /* ---------------------------------------------------------------------------
+ * Power-of-two (e8m0) scales.
+ *
+ * [D56433] "风险与影响" item 3 (weight block scales stored as
+ * float8_e8m0fnu) and the PRHub digest of vLLM PR #56560 (the native gfx950
+ * MXFP8 GEMM, scales as e8m0 exponents, K in blocks of 128): an e8m0 scale
+ * is a bare exponent byte E with value 2^(E - 127) (E = 255: NaN).  The pages
+ * give no rule for picking a power-of-two scale for a group; the reading
+ * taken: the smallest power of two not below the group's fp32-path scale
+ * before rounding, s = 2^ceil(log2(max(amax / 448, 1e-12))), so that
+ * |y| / s <= 448 (no clamping) and y / s is exact (a power-of-two scaling),
+ * leaving the e4m3 rounding as the only rounding.
+ * ------------------------------------------------------------------------- */
+double oracle_e8m0_decode(uint8_t e)
+{
+    if (e == 0xFF)
+        return NAN;
+    return ldexp(1.0, (int)e - 127);
+}
+
+/* exponent e of the smallest power of two >= v (v > 0, finite) */
+static int pow2_ceil_exponent(double v)
+{
+    int E;
+    double f = frexp(v, &E); /* v = f * 2^E, f in [0.5, 1) */
+    return f == 0.5 ? E - 1 : E;
+}
+
+/* Dual RMSNorm + per-1x128 group quantisation with e8m0 scales: the
+ * normalised values y (and kv) exactly as oracle_dual_rmsnorm_group_quant
+ * computes them (fused semantics), then per group e = ceil(log2(max(amax /
+ * 448, 1e-12))), scale byte e + 127 in the requested layout, code =
+ * e4m3(y * 2^-e).  out_ratio (nullable): y * 2^-e. */
+void oracle_dual_rmsnorm_group_quant_e8m0(
+    const uint16_t *q, int64_t q_row_stride,
+    const uint16_t *kv, int64_t kv_row_stride,
+    const uint16_t *gamma_q, const uint16_t *gamma_kv,
+    float eps, int64_t M, int64_t Nq, int64_t Nkv,
+    int transpose_scale,
+    uint8_t *out_q, uint8_t *out_scale, uint16_t *out_kv,
+    double *out_ratio)
+{
+    const int64_t G = Nq / ORACLE_GROUP;
+    double *y = (double *)malloc(sizeof(double) * (size_t)(M * Nq));
+    uint8_t *tmp_q = (uint8_t *)malloc((size_t)(M * Nq));
+    float *tmp_s = (float *)malloc(sizeof(float) * (size_t)(M * G));
+    oracle_dual_rmsnorm_group_quant(q, q_row_stride, kv, kv_row_stride, gamma_q, gamma_kv, eps, M, Nq, Nkv,
+                                    transpose_scale, 0, tmp_q, tmp_s, out_kv, NULL, y);
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t g = 0; g < G; ++g) {
+            const double *yg = y + m * Nq + g * ORACLE_GROUP;
+            double amax = 0.0;
+            for (int j = 0; j < ORACLE_GROUP; ++j)
+                if (fabs(yg[j]) > amax)
+                    amax = fabs(yg[j]);
+            double t = amax / ORACLE_E4M3_MAX;
+            if (t < (double)ORACLE_SCALE_FLOOR)
+                t = (double)ORACLE_SCALE_FLOOR;
+            int e = pow2_ceil_exponent(t);
+            out_scale[transpose_scale ? g * M + m : m * G + g] = (uint8_t)(e + 127);
+            for (int j = 0; j < ORACLE_GROUP; ++j) {
+                int64_t i = m * Nq + g * ORACLE_GROUP + j;
+                double ratio = ldexp(yg[j], -e);
+                if (out_ratio)
+                    out_ratio[i] = ratio;
+                double c = ratio;
+                if (c > ORACLE_E4M3_MAX)
+                    c = ORACLE_E4M3_MAX;
+                if (c < -ORACLE_E4M3_MAX)
+                    c = -ORACLE_E4M3_MAX;
+                out_q[i] = oracle_e4m3_encode(c);
+            }
+        }
+    free(y);
+    free(tmp_q);
+    free(tmp_s);
+}
+
+/* ---------------------------------------------------------------------------
  * Load-time weight relayout (the tiled byte order of the library's GEMMs).
  *
  * [D56433] "实现拆解" items 1-3: a block-scale GEMM may ask for its weight to
