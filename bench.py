@@ -371,6 +371,64 @@ def sweep(torch, np, mi, W, wa, wb, dev, cold, tiled):
             del g, fns
         del wac0, wbc0
         torch.cuda.empty_cache()
+    # e8m0 (power-of-two) scales: the whole step at M = 64 (norm-quant + pair),
+    # and the GEMMs at M = 256, weights tiled
+    ea = W.block_fp8_weight_e8m0(*W.W_A_SHAPE, W.W_A_SEED)
+    eb = W.block_fp8_weight_e8m0(*W.W_B_SHAPE, W.W_B_SEED)
+    eac0, ebc0 = dev_weight(ea.codes, True), dev_weight(eb.codes, True)
+    eas, ebs = torch.from_numpy(ea.scale).to(dev), torch.from_numpy(eb.scale).to(dev)
+    NA, NB = ea.codes.shape[0], eb.codes.shape[0]
+    M = 64
+    case = W.producer_activations(M)
+    buf0 = bf16_dev(torch, np, case.buffer, dev)
+    gq, gk = bf16_dev(torch, np, case.gamma_q, dev), bf16_dev(torch, np, case.gamma_kv, dev)
+    per = algorithmic_bytes_normquant(M) - 3 * M * 12 + algorithmic_bytes_gemm_pair(M, NA, NB, 1536) - \
+        3 * (M * 12 + (NA + NB) // 128 * 12)   # 1-byte scales instead of 4-byte ones
+    nsets = max(1, COLD_BYTES // per + 1) if cold else 1
+    step_fns, pair_fns = [], []
+    for i in range(nsets):
+        b = buf0 if i == 0 else buf0.clone()
+        oq = torch.empty((M, W.NQ), dtype=torch.uint8, device=dev)
+        osc = torch.empty(M * 12, dtype=torch.uint8, device=dev)
+        okv = torch.empty((M, W.NKV), dtype=torch.bfloat16, device=dev)
+        nq = mi.prepare_fused_dual_rmsnorm_group_quant_e8m0(b[:, :W.NQ], b[:, W.NQ:], gq, gk, W.EPS, True, oq, osc, okv)
+        wac = eac0 if i == 0 else copy_weight(eac0)
+        wbc = ebc0 if i == 0 else copy_weight(ebc0)
+        oa = torch.empty((M, NA), dtype=torch.bfloat16, device=dev)
+        ob = torch.empty((M, NB), dtype=torch.bfloat16, device=dev)
+        gp = mi.prepare_block_scaled_fp8_gemm_pair(oq, osc.as_strided((M, 12), (1, M)), wac, eas, oa, wbc, ebs, ob)
+        step_fns += [nq, gp]
+        pair_fns.append(gp)
+    g = make_graph(torch, step_fns)
+    res["e8m0_step_M64_us"] = round(time_graph(torch, g, nsets, max(1, 200 // nsets)), 3)
+    del g
+    g = make_graph(torch, pair_fns)
+    us = time_graph(torch, g, nsets, max(1, 200 // nsets))
+    pb = algorithmic_bytes_gemm_pair(M, NA, NB, 1536) - 3 * (M * 12 + (NA + NB) // 128 * 12)
+    res["e8m0_pair_M64"] = {"us": round(us, 3), "GB/s": round(pb / us / 1e3, 1),
+                            "frac_hbm": round(pb / us / 1e3 / HBM_PEAK_GBS, 4)}
+    del g, step_fns, pair_fns
+    torch.cuda.empty_cache()
+    M = 256
+    a = torch.randint(0, 0x78, (M, 1536), dtype=torch.uint8, device=dev)
+    asc = torch.randint(118, 127, (12, M), dtype=torch.uint8, device=dev).T
+    for name, wc0, ws, N in (("W_a", eac0, eas, NA), ("W_b", ebc0, ebs, NB)):
+        perg = algorithmic_bytes_gemm(M, N, 1536) - 3 * (M * 12 + N // 128 * 12)
+        nsets = max(1, COLD_BYTES // perg + 1) if cold else 1
+        fns = []
+        for i in range(nsets):
+            wc = wc0 if i == 0 else copy_weight(wc0)
+            fns.append(mi.prepare_block_scaled_fp8_gemm(a, asc, wc, ws, torch.empty((M, N), dtype=torch.bfloat16,
+                                                                                      device=dev)))
+        g = make_graph(torch, fns)
+        us = time_graph(torch, g, len(fns), max(1, 200 // len(fns)))
+        tf = gemm_flops(M, N, 1536) / us / 1e6
+        res[f"e8m0_gemm_{name}_M256"] = {"us": round(us, 3), "TFLOP/s": round(tf, 1),
+                                         "frac_fp8_mfma": round(tf / FP8_MFMA_PEAK_TFLOPS, 4),
+                                         "GB/s": round(perg / us / 1e3, 1)}
+        del g, fns
+    del eac0, ebc0
+    torch.cuda.empty_cache()
     # GEMMs at M = 256
     M = 256
     a = torch.randint(0, 0x78, (M, 1536), dtype=torch.uint8, device=dev)

@@ -246,6 +246,7 @@ typedef enum {
 #define MI_CAP_AS_ROW_MAJOR 1u   /* GEMMs read row-major activation scales */
 #define MI_CAP_AS_COL_MAJOR 2u   /* ... and column-major ones */
 #define MI_CAP_WEIGHT_TILED 4u   /* GEMMs read MI_WEIGHT_TILED weights */
+#define MI_CAP_SCALE_E8M0 8u     /* e8m0 (power-of-two) scale entry points */
 
 /* The capability flags of this library's GEMMs (a constant bit set). */
 unsigned mi_gemm_capabilities(void);
@@ -289,6 +290,64 @@ mi_status mi_block_scaled_fp8_gemm_pair_ex(
     const uint8_t *a_fp8, const float *a_scale, int a_scale_transposed, int w_layout,
     const uint8_t *w1_fp8, const float *w1_scale, uint16_t *out1_bf16, int64_t N1,
     const uint8_t *w2_fp8, const float *w2_scale, uint16_t *out2_bf16, int64_t N2,
+    int64_t M, int64_t K,
+    hipStream_t stream);
+
+/*
+ * e8m0 (power-of-two) scales
+ *
+ * [D56433] "风险与影响" item 3: weight block scales stored as e8m0
+ * (float8_e8m0fnu) exponents; the PRHub digest of vLLM PR #56560: the native
+ * gfx950 MXFP8 GEMM, whose scales are e8m0 exponents applied by the matrix
+ * cores.  An e8m0 scale is a byte E with value 2^(E - 127) (255 is NaN).
+ * The pages give no rule for choosing a group's power-of-two scale; here it
+ * is the smallest power of two not below the fp32 scale before rounding:
+ *   e      = ceil(log2(max(max_{i in g} |y_i| / 448, 1e-12))), E = e + 127
+ *   code_i = e4m3fn_rne(y_i * 2^-e)          (|y_i| * 2^-e <= 448)
+ * so y_i * 2^-e is exact and the e4m3 rounding is the only one; a group's
+ * largest code lies in [224, 448].  The GEMM then needs no fp32 scale
+ * arithmetic: the matrix core applies 2^(Ea-127) and 2^(Eb-127) to the
+ * operands of each 128-deep K-block and accumulates the whole K in place.
+ */
+
+/*
+ * mi_fused_dual_rmsnorm_group_quant_e8m0: mi_fused_dual_rmsnorm_group_quant
+ * with e8m0 scales (out_scale_e8m0: M*G exponent bytes in the layout chosen by
+ * transpose_scale).  kv is identical to the fp32-scale call.  In fp32 the
+ * group maximum times rstd / 448 is within a few ulps of its exact value;
+ * when that value is that close to a power of two, the exponent may be one
+ * higher or lower than the exact rule gives.
+ */
+mi_status mi_fused_dual_rmsnorm_group_quant_e8m0(
+    const uint16_t *q, int64_t q_row_stride,
+    const uint16_t *kv, int64_t kv_row_stride,
+    const uint16_t *gamma_q, const uint16_t *gamma_kv,
+    float eps, int64_t M, int64_t Nq, int64_t Nkv,
+    int transpose_scale,
+    uint8_t *out_q_fp8, uint8_t *out_scale_e8m0, uint16_t *out_kv,
+    hipStream_t stream);
+
+/*
+ * mi_block_scaled_fp8_gemm_e8m0 / mi_block_scaled_fp8_gemm_pair_e8m0: the
+ * block-scaled GEMM (single / both consumers) with e8m0 scales:
+ *   out[m, n] = bf16_rne( sum_kb 2^(As[m,kb]-127) * 2^(Bs[n/128,kb]-127)
+ *                         * sum_{k in kb} dec(a[m,k]) * dec(w[n,k]) )
+ * a_scale_e8m0: M*K/128 bytes, [M, K/128] row-major (a_scale_transposed 0)
+ * or [K/128, M] (1); w*_scale_e8m0: [N/128, K/128] bytes row-major; both
+ * 4-byte aligned.  Other arguments as mi_block_scaled_fp8_gemm_ex /
+ * mi_block_scaled_fp8_gemm_pair_ex.
+ */
+mi_status mi_block_scaled_fp8_gemm_e8m0(
+    const uint8_t *a_fp8, const uint8_t *a_scale_e8m0, int a_scale_transposed,
+    const uint8_t *w_fp8, int w_layout, const uint8_t *w_scale_e8m0,
+    uint16_t *out_bf16,
+    int64_t M, int64_t N, int64_t K,
+    hipStream_t stream);
+
+mi_status mi_block_scaled_fp8_gemm_pair_e8m0(
+    const uint8_t *a_fp8, const uint8_t *a_scale_e8m0, int a_scale_transposed, int w_layout,
+    const uint8_t *w1_fp8, const uint8_t *w1_scale_e8m0, uint16_t *out1_bf16, int64_t N1,
+    const uint8_t *w2_fp8, const uint8_t *w2_scale_e8m0, uint16_t *out2_bf16, int64_t N2,
     int64_t M, int64_t K,
     hipStream_t stream);
 

@@ -19,16 +19,19 @@ GROUP = 128
 
 MI_OK, MI_ERR_NULL, MI_ERR_SHAPE, MI_ERR_STRIDE, MI_ERR_ALIGN, MI_ERR_HIP, MI_ERR_ALIAS, MI_ERR_LAYOUT = range(8)
 MI_WEIGHT_ROW_MAJOR, MI_WEIGHT_TILED = 0, 1
-MI_CAP_AS_ROW_MAJOR, MI_CAP_AS_COL_MAJOR, MI_CAP_WEIGHT_TILED = 1, 2, 4
+MI_CAP_AS_ROW_MAJOR, MI_CAP_AS_COL_MAJOR, MI_CAP_WEIGHT_TILED, MI_CAP_SCALE_E8M0 = 1, 2, 4, 8
 
 EXPORTED = (
     "mi_fused_dual_rmsnorm_group_quant",
+    "mi_fused_dual_rmsnorm_group_quant_e8m0",
     "mi_rmsnorm_group_quant",
     "mi_group_quant_1x128",
     "mi_block_scaled_fp8_gemm",
     "mi_block_scaled_fp8_gemm_ex",
+    "mi_block_scaled_fp8_gemm_e8m0",
     "mi_block_scaled_fp8_gemm_pair",
     "mi_block_scaled_fp8_gemm_pair_ex",
+    "mi_block_scaled_fp8_gemm_pair_e8m0",
     "mi_gemm_capabilities",
     "mi_preferred_weight_layout",
     "mi_relayout_weight",
@@ -62,6 +65,13 @@ def lib() -> ctypes.CDLL:
         L.mi_rmsnorm_group_quant.argtypes = [p, i64, p, ctypes.c_float, i64, i64, c_int, p, p, p]
         L.mi_group_quant_1x128.restype = c_int
         L.mi_group_quant_1x128.argtypes = [p, i64, i64, i64, c_int, p, p, p]
+        L.mi_fused_dual_rmsnorm_group_quant_e8m0.restype = c_int
+        L.mi_fused_dual_rmsnorm_group_quant_e8m0.argtypes = [
+            p, i64, p, i64, p, p, ctypes.c_float, i64, i64, i64, c_int, p, p, p, p]
+        L.mi_block_scaled_fp8_gemm_e8m0.restype = c_int
+        L.mi_block_scaled_fp8_gemm_e8m0.argtypes = [p, p, c_int, p, c_int, p, p, i64, i64, i64, p]
+        L.mi_block_scaled_fp8_gemm_pair_e8m0.restype = c_int
+        L.mi_block_scaled_fp8_gemm_pair_e8m0.argtypes = [p, p, c_int, c_int, p, p, p, i64, p, p, p, i64, i64, i64, p]
         L.mi_block_scaled_fp8_gemm.restype = c_int
         L.mi_block_scaled_fp8_gemm.argtypes = [p, p, c_int, p, p, p, i64, i64, i64, p]
         L.mi_block_scaled_fp8_gemm_pair.restype = c_int
@@ -153,6 +163,43 @@ def mi_fused_dual_rmsnorm_group_quant(q: torch.Tensor, kv: torch.Tensor,
         M, Nq, Nkv, int(bool(transpose_scale)), _ptr(out_q), _ptr(out_scale), _ptr(out_kv),
         _stream(q))
     _check("mi_fused_dual_rmsnorm_group_quant", status)
+    return out_q, _scale_view(out_scale, M, G, transpose_scale), out_kv
+
+
+E8M0_DTYPES = (torch.uint8, getattr(torch, "float8_e8m0fnu", torch.uint8))
+
+
+def _u8(t: torch.Tensor) -> torch.Tensor:
+    """An e8m0 scale tensor as uint8 bytes (float8_e8m0fnu is viewed)."""
+    return t if t.dtype == torch.uint8 else t.view(torch.uint8)
+
+
+def mi_fused_dual_rmsnorm_group_quant_e8m0(q: torch.Tensor, kv: torch.Tensor,
+                                           gamma_q: torch.Tensor, gamma_kv: torch.Tensor,
+                                           eps: float, transpose_scale: bool,
+                                           out_q: torch.Tensor | None = None,
+                                           out_scale: torch.Tensor | None = None,
+                                           out_kv: torch.Tensor | None = None):
+    """As :func:`mi_fused_dual_rmsnorm_group_quant` with e8m0 (power-of-two)
+    scales: ``scale`` is a uint8 tensor of exponent bytes with logical shape
+    [M, Nq/128] and the requested layout."""
+    qs = _rows(q, "q", torch.bfloat16)
+    ks = _rows(kv, "kv", torch.bfloat16)
+    M, Nq = q.shape
+    Nkv = kv.shape[1]
+    if kv.shape[0] != M or gamma_q.numel() != Nq or gamma_kv.numel() != Nkv:
+        raise ValueError("shape mismatch")
+    G = Nq // GROUP
+    dev = q.device
+    out_q = torch.empty((M, Nq), dtype=torch.uint8, device=dev) if out_q is None else out_q
+    out_scale = torch.empty(M * G, dtype=torch.uint8, device=dev) if out_scale is None else _u8(out_scale)
+    out_kv = torch.empty((M, Nkv), dtype=torch.bfloat16, device=dev) if out_kv is None else out_kv
+    if out_q.numel() < M * Nq or out_scale.numel() < M * G or out_kv.numel() < M * Nkv:
+        raise ValueError("output buffers too small")
+    status = lib().mi_fused_dual_rmsnorm_group_quant_e8m0(
+        _ptr(q), qs, _ptr(kv), ks, _ptr(gamma_q), _ptr(gamma_kv), ctypes.c_float(eps),
+        M, Nq, Nkv, int(bool(transpose_scale)), _ptr(out_q), _ptr(out_scale), _ptr(out_kv), _stream(q))
+    _check("mi_fused_dual_rmsnorm_group_quant_e8m0", status)
     return out_q, _scale_view(out_scale, M, G, transpose_scale), out_kv
 
 
@@ -280,11 +327,15 @@ def _weight_arg(w):
 
 
 def _check_gemm_operands(a, a_scale, w, w_scale):
-    """Returns (M, N, K, weight data tensor, weight layout)."""
-    for name, t, dt in (("a", a, torch.uint8), ("w_scale", w_scale, torch.float32),
-                        ("a_scale", a_scale, torch.float32)):
-        if t.dtype != dt or t.dim() != 2:
-            raise ValueError(f"{name}: expected a 2-D {dt} tensor")
+    """Returns (M, N, K, weight data tensor, weight layout).  Scales are
+    fp32, or e8m0 exponent bytes (uint8 / float8_e8m0fnu) for both."""
+    e8m0 = a_scale.dtype in E8M0_DTYPES
+    sdt = "e8m0 (uint8)" if e8m0 else torch.float32
+    for name, t, ok in (("a", a, a.dtype == torch.uint8), ("w_scale", w_scale, (w_scale.dtype in E8M0_DTYPES) == e8m0
+                                                              and (e8m0 or w_scale.dtype == torch.float32)),
+                        ("a_scale", a_scale, e8m0 or a_scale.dtype == torch.float32)):
+        if not ok or t.dim() != 2:
+            raise ValueError(f"{name}: expected a 2-D tensor of {'uint8' if name == 'a' else sdt}")
     if not (a.is_contiguous() and w_scale.is_contiguous()):
         raise ValueError("a and w_scale must be contiguous")
     wd, wl, N, Kw = _weight_arg(w)
@@ -315,9 +366,10 @@ def mi_block_scaled_fp8_gemm(a: torch.Tensor, a_scale: torch.Tensor, w, w_scale:
     if a_scale_transposed is not None and M > 1 and bool(a_scale_transposed) != layout:
         raise ValueError("a_scale_transposed disagrees with the strides of a_scale")
     out = _gemm_out(out, M, N, a.device)
-    status = lib().mi_block_scaled_fp8_gemm_ex(
+    fn = "mi_block_scaled_fp8_gemm_e8m0" if a_scale.dtype in E8M0_DTYPES else "mi_block_scaled_fp8_gemm_ex"
+    status = getattr(lib(), fn)(
         _ptr(a), _ptr(a_scale), int(layout), _ptr(wd), wl, _ptr(w_scale), _ptr(out), M, N, K, _stream(a))
-    _check("mi_block_scaled_fp8_gemm_ex", status)
+    _check(fn, status)
     return out
 
 
@@ -335,10 +387,11 @@ def mi_block_scaled_fp8_gemm_pair(a: torch.Tensor, a_scale: torch.Tensor, w1, w1
         raise ValueError("both weights of a pair must have the same layout")
     out1 = _gemm_out(out1, M, N1, a.device)
     out2 = _gemm_out(out2, M, N2, a.device)
-    status = lib().mi_block_scaled_fp8_gemm_pair_ex(
+    fn = "mi_block_scaled_fp8_gemm_pair_e8m0" if a_scale.dtype in E8M0_DTYPES else "mi_block_scaled_fp8_gemm_pair_ex"
+    status = getattr(lib(), fn)(
         _ptr(a), _ptr(a_scale), int(scale_is_transposed(a_scale)), wl1, _ptr(wd1), _ptr(w1_scale), _ptr(out1), N1,
         _ptr(wd2), _ptr(w2_scale), _ptr(out2), N2, M, K, _stream(a))
-    _check("mi_block_scaled_fp8_gemm_pair_ex", status)
+    _check(fn, status)
     return out1, out2
 
 
@@ -406,6 +459,22 @@ def prepare_group_quant_1x128(x, transpose_scale, out_q, out_scale) -> PreparedC
     return PreparedCall("mi_group_quant_1x128", args, (x, out_q, out_scale), x.device)
 
 
+def prepare_fused_dual_rmsnorm_group_quant_e8m0(q, kv, gamma_q, gamma_kv, eps, transpose_scale,
+                                                out_q, out_scale, out_kv) -> PreparedCall:
+    """Marshal the arguments of mi_fused_dual_rmsnorm_group_quant_e8m0 once."""
+    qs = _rows(q, "q", torch.bfloat16)
+    ks = _rows(kv, "kv", torch.bfloat16)
+    M, Nq = q.shape
+    Nkv = kv.shape[1]
+    out_scale = _u8(out_scale)
+    if out_q.numel() < M * Nq or out_scale.numel() < M * (Nq // GROUP) or out_kv.numel() < M * Nkv:
+        raise ValueError("output buffers too small")
+    args = (_ptr(q), qs, _ptr(kv), ks, _ptr(gamma_q), _ptr(gamma_kv), ctypes.c_float(eps),
+            M, Nq, Nkv, int(bool(transpose_scale)), _ptr(out_q), _ptr(out_scale), _ptr(out_kv))
+    return PreparedCall("mi_fused_dual_rmsnorm_group_quant_e8m0", args,
+                        (q, kv, gamma_q, gamma_kv, out_q, out_scale, out_kv), q.device)
+
+
 def prepare_block_scaled_fp8_gemm(a, a_scale, w, w_scale, out) -> PreparedCall:
     """Marshal the arguments of mi_block_scaled_fp8_gemm_ex once; the As
     layout is read from the strides of ``a_scale`` ([M, K/128]), the weight
@@ -415,7 +484,8 @@ def prepare_block_scaled_fp8_gemm(a, a_scale, w, w_scale, out) -> PreparedCall:
         raise ValueError("shape mismatch")
     args = (_ptr(a), _ptr(a_scale), int(scale_is_transposed(a_scale)), _ptr(wd), wl, _ptr(w_scale),
             _ptr(out), M, N, K)
-    return PreparedCall("mi_block_scaled_fp8_gemm_ex", args, (a, a_scale, wd, w_scale, out), a.device)
+    fn = "mi_block_scaled_fp8_gemm_e8m0" if a_scale.dtype in E8M0_DTYPES else "mi_block_scaled_fp8_gemm_ex"
+    return PreparedCall(fn, args, (a, a_scale, wd, w_scale, out), a.device)
 
 
 def prepare_block_scaled_fp8_gemm_pair(a, a_scale, w1, w1_scale, out1, w2, w2_scale, out2) -> PreparedCall:
@@ -428,5 +498,5 @@ def prepare_block_scaled_fp8_gemm_pair(a, a_scale, w1, w1_scale, out1, w2, w2_sc
         raise ValueError("shape mismatch")
     args = (_ptr(a), _ptr(a_scale), int(scale_is_transposed(a_scale)), wl1, _ptr(wd1), _ptr(w1_scale), _ptr(out1),
             N1, _ptr(wd2), _ptr(w2_scale), _ptr(out2), N2, M, K)
-    return PreparedCall("mi_block_scaled_fp8_gemm_pair_ex", args,
-                        (a, a_scale, wd1, w1_scale, out1, wd2, w2_scale, out2), a.device)
+    fn = "mi_block_scaled_fp8_gemm_pair_e8m0" if a_scale.dtype in E8M0_DTYPES else "mi_block_scaled_fp8_gemm_pair_ex"
+    return PreparedCall(fn, args, (a, a_scale, wd1, w1_scale, out1, wd2, w2_scale, out2), a.device)

@@ -10,20 +10,20 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 
 }  // namespace
 
-extern "C" mi_status mi_fused_dual_rmsnorm_group_quant(
-    const uint16_t *q, int64_t q_row_stride,
-    const uint16_t *kv, int64_t kv_row_stride,
-    const uint16_t *gamma_q, const uint16_t *gamma_kv,
-    float eps, int64_t M, int64_t Nq, int64_t Nkv,
-    int transpose_scale,
-    uint8_t *out_q_fp8, float *out_scale, uint16_t *out_kv,
-    hipStream_t stream) {
+namespace {
+
+// e8m0: scales to out_scale_e8m0 (exponent bytes), else to out_scale (fp32)
+mi_status dual_normquant(const uint16_t *q, int64_t q_row_stride, const uint16_t *kv, int64_t kv_row_stride,
+                         const uint16_t *gamma_q, const uint16_t *gamma_kv, float eps, int64_t M, int64_t Nq,
+                         int64_t Nkv, int transpose_scale, uint8_t *out_q_fp8, float *out_scale,
+                         uint8_t *out_scale_e8m0, bool e8m0, uint16_t *out_kv, hipStream_t stream) {
     if (M < 0 || Nq < MI_GROUP || Nq > MI_MAX_NQ || (Nq % MI_GROUP) != 0 || Nkv < 1 ||
         Nkv > MI_MAX_NKV)
         return MI_ERR_SHAPE;
     if (M == 0)
         return MI_OK;
-    if (!q || !kv || !gamma_q || !gamma_kv || !out_q_fp8 || !out_scale || !out_kv)
+    if (!q || !kv || !gamma_q || !gamma_kv || !out_q_fp8 || !(e8m0 ? out_scale_e8m0 != nullptr : out_scale != nullptr) ||
+        !out_kv)
         return MI_ERR_NULL;
     if (q_row_stride < Nq || kv_row_stride < Nkv)
         return MI_ERR_STRIDE;
@@ -45,7 +45,35 @@ extern "C" mi_status mi_fused_dual_rmsnorm_group_quant(
     p.out_q = out_q_fp8;
     p.out_scale = out_scale;
     p.out_kv = out_kv;
-    return mi::launch_normquant(p, stream) == hipSuccess ? MI_OK : MI_ERR_HIP;
+    p.out_scale_e8m0 = out_scale_e8m0;
+    const hipError_t e = e8m0 ? mi::launch_normquant_e8m0(p, stream) : mi::launch_normquant(p, stream);
+    return e == hipSuccess ? MI_OK : MI_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" mi_status mi_fused_dual_rmsnorm_group_quant(
+    const uint16_t *q, int64_t q_row_stride,
+    const uint16_t *kv, int64_t kv_row_stride,
+    const uint16_t *gamma_q, const uint16_t *gamma_kv,
+    float eps, int64_t M, int64_t Nq, int64_t Nkv,
+    int transpose_scale,
+    uint8_t *out_q_fp8, float *out_scale, uint16_t *out_kv,
+    hipStream_t stream) {
+    return dual_normquant(q, q_row_stride, kv, kv_row_stride, gamma_q, gamma_kv, eps, M, Nq, Nkv, transpose_scale,
+                          out_q_fp8, out_scale, nullptr, false, out_kv, stream);
+}
+
+extern "C" mi_status mi_fused_dual_rmsnorm_group_quant_e8m0(
+    const uint16_t *q, int64_t q_row_stride,
+    const uint16_t *kv, int64_t kv_row_stride,
+    const uint16_t *gamma_q, const uint16_t *gamma_kv,
+    float eps, int64_t M, int64_t Nq, int64_t Nkv,
+    int transpose_scale,
+    uint8_t *out_q_fp8, uint8_t *out_scale_e8m0, uint16_t *out_kv,
+    hipStream_t stream) {
+    return dual_normquant(q, q_row_stride, kv, kv_row_stride, gamma_q, gamma_kv, eps, M, Nq, Nkv, transpose_scale,
+                          out_q_fp8, nullptr, out_scale_e8m0, true, out_kv, stream);
 }
 
 namespace {
@@ -186,8 +214,79 @@ extern "C" mi_status mi_block_scaled_fp8_gemm_pair(
                                             w1_scale, out1_bf16, N1, w2_fp8, w2_scale, out2_bf16, N2, M, K, stream);
 }
 
+extern "C" mi_status mi_block_scaled_fp8_gemm_e8m0(
+    const uint8_t *a_fp8, const uint8_t *a_scale_e8m0, int a_scale_transposed,
+    const uint8_t *w_fp8, int w_layout, const uint8_t *w_scale_e8m0,
+    uint16_t *out_bf16,
+    int64_t M, int64_t N, int64_t K,
+    hipStream_t stream) {
+    if (w_layout != MI_WEIGHT_ROW_MAJOR && w_layout != MI_WEIGHT_TILED)
+        return MI_ERR_LAYOUT;
+    if (M < 0 || N <= 0 || K <= 0 || (N % MI_GROUP) != 0 || (K % MI_GROUP) != 0)
+        return MI_ERR_SHAPE;
+    if (M == 0)
+        return MI_OK;
+    if (!a_fp8 || !a_scale_e8m0 || !w_fp8 || !w_scale_e8m0 || !out_bf16)
+        return MI_ERR_NULL;
+    if (!aligned16(a_fp8) || !aligned16(w_fp8) || !aligned16(out_bf16) ||
+        (reinterpret_cast<uintptr_t>(a_scale_e8m0) & 3) || (reinterpret_cast<uintptr_t>(w_scale_e8m0) & 3))
+        return MI_ERR_ALIGN;
+    mi::GemmParams p = {};
+    p.a = a_fp8;
+    p.a_scale_transposed = a_scale_transposed ? 1 : 0;
+    p.w = w_fp8;
+    p.out = out_bf16;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.w_tiled = w_layout == MI_WEIGHT_TILED ? 1 : 0;
+    p.scale_e8m0 = 1;
+    p.a_scale8 = a_scale_e8m0;
+    p.w_scale8 = w_scale_e8m0;
+    return mi::launch_block_scaled_gemm(p, stream) == hipSuccess ? MI_OK : MI_ERR_HIP;
+}
+
+extern "C" mi_status mi_block_scaled_fp8_gemm_pair_e8m0(
+    const uint8_t *a_fp8, const uint8_t *a_scale_e8m0, int a_scale_transposed, int w_layout,
+    const uint8_t *w1_fp8, const uint8_t *w1_scale_e8m0, uint16_t *out1_bf16, int64_t N1,
+    const uint8_t *w2_fp8, const uint8_t *w2_scale_e8m0, uint16_t *out2_bf16, int64_t N2,
+    int64_t M, int64_t K,
+    hipStream_t stream) {
+    if (w_layout != MI_WEIGHT_ROW_MAJOR && w_layout != MI_WEIGHT_TILED)
+        return MI_ERR_LAYOUT;
+    if (M < 0 || N1 <= 0 || N2 <= 0 || K <= 0 || (N1 % MI_GROUP) != 0 || (N2 % MI_GROUP) != 0 ||
+        (K % MI_GROUP) != 0)
+        return MI_ERR_SHAPE;
+    if (M == 0)
+        return MI_OK;
+    if (!a_fp8 || !a_scale_e8m0 || !w1_fp8 || !w1_scale_e8m0 || !out1_bf16 || !w2_fp8 || !w2_scale_e8m0 ||
+        !out2_bf16)
+        return MI_ERR_NULL;
+    if (!aligned16(a_fp8) || !aligned16(w1_fp8) || !aligned16(out1_bf16) || !aligned16(w2_fp8) ||
+        !aligned16(out2_bf16) || (reinterpret_cast<uintptr_t>(a_scale_e8m0) & 3) ||
+        (reinterpret_cast<uintptr_t>(w1_scale_e8m0) & 3) || (reinterpret_cast<uintptr_t>(w2_scale_e8m0) & 3))
+        return MI_ERR_ALIGN;
+    mi::GemmParams p = {};
+    p.a = a_fp8;
+    p.a_scale_transposed = a_scale_transposed ? 1 : 0;
+    p.w = w1_fp8;
+    p.out = out1_bf16;
+    p.M = M;
+    p.N = N1;
+    p.K = K;
+    p.w2 = w2_fp8;
+    p.out2 = out2_bf16;
+    p.N2 = N2;
+    p.w_tiled = w_layout == MI_WEIGHT_TILED ? 1 : 0;
+    p.scale_e8m0 = 1;
+    p.a_scale8 = a_scale_e8m0;
+    p.w_scale8 = w1_scale_e8m0;
+    p.w_scale8_2 = w2_scale_e8m0;
+    return mi::launch_block_scaled_gemm_pair(p, stream) == hipSuccess ? MI_OK : MI_ERR_HIP;
+}
+
 extern "C" unsigned mi_gemm_capabilities(void) {
-    return MI_CAP_AS_ROW_MAJOR | MI_CAP_AS_COL_MAJOR | MI_CAP_WEIGHT_TILED;
+    return MI_CAP_AS_ROW_MAJOR | MI_CAP_AS_COL_MAJOR | MI_CAP_WEIGHT_TILED | MI_CAP_SCALE_E8M0;
 }
 
 extern "C" int mi_preferred_weight_layout(int64_t N, int64_t K) {

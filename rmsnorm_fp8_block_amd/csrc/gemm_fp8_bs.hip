@@ -87,6 +87,22 @@ __device__ __forceinline__ v8i load_weight_frag(const uint8_t *p, bool swap) {
     return swap ? join(b, a) : join(a, b);
 }
 
+// e8m0 exponent byte -> its value 2^(e - 127) as fp32 (exact; e = 0 is the
+// subnormal 2^-127, e = 255 NaN)
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+    return e == 0 ? __uint_as_float(0x00400000u) : e == 255 ? __uint_as_float(0x7FC00000u) : __uint_as_float(e << 23);
+}
+
+// Block-scaled MFMA with e8m0 scales: acc + sum_k (2^(sa-127) a_k) (2^(sb-127) b_k)
+// over one 128-deep K-block, sa / sb in the low byte of each lane's scale
+// word (A: the weight, one scale per 16-row subtile and K-block; B: the
+// activation, one per row and K-block).
+__device__ __forceinline__ v4f mfma_e4m3_16x16x128_scaled(const v8i &a, const v8i &b, const v4f &acc, uint32_t sa,
+                                                          uint32_t sb) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 0, static_cast<int>(sa), 0,
+                                                           static_cast<int>(sb));
+}
+
 __device__ __forceinline__ v4f mfma_e4m3_16x16x128(const v8i &a, const v8i &b) {
     const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
     // format 0 = e4m3 for both operands; zero scale operands select the
@@ -113,6 +129,7 @@ __global__ __launch_bounds__(256) void block_scaled_fp8_gemm_kernel(GemmParams p
     const WeightFrag wfrag = weight_frag(lane, K, p.w_tiled);
     const uint8_t *wrow = p.w + n0 * K + wfrag.lane_off;
     const float *bs_row = p.w_scale + (n0 / kBlk) * KB;
+    const uint8_t *bs8_row = p.w_scale8 + (n0 / kBlk) * KB;
 
     v4f acc[kMT];
 #pragma unroll
@@ -149,9 +166,10 @@ __global__ __launch_bounds__(256) void block_scaled_fp8_gemm_kernel(GemmParams p
             const int r = i % (kMT * 16), kb = i / (kMT * 16);
             const int64_t m = m0 + r;
             float s = 0.0f;
-            if (m < M)
-                s = p.a_scale_transposed ? p.a_scale[static_cast<int64_t>(kb0 + kb) * M + m]
-                                         : p.a_scale[m * KB + kb0 + kb];
+            if (m < M) {
+                const int64_t at = p.a_scale_transposed ? static_cast<int64_t>(kb0 + kb) * M + m : m * KB + kb0 + kb;
+                s = p.scale_e8m0 ? e8m0_to_f32(p.a_scale8[at]) : p.a_scale[at];
+            }
             s_as[kb][r] = s;
         }
         __syncthreads();
@@ -160,7 +178,7 @@ __global__ __launch_bounds__(256) void block_scaled_fp8_gemm_kernel(GemmParams p
         for (int j = 0; j < kStageKb; ++j) {
             if (j >= kc)
                 break;
-            const float bs = bs_row[kb0 + j];
+            const float bs = p.scale_e8m0 ? e8m0_to_f32(bs8_row[kb0 + j]) : bs_row[kb0 + j];
 #pragma unroll
             for (int t = 0; t < kMT; ++t) {
                 const uint4 lo = s_act[((j * kMT + t) * 2 + 0) * kWave + lane];
@@ -230,6 +248,7 @@ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 struct SubTile {
     const uint8_t *w;   // first weight row of the subtile
     const float *ws;    // its row of 128x128 block scales
+    const uint8_t *ws8;  // the same row of e8m0 block scales
     uint16_t *out;      // output of its consumer
     int64_t n0;         // its first output column
     int64_t ldo;        // row stride of that output
@@ -238,12 +257,15 @@ struct SubTile {
 __device__ __forceinline__ SubTile subtile(const GemmParams &p, int64_t st) {
     const int64_t S1 = p.N / 16, KB = p.K / kBlk;
     if (st < S1)
-        return {p.w + st * 16 * p.K, p.w_scale + (st * 16 / kBlk) * KB, p.out, st * 16, p.N};
+        return {p.w + st * 16 * p.K, p.w_scale + (st * 16 / kBlk) * KB, p.w_scale8 + (st * 16 / kBlk) * KB, p.out,
+                st * 16, p.N};
     const int64_t l = st - S1;
-    return {p.w2 + l * 16 * p.K, p.w_scale2 + (l * 16 / kBlk) * KB, p.out2, l * 16, p.N2};
+    return {p.w2 + l * 16 * p.K, p.w_scale2 + (l * 16 / kBlk) * KB, p.w_scale8_2 + (l * 16 / kBlk) * KB, p.out2,
+            l * 16, p.N2};
 }
 
-template <int kKB, int kNS, int kMT, int kWaves>
+// kE8m0: e8m0 scales, applied by the matrix core (no scale stages in LDS).
+template <int kKB, int kNS, int kMT, int kWaves, bool kE8m0 = false>
 struct WidePlan {
     static_assert(kNS % 2 == 0 && kNS >= 2 && kNS <= (kMT == 1 ? 8 : 6),
                   "whole 2-slot subtiles; two fragment sets fit the registers");
@@ -252,7 +274,7 @@ struct WidePlan {
     static constexpr int kSlot = 1024;                         // 8 rows x 128 bytes
     static constexpr int kWStage = kNS * 2 * kSlot;            // weight bytes per K-block
     static constexpr int kAStage = kWaves * kMT * 2 * kSlot;   // activation bytes per K-block
-    static constexpr int kSStage = kWaves * 2 * kWave * 4;     // per wave: As (one per lane), Bs
+    static constexpr int kSStage = kE8m0 ? 0 : kWaves * 2 * kWave * 4;  // per wave: As (one per lane), Bs
     static constexpr int kRA = cmin(kKB, 3);                   // activation stages
     // weight stages: as many as the rest of the 160 KB allows, up to 6
     static constexpr int kRW = cmin(kKB, cmin(6, (160 * 1024 - kRA * (kAStage + kSStage)) / kWStage));
@@ -260,7 +282,7 @@ struct WidePlan {
     // the extra loads repeat a slot of the same row half (same bytes to the
     // same place: harmless, and every wave then counts the same loads)
     static constexpr int kNW = (2 * kNS + kWaves - 1) / kWaves;
-    static constexpr int kNA = 2 * kMT + 2;                    // activation, As and Bs loads
+    static constexpr int kNA = 2 * kMT + (kE8m0 ? 0 : 2);      // activation, As and Bs loads
     static constexpr int kWOff = 0;
     static constexpr int kAOff = kWOff + kRW * kWStage;
     static constexpr int kSOff = kAOff + kRA * kAStage;
@@ -312,9 +334,9 @@ __device__ __forceinline__ v8i join4(const v4u32 &lo, const v4u32 &hi) {
 // MFMA -> FMA pipeline.  Member functions instead of lambdas: the host pass
 // of the compiler drops a kernel's launch stub when the kernel calls a
 // lambda that issues direct global -> LDS loads.
-template <int kKB, int kNS, int kMT, int kWaves>
+template <int kKB, int kNS, int kMT, int kWaves, bool kE8m0>
 struct WideWave {
-    using P = WidePlan<kKB, kNS, kMT, kWaves>;
+    using P = WidePlan<kKB, kNS, kMT, kWaves, kE8m0>;
     static constexpr int kLag = 2;                // FMAs of MFMA n are issued after MFMA n + kLag
     static constexpr int kRing = kLag + 2;        // partial results in flight
     static constexpr int kSeq = kKB * kNS * kMT;  // MFMAs per wave
@@ -336,6 +358,10 @@ struct WideWave {
     v4f acc[kMT][kNS];
     v4f part[kRing];   // MFMA n -> part[n % kRing]
     float scl[kRing];  // its As * Bs
+    // e8m0: scale bytes of every K-block, 4 per word (loaded once):
+    // asw: this lane's activation row of m-tile j; bsw: subtile t (uniform)
+    uint32_t asw[kMT][(kKB + 3) / 4];
+    uint32_t bsw[kNS][(kKB + 3) / 4];
 
     __device__ __forceinline__ void issue_w(int s) {
         uint8_t *dst = lds + P::kWOff + (s % P::kRW) * P::kWStage;
@@ -352,10 +378,12 @@ struct WideWave {
             __builtin_amdgcn_global_load_lds(src + a_off[j][0], dst + (2 * j) * P::kSlot, 16, 0, 0);
             __builtin_amdgcn_global_load_lds(src + a_off[j][1], dst + (2 * j + 1) * P::kSlot, 16, 0, 0);
         }
-        uint8_t *sdst = lds + P::kSOff + (s % P::kRA) * P::kSStage + wave * 2 * kWave * 4;
-        const uint8_t *ssrc = reinterpret_cast<const uint8_t *>(a_scale + s * s_stride);
-        __builtin_amdgcn_global_load_lds(ssrc + s_off, sdst, 4, 0, 0);
-        __builtin_amdgcn_global_load_lds(bsrc + s, sdst + kWave * 4, 4, 0, 0);
+        if constexpr (!kE8m0) {
+            uint8_t *sdst = lds + P::kSOff + (s % P::kRA) * P::kSStage + wave * 2 * kWave * 4;
+            const uint8_t *ssrc = reinterpret_cast<const uint8_t *>(a_scale + s * s_stride);
+            __builtin_amdgcn_global_load_lds(ssrc + s_off, sdst, 4, 0, 0);
+            __builtin_amdgcn_global_load_lds(bsrc + s, sdst + kWave * 4, 4, 0, 0);
+        }
     }
 
     // The wait counts assume exactly this issue order (activations, then
@@ -410,13 +438,15 @@ struct WideWave {
         for (int j = 0; j < kMT; ++j) {
             af[b][j] = join4(*reinterpret_cast<const v4u32 *>(as + (2 * j) * P::kSlot + frag_lo),
                              *reinterpret_cast<const v4u32 *>(as + (2 * j) * P::kSlot + frag_hi));
-            asv[b][j] = ss[16 * j + (lane & 15)];
+            if constexpr (!kE8m0)
+                asv[b][j] = ss[16 * j + (lane & 15)];
         }
 #pragma unroll
         for (int t = 0; t < kNS; ++t) {
             wfs[b][t] = join4(*reinterpret_cast<const v4u32 *>(ws + (2 * t) * P::kSlot + frag_lo),
                               *reinterpret_cast<const v4u32 *>(ws + (2 * t) * P::kSlot + frag_hi));
-            bss[b][t] = ss[kWave + t];  // same address in every lane: broadcast read
+            if constexpr (!kE8m0)
+                bss[b][t] = ss[kWave + t];  // same address in every lane: broadcast read
         }
     }
 
@@ -434,6 +464,16 @@ struct WideWave {
             read_frags<kb + 1>();
         }
         constexpr int b = kb & 1;
+        if constexpr (kE8m0) {
+            // the scales ride on the MFMA: accumulate the whole K in place
+            constexpr int wd = kb / 4, sh = 8 * (kb % 4);
+#pragma unroll
+            for (int t = 0; t < kNS; ++t)
+#pragma unroll
+                for (int j = 0; j < kMT; ++j)
+                    acc[j][t] = mfma_e4m3_16x16x128_scaled(wfs[b][t], af[b][j], acc[j][t], (bsw[t][wd] >> sh) & 0xFFu,
+                                                           (asw[j][wd] >> sh) & 0xFFu);
+        } else {
 #pragma unroll
         for (int t = 0; t < kNS; ++t) {
 #pragma unroll
@@ -450,14 +490,15 @@ struct WideWave {
                 }
             }
         }
+        }
         if constexpr (kb + 1 < kKB)
             kblock<kb + 1>();
     }
 };
 
-template <int kKB, int kNS, int kMT, int kWaves>
+template <int kKB, int kNS, int kMT, int kWaves, bool kE8m0>
 __global__ __launch_bounds__(kWaves * kWave) void block_scaled_fp8_gemm_wide_kernel(GemmParams p) {
-    using W = WideWave<kKB, kNS, kMT, kWaves>;
+    using W = WideWave<kKB, kNS, kMT, kWaves, kE8m0>;
     extern __shared__ uint4 s_dyn[];
     W w;
     w.lds = reinterpret_cast<uint8_t *>(s_dyn);
@@ -525,6 +566,36 @@ __global__ __launch_bounds__(kWaves * kWave) void block_scaled_fp8_gemm_wide_ker
     // repeat the last subtile)
     w.bsrc = subtile(p, min<int64_t>(st0 + min(lane, kNS - 1), S - 1)).ws;
 
+    if constexpr (kE8m0) {
+        // every K-block's scale bytes into registers, before the rings start
+        // (these loads are older than every ring load, so each ring wait
+        // also covers them)
+        constexpr int kWords = (kKB + 3) / 4;
+#pragma unroll
+        for (int j = 0; j < kMT; ++j) {
+            const int64_t r = min<int64_t>(m_base + 16 * j + (lane & 15), M - 1);
+#pragma unroll
+            for (int i = 0; i < kWords; ++i) {
+                if (p.a_scale_transposed) {
+                    uint32_t v = 0;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        v |= static_cast<uint32_t>(p.a_scale8[static_cast<int64_t>(4 * i + q) * M + r]) << (8 * q);
+                    w.asw[j][i] = v;
+                } else {
+                    w.asw[j][i] = reinterpret_cast<const uint32_t *>(p.a_scale8 + r * kKB)[i];
+                }
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < kNS; ++t) {
+            const uint32_t *src =
+                reinterpret_cast<const uint32_t *>(subtile(p, min<int64_t>(st0 + t, S - 1)).ws8);
+#pragma unroll
+            for (int i = 0; i < kWords; ++i)
+                w.bsw[t][i] = src[i];
+        }
+    }
     w.prologue();
 #pragma unroll
     for (int j = 0; j < kMT; ++j)
@@ -534,9 +605,11 @@ __global__ __launch_bounds__(kWaves * kWave) void block_scaled_fp8_gemm_wide_ker
     w.template arrive<0>();
     w.template read_frags<0>();
     w.template kblock<0>();
+    if constexpr (!kE8m0) {
 #pragma unroll
-    for (int n = W::kSeq - W::kLag; n < W::kSeq; ++n)
-        w.fold(n);
+        for (int n = W::kSeq - W::kLag; n < W::kSeq; ++n)
+            w.fold(n);
+    }
 
     // Output: lane holds out[m_base + 16j + L%16][16 (st0 + t) + 4 (L/16) + i].
     // The wave's tile (16 kMT rows x 16 kNS columns, bf16) goes through LDS
@@ -807,20 +880,27 @@ hipError_t launch_decode_kb(const GemmParams &p, hipStream_t stream) {
     return launch_decode<4, kKB>(p, stream);
 }
 
-template <int kKB, int kNS, int kMT, int kWaves>
-hipError_t launch_wide(const GemmParams &p, hipStream_t stream) {
-    using P = WidePlan<kKB, kNS, kMT, kWaves>;
+template <int kKB, int kNS, int kMT, int kWaves, bool kE8m0>
+hipError_t launch_wide_scaled(const GemmParams &p, hipStream_t stream) {
+    using P = WidePlan<kKB, kNS, kMT, kWaves, kE8m0>;
     const int64_t nm = (p.M + kWaves * 16 * kMT - 1) / (kWaves * 16 * kMT);
     const int64_t blocks = ((p.N + p.N2) / 16 + kNS - 1) / kNS * nm;
     if (blocks > 0x7FFFFFFF || p.M > 256)
         return hipErrorInvalidValue;
-    auto kern = block_scaled_fp8_gemm_wide_kernel<kKB, kNS, kMT, kWaves>;
+    auto kern = block_scaled_fp8_gemm_wide_kernel<kKB, kNS, kMT, kWaves, kE8m0>;
     static std::atomic<uint64_t> lds_set{0};
     const hipError_t e = allow_dynamic_lds(kern, P::kLds, lds_set);
     if (e != hipSuccess)
         return e;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kWaves * kWave), P::kLds, stream, p);
     return hipGetLastError();
+}
+
+template <int kKB, int kNS, int kMT, int kWaves>
+hipError_t launch_wide(const GemmParams &p, hipStream_t stream) {
+    if (p.scale_e8m0)
+        return launch_wide_scaled<kKB, kNS, kMT, kWaves, true>(p, stream);
+    return launch_wide_scaled<kKB, kNS, kMT, kWaves, false>(p, stream);
 }
 
 template <int kKB, int kMT>
@@ -883,7 +963,8 @@ hipError_t launch_mt(const GemmParams &p, hipStream_t stream) {
 hipError_t launch_block_scaled_gemm(const GemmParams &p, hipStream_t stream) {
     // Small decode batches over wide weights (more than 4 subtiles per CU):
     // weight ring per wave, activations resident in LDS.
-    if (p.M <= kDecodeMaxRows && p.N / 16 > 4 * static_cast<int64_t>(device_cu_count())) {
+    // (e8m0 scales: the wide kernel, whose matrix cores apply them)
+    if (!p.scale_e8m0 && p.M <= kDecodeMaxRows && p.N / 16 > 4 * static_cast<int64_t>(device_cu_count())) {
         switch (p.K / kBlk) {
         case 4:
             return launch_decode_kb<4>(p, stream);
@@ -980,14 +1061,17 @@ hipError_t launch_block_scaled_gemm_pair(const GemmParams &p, hipStream_t stream
     GemmParams a = p, b = p;
     a.w2 = nullptr;
     a.w_scale2 = nullptr;
+    a.w_scale8_2 = nullptr;
     a.out2 = nullptr;
     a.N2 = 0;
     b.w = p.w2;
     b.w_scale = p.w_scale2;
+    b.w_scale8 = p.w_scale8_2;
     b.out = p.out2;
     b.N = p.N2;
     b.w2 = nullptr;
     b.w_scale2 = nullptr;
+    b.w_scale8_2 = nullptr;
     b.out2 = nullptr;
     b.N2 = 0;
     const hipError_t e = launch_block_scaled_gemm(a, stream);

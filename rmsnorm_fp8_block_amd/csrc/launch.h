@@ -25,6 +25,9 @@ struct NormQuantParams {
     uint8_t *out_q;
     float *out_scale;
     uint16_t *out_kv;
+    // e8m0 mode: power-of-two scales, one exponent byte each, written here
+    // (out_scale unused)
+    uint8_t *out_scale_e8m0 = nullptr;
 };
 
 struct GemmParams {
@@ -44,11 +47,20 @@ struct GemmParams {
     uint16_t *out2 = nullptr;
     int64_t N2 = 0;
     // weight byte order of w (and w2): 0 row-major, 1 tiled (see
-    // mi_relayout_weight_tiled)
+    // mi_relayout_weight)
     int w_tiled = 0;
+    // e8m0 scales: a_scale8 / w_scale8 / w_scale8_2 hold exponent bytes (value
+    // 2^(e - 127)) in the layouts of a_scale / w_scale / w_scale2, which are
+    // then unused
+    int scale_e8m0 = 0;
+    const uint8_t *a_scale8 = nullptr;
+    const uint8_t *w_scale8 = nullptr;
+    const uint8_t *w_scale8_2 = nullptr;
 };
 
 hipError_t launch_normquant(const NormQuantParams &p, hipStream_t stream);
+// the same with e8m0 scales (p.out_scale_e8m0)
+hipError_t launch_normquant_e8m0(const NormQuantParams &p, hipStream_t stream);
 // weight [N, K] row-major <-> tiled (to_tiled selects the direction)
 hipError_t launch_weight_relayout(const uint8_t *src, uint8_t *dst, int64_t N, int64_t K, bool to_tiled,
                                   hipStream_t stream);

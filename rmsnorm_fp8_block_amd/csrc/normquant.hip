@@ -43,6 +43,7 @@ constexpr int kGroup = 128;
 constexpr float kE4m3Max = 448.0f;
 constexpr float kInvE4m3Max = 1.0f / 448.0f;  // rounded to fp32
 constexpr float kScaleFloor = 1e-12f;
+constexpr int kE8m0MinExponent = -39;  // ceil(log2(1e-12)): the floor as a power of two
 
 // 8 consecutive bf16 at p[col, col+8); elements at or beyond n read as zero.
 // kVec: p + col is 16-byte aligned whenever col + 8 <= n.  kFull: the caller
@@ -145,8 +146,10 @@ __device__ __forceinline__ float div_round_to_odd(float x, float s, float inv) {
 
 // Chunk c (512 elements, 4 groups) of row m: group amax, scale, e4m3fn codes.
 // x: this lane's 8 elements; g: their gamma (unused without the norm);
-// rq: the row's rstd (1 without the norm).
-template <bool kVec, bool kFull, bool kNorm>
+// rq: the row's rstd (1 without the norm).  kE8m0: the scale is rounded up
+// to a power of two 2^e (the smallest not below the fp32 scale), stored as
+// the exponent byte e + 127, and the codes are z * (rq * 2^-e).
+template <bool kVec, bool kFull, bool kNorm, bool kE8m0 = false>
 __device__ __forceinline__ void quant_chunk(const NormQuantParams &a, int64_t m, int lane, int c,
                                             const uint4 &x, const GammaSlice &g, float rq) {
     const int G = a.Nq / kGroup;
@@ -165,14 +168,27 @@ __device__ __forceinline__ void quant_chunk(const NormQuantParams &a, int64_t m,
     amax = row16_max(amax);
     // without the norm, amax is an exact bf16 value and one correctly
     // rounded division gives the scale bit for bit (once per group)
-    const float s = kNorm ? fmaxf((amax * rq) * kInvE4m3Max, kScaleFloor)
-                          : fmaxf(amax / kE4m3Max, kScaleFloor);
-    const float inv = rq * __builtin_amdgcn_rcpf(s);
+    float s = kNorm ? fmaxf((amax * rq) * kInvE4m3Max, kScaleFloor)
+                    : fmaxf(amax / kE4m3Max, kScaleFloor);
+    int e = 0;
+    if constexpr (kE8m0) {
+        // e = ceil(log2(v / 448)), v = amax * rq, read off v's bits exactly
+        // (no rounded 1/448): with v = 1.f * 2^E and 448 = 1.75 * 2^8, v / 448
+        // lies in (2^(E-9), 2^(E-8)] when 1.f <= 1.75, else in (2^(E-8),
+        // 2^(E-7)); then the floor 2^ceil(log2(1e-12)) = 2^-39 (also taking
+        // zero and subnormal v)
+        const uint32_t vb = __float_as_uint(amax * rq);
+        e = static_cast<int>((vb >> 23) & 0xFFu) - 127 - 8 + ((vb & 0x7FFFFFu) > 0x600000u);
+        e = e < kE8m0MinExponent ? kE8m0MinExponent : e;
+        s = __uint_as_float(static_cast<uint32_t>(e + 127) << 23);
+    }
+    const float inv = kE8m0 ? rq * __uint_as_float(static_cast<uint32_t>(127 - e) << 23)
+                            : rq * __builtin_amdgcn_rcpf(s);
     float r[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-        r[j] = __builtin_amdgcn_fmed3f(kNorm ? z[j] * inv : div_round_to_odd(z[j], s, inv), -kE4m3Max,
-                                       kE4m3Max);
+        r[j] = __builtin_amdgcn_fmed3f(kNorm || kE8m0 ? z[j] * inv : div_round_to_odd(z[j], s, inv),
+                                       -kE4m3Max, kE4m3Max);
     const uint32_t lo = pack4_e4m3(r[0], r[1], r[2], r[3]);
     const uint32_t hi = pack4_e4m3(r[4], r[5], r[6], r[7]);
     if (kFull || col < a.Nq) {  // Nq % 128 == 0: a lane's 8 codes are all in range
@@ -191,7 +207,10 @@ __device__ __forceinline__ void quant_chunk(const NormQuantParams &a, int64_t m,
     if ((lane & 15) == 0 && (kFull || grp < G)) {
         const int64_t at = a.transpose_scale ? static_cast<int64_t>(grp) * a.M + m
                                              : m * G + grp;
-        a.out_scale[at] = s;
+        if constexpr (kE8m0)
+            a.out_scale_e8m0[at] = static_cast<uint8_t>(e + 127);
+        else
+            a.out_scale[at] = s;
     }
 }
 
@@ -202,7 +221,7 @@ __device__ __forceinline__ void quant_chunk(const NormQuantParams &a, int64_t m,
 // once per element.  kNorm == false: the per-1x128 quantisation of x itself
 // (z = x, r = 1, no gamma); there x and s are exact, and scales and codes
 // are the correctly rounded ones.  kKv == 0: no second input.
-template <int kQ, int kKv, bool kVec, bool kFull, bool kNorm>
+template <int kQ, int kKv, bool kVec, bool kFull, bool kNorm, bool kE8m0>
 __device__ __forceinline__ void process_row(const NormQuantParams &a, int64_t m, int lane,
                                             const uint4 (&xq)[kQ], const uint4 (&xk)[kKv > 0 ? kKv : 1],
                                             const GammaSlice (&gq)[kQ], const GammaSlice (&gk)[kKv > 0 ? kKv : 1]) {
@@ -255,7 +274,7 @@ __device__ __forceinline__ void process_row(const NormQuantParams &a, int64_t m,
     for (int c = 0; c < kQ; ++c) {
         if (!kFull && c * kChunk >= a.Nq)
             break;  // uniform across the wave
-        quant_chunk<kVec, kFull, kNorm>(a, m, lane, c, xq[c], gq[c], rq);
+        quant_chunk<kVec, kFull, kNorm, kE8m0>(a, m, lane, c, xq[c], gq[c], rq);
     }
 }
 
@@ -264,7 +283,7 @@ __device__ __forceinline__ void process_row(const NormQuantParams &a, int64_t m,
 // output row is 16-byte aligned and Nkv % 8 == 0.  kRows: consecutive rows
 // per wave; all their loads are issued together, gammas once per wave.
 // kFull: Nq == 512 * kQ and Nkv == 512 * kKv (no bounds tests).
-template <int kQ, int kKv, bool kVec, int kRows, bool kFull, bool kNorm>
+template <int kQ, int kKv, bool kVec, int kRows, bool kFull, bool kNorm, bool kE8m0>
 __global__ __launch_bounds__(256) void fused_dual_rmsnorm_group_quant_kernel(NormQuantParams a) {
     constexpr int kKvA = kKv > 0 ? kKv : 1;  // array extents
     const int lane = threadIdx.x & (kWave - 1);
@@ -318,7 +337,7 @@ __global__ __launch_bounds__(256) void fused_dual_rmsnorm_group_quant_kernel(Nor
         const int64_t m = row0 + r;
         if (m >= a.M)
             break;
-        process_row<kQ, kKv, kVec, kFull, kNorm>(a, m, lane, xq[r], xk[r], gq, gk);
+        process_row<kQ, kKv, kVec, kFull, kNorm, kE8m0>(a, m, lane, xq[r], xk[r], gq, gk);
     }
 }
 
@@ -384,14 +403,14 @@ __global__ __launch_bounds__(256) void split_row_group_quant_kernel(NormQuantPar
     }
 }
 
-template <int kQ, int kKv, bool kVec, int kRows, bool kFull = false, bool kNorm = true>
+template <int kQ, int kKv, bool kVec, int kRows, bool kFull = false, bool kNorm = true, bool kE8m0 = false>
 hipError_t launch_variant(const NormQuantParams &p, hipStream_t stream) {
     const int64_t waves = (p.M + kRows - 1) / kRows;
     const int waves_per_block = waves >= 4 ? 4 : static_cast<int>(waves);
     const int64_t blocks = (waves + waves_per_block - 1) / waves_per_block;
     if (blocks > 0x7FFFFFFF)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((fused_dual_rmsnorm_group_quant_kernel<kQ, kKv, kVec, kRows, kFull, kNorm>),
+    hipLaunchKernelGGL((fused_dual_rmsnorm_group_quant_kernel<kQ, kKv, kVec, kRows, kFull, kNorm, kE8m0>),
                        dim3(static_cast<unsigned>(blocks)), dim3(waves_per_block * kWave), 0, stream, p);
     return hipGetLastError();
 }
@@ -409,7 +428,10 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 
 }  // namespace
 
-hipError_t launch_normquant(const NormQuantParams &p, hipStream_t stream) {
+namespace {
+
+template <bool kE8m0>
+hipError_t launch_dual(const NormQuantParams &p, hipStream_t stream) {
     // The vector path needs every 8-element lane slice to be 16-byte aligned.
     // out_q rows are Nq bytes (a multiple of 128) and need 8-byte stores.
     const bool vec = aligned16(p.q) && aligned16(p.kv) && aligned16(p.gamma_q) &&
@@ -418,10 +440,19 @@ hipError_t launch_normquant(const NormQuantParams &p, hipStream_t stream) {
     const int qch = (p.Nq + kChunk - 1) / kChunk;
     const int kch = (p.Nkv + kChunk - 1) / kChunk;
     if (vec && p.Nq == 3 * kChunk && p.Nkv == kChunk)  // the MLA latent shape: 1536 + 512
-        return launch_variant<3, 1, true, 1, true>(p, stream);
+        return launch_variant<3, 1, true, 1, true, true, kE8m0>(p, stream);
     if (qch <= 8 && kch <= 4)
-        return vec ? launch_variant<8, 4, true, 1>(p, stream) : launch_variant<8, 4, false, 1>(p, stream);
+        return vec ? launch_variant<8, 4, true, 1, false, true, kE8m0>(p, stream)
+                   : launch_variant<8, 4, false, 1, false, true, kE8m0>(p, stream);
     return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_normquant(const NormQuantParams &p, hipStream_t stream) { return launch_dual<false>(p, stream); }
+
+hipError_t launch_normquant_e8m0(const NormQuantParams &p, hipStream_t stream) {
+    return launch_dual<true>(p, stream);
 }
 
 // Below this many rows, one wave per row leaves CUs idle for wide rows.

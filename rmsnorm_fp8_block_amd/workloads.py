@@ -175,3 +175,32 @@ def block_fp8_weight(N: int, K: int, seed: int, std: float = 0.02) -> BlockFp8We
     codes = (blocks / scale[:, None, :, None]).clamp(-448.0, 448.0)
     codes = codes.reshape(N, K).to(torch.float8_e4m3fn).view(torch.uint8)
     return BlockFp8Weight(codes.numpy().copy(), scale.numpy().copy())
+
+
+@dataclass
+class BlockFp8WeightE8m0:
+    """A weight [N, K] as e4m3fn codes plus e8m0 block scales [N/128, K/128]
+    (exponent bytes; dequantised value = dec(code) * 2^(byte - 127))."""
+    codes: np.ndarray   # uint8 [N, K]
+    scale: np.ndarray   # uint8 [N/128, K/128]
+
+    @property
+    def shape(self):
+        return self.codes.shape
+
+
+def block_fp8_weight_e8m0(N: int, K: int, seed: int, std: float = 0.02) -> BlockFp8WeightE8m0:
+    """Checkpoint-style fp8 weight with power-of-two block scales: the same
+    N(0, std) draw as block_fp8_weight, each 128x128 block scaled by 2^e, the
+    smallest power of two not below block amax / 448 (floored at 1e-12),
+    codes = torch's float8_e4m3fn cast of W * 2^-e (exact power-of-two
+    scaling, |.| <= 448)."""
+    assert N % GROUP == 0 and K % GROUP == 0
+    w = torch.from_numpy(rng(seed).standard_normal((N, K), dtype=np.float32)) * std
+    blocks = w.view(N // GROUP, GROUP, K // GROUP, GROUP).double()
+    t = torch.clamp(blocks.abs().amax(dim=(1, 3)) / 448.0, min=float(np.float32(1e-12)))
+    m, ex = torch.frexp(t)                      # t = m * 2^ex, m in [0.5, 1)
+    e = torch.where(m == 0.5, ex - 1, ex)
+    codes = torch.ldexp(blocks, -e[:, None, :, None].double()).clamp(-448.0, 448.0).float()
+    codes = codes.reshape(N, K).to(torch.float8_e4m3fn).view(torch.uint8)
+    return BlockFp8WeightE8m0(codes.numpy().copy(), (e + 127).to(torch.uint8).numpy().copy())

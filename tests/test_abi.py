@@ -190,7 +190,7 @@ def test_gemm_ex_layout_validation(L):
 
 def test_capabilities_and_preferred_layout(L):
     caps = mi.mi_gemm_capabilities()
-    assert caps == B.MI_CAP_AS_ROW_MAJOR | B.MI_CAP_AS_COL_MAJOR | B.MI_CAP_WEIGHT_TILED
+    assert caps == B.MI_CAP_AS_ROW_MAJOR | B.MI_CAP_AS_COL_MAJOR | B.MI_CAP_WEIGHT_TILED | B.MI_CAP_SCALE_E8M0
     assert mi.mi_preferred_weight_layout(24576, 1536) in (B.MI_WEIGHT_ROW_MAJOR, B.MI_WEIGHT_TILED)
     for n, k in ((100, 1536), (256, 0), (-128, 128)):
         assert mi.mi_preferred_weight_layout(n, k) == -1
@@ -206,3 +206,28 @@ def test_binding_refuses_a_second_relayout():
         mi.relayout_weight(tw)
     with pytest.raises(TypeError):
         mi.untile_weight(torch.empty((128, 128), dtype=torch.uint8))
+
+
+def test_e8m0_entry_validation(L):
+    # dual norm-quant: same checks as the fp32-scale call, the byte scales required
+    nq8 = lambda **kw: L.mi_fused_dual_rmsnorm_group_quant_e8m0(
+        kw.get("q", FAKE), 1536, FAKE, 512, FAKE, FAKE, ctypes.c_float(1e-6), kw.get("M", 4), kw.get("Nq", 1536), 512,
+        0, FAKE, kw.get("os_", FAKE), FAKE, NULL)
+    assert nq8(Nq=1500) == B.MI_ERR_SHAPE
+    assert nq8(os_=NULL) == B.MI_ERR_NULL
+    assert nq8(os_=NULL, M=0) == B.MI_OK
+    assert nq8(M=-1, os_=NULL) == B.MI_ERR_SHAPE
+    # GEMMs
+    g8 = lambda **kw: L.mi_block_scaled_fp8_gemm_e8m0(
+        FAKE, kw.get("As", FAKE), 0, FAKE, kw.get("wl", 0), kw.get("Bs", FAKE), FAKE, 4, kw.get("N", 1024), 1536, NULL)
+    assert g8(wl=3) == B.MI_ERR_LAYOUT
+    assert g8(N=1000) == B.MI_ERR_SHAPE
+    assert g8(As=NULL) == B.MI_ERR_NULL
+    assert g8(As=ctypes.c_void_p(0x1002)) == B.MI_ERR_ALIGN
+    assert g8(Bs=ctypes.c_void_p(0x1001)) == B.MI_ERR_ALIGN
+    p8 = lambda **kw: L.mi_block_scaled_fp8_gemm_pair_e8m0(
+        FAKE, FAKE, 0, kw.get("wl", 0), FAKE, kw.get("Bs1", FAKE), FAKE, 256, FAKE, FAKE, FAKE, kw.get("N2", 256), 4,
+        1536, NULL)
+    assert p8(wl=9) == B.MI_ERR_LAYOUT
+    assert p8(N2=100) == B.MI_ERR_SHAPE
+    assert p8(Bs1=NULL) == B.MI_ERR_NULL
