@@ -232,11 +232,12 @@ mi_status mi_block_scaled_fp8_gemm_pair(
  * MI_WEIGHT_TILED: the [N, K] e4m3fn weight as N/16 x K/128 tiles of
  * 2048 bytes, tile (s, kb) at byte (s * (K/128) + kb) * 2048 (the tiles of
  * one 16-row subtile are contiguous); inside a tile, byte
- * g * 1024 + r * 128 + 16 * p + b (g < 2, r < 8, p < 8, b < 16) holds
- * w[16 s + 8 g + r][128 kb + 16 (p ^ r ^ g) + b].  This is the image the
- * GEMM keeps in LDS for a 16 x 128 weight tile (bank-conflict-free
- * fragment reads), so each 1 KB half is one contiguous direct load.  The
- * block scales (w_scale) are not relaid out.
+ * h * 1024 + 16 * L + b (h < 2, L < 64, b < 16) holds
+ * w[16 s + L % 16][128 kb + 32 (L / 16) + 16 h + b]: the tile in the order
+ * the 16x16x128 matrix instruction takes it (lane L = 16 q + r holds row r,
+ * bytes 32 q .. 32 q + 31), so each half of a wave's load of its fragments
+ * is 1 KB of contiguous bytes, into registers or into LDS.  The block scales
+ * (w_scale) are not relaid out.
  */
 typedef enum {
     MI_WEIGHT_ROW_MAJOR = 0,

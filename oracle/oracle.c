@@ -445,25 +445,26 @@ void oracle_dual_rmsnorm_group_quant_e8m0(
  * [D56433] "实现拆解" items 1-3: a block-scale GEMM may ask for its weight to
  * be relaid out once at load time; the relayout is a permutation (not an
  * involution).  The pages do not define a layout for this hardware; the
- * contract checked here is the library's own: the [N, K] weight as N/16 x
- * K/128 tiles of 2048 bytes, tile (s, kb) at (s * K/128 + kb) * 2048, and
- * inside a tile byte g*1024 + r*128 + 16*p + b holding
- * w[16 s + 8 g + r][128 kb + 16 (p ^ r ^ g) + b].  Written as plain loops
- * over the destination, and its inverse as loops over the source.
+ * contract checked here is the library's own, the order in which the
+ * matrix-core instruction consumes a 16-row x 128-byte weight tile: the
+ * [N, K] weight as N/16 x K/128 tiles of 2048 bytes, tile (s, kb) at
+ * (s * K/128 + kb) * 2048, and inside a tile byte h*1024 + 16*L + b
+ * (h < 2, lane L < 64, b < 16) holding w[16 s + L % 16][128 kb + 32 (L / 16)
+ * + 16 h + b].  Written as plain loops over the destination, and its inverse
+ * as loops over the source.
  * ------------------------------------------------------------------------- */
 void oracle_tile_weight(const uint8_t *w, int64_t N, int64_t K, uint8_t *out)
 {
     const int64_t KB = K / ORACLE_GROUP;
     for (int64_t s = 0; s < N / 16; ++s)
         for (int64_t kb = 0; kb < KB; ++kb)
-            for (int g = 0; g < 2; ++g)
-                for (int r = 0; r < 8; ++r)
-                    for (int p = 0; p < 8; ++p)
-                        for (int b = 0; b < 16; ++b) {
-                            int64_t row = 16 * s + 8 * g + r;
-                            int64_t col = ORACLE_GROUP * kb + 16 * (p ^ r ^ g) + b;
-                            out[(s * KB + kb) * 2048 + g * 1024 + r * 128 + 16 * p + b] = w[row * K + col];
-                        }
+            for (int h = 0; h < 2; ++h)
+                for (int L = 0; L < 64; ++L)
+                    for (int b = 0; b < 16; ++b) {
+                        int64_t row = 16 * s + L % 16;
+                        int64_t col = ORACLE_GROUP * kb + 32 * (L / 16) + 16 * h + b;
+                        out[(s * KB + kb) * 2048 + h * 1024 + 16 * L + b] = w[row * K + col];
+                    }
 }
 
 void oracle_untile_weight(const uint8_t *tiled, int64_t N, int64_t K, uint8_t *w)
@@ -471,10 +472,11 @@ void oracle_untile_weight(const uint8_t *tiled, int64_t N, int64_t K, uint8_t *w
     const int64_t KB = K / ORACLE_GROUP;
     for (int64_t row = 0; row < N; ++row)
         for (int64_t col = 0; col < K; ++col) {
-            int64_t s = row / 16, g = (row % 16) / 8, r = row % 8;
-            int64_t kb = col / ORACLE_GROUP, c = (col % ORACLE_GROUP) / 16, b = col % 16;
-            int64_t p = c ^ r ^ g;
-            w[row * K + col] = tiled[(s * KB + kb) * 2048 + g * 1024 + r * 128 + 16 * p + b];
+            int64_t s = row / 16, rho = row % 16;
+            int64_t kb = col / ORACLE_GROUP, c = col % ORACLE_GROUP;
+            int64_t q = c / 32, h = (c % 32) / 16, b = c % 16;
+            int64_t L = 16 * q + rho;
+            w[row * K + col] = tiled[(s * KB + kb) * 2048 + h * 1024 + 16 * L + b];
         }
 }
 

@@ -60,31 +60,26 @@ __device__ __forceinline__ v8i join(const uint4 &lo, const uint4 &hi) {
     return r;
 }
 
-// Weight fragment of lane L for the register-path kernels: row L % 16 of a
-// 16-row subtile, chunks 2q and 2q + 1 (q = L / 16) of each K-block.
-//  row-major: at row * K + 32 q, K-blocks 128 bytes apart;
-//  tiled: the subtile's K-block tiles are 2 KB apart, and inside a tile
-//  chunk c of row 8 g + r sits at g * 1024 + r * 128 + 16 (c ^ r ^ g), so
-//  the two chunks are the aligned 32-byte pair at (2q) ^ (f & 6), f = r ^ g,
-//  in swapped order when f is odd.
+// Weight fragment of lane L: row L % 16 of a 16-row subtile, chunks 2q and
+// 2q + 1 (q = L / 16) of each K-block, as two 16-byte halves.
+//  row-major: at row * K + 32 q (halves adjacent), K-blocks 128 bytes apart;
+//  tiled: the subtile's K-block tiles are 2 KB apart and hold the fragments
+//  in lane order, half h of lane L at h * 1024 + 16 L: each half of a wave's
+//  load is 1 KB of contiguous bytes.
 struct WeightFrag {
     int64_t lane_off;  // from the subtile's first byte
     int64_t kstride;   // between K-blocks
-    bool swap;         // halves in swapped order
+    int64_t hstride;   // between the two halves
 };
 
 __device__ __forceinline__ WeightFrag weight_frag(int lane, int64_t K, int tiled) {
-    const int rho = lane & 15, q = lane >> 4;
     if (!tiled)
-        return {rho * K + 32 * q, kBlk, false};
-    const int g = rho >> 3, r = rho & 7, f = r ^ g;
-    return {g * 1024 + r * 128 + 16 * ((2 * q) ^ (f & 6)), 16 * kBlk, (f & 1) != 0};
+        return {(lane & 15) * K + 32 * (lane >> 4), kBlk, 16};
+    return {16 * lane, 16 * kBlk, 1024};
 }
 
-__device__ __forceinline__ v8i load_weight_frag(const uint8_t *p, bool swap) {
-    const uint4 *src = reinterpret_cast<const uint4 *>(p);
-    const uint4 a = src[0], b = src[1];
-    return swap ? join(b, a) : join(a, b);
+__device__ __forceinline__ v8i load_weight_frag(const uint8_t *p, int64_t hstride) {
+    return join(*reinterpret_cast<const uint4 *>(p), *reinterpret_cast<const uint4 *>(p + hstride));
 }
 
 // e8m0 exponent byte -> its value 2^(e - 127) as fp32 (exact; e = 0 is the
@@ -145,7 +140,7 @@ __global__ __launch_bounds__(256) void block_scaled_fp8_gemm_kernel(GemmParams p
 #pragma unroll
         for (int j = 0; j < kStageKb; ++j) {
             if (j < kc)
-                wf[j] = load_weight_frag(wrow + (kb0 + j) * wfrag.kstride, wfrag.swap);
+                wf[j] = load_weight_frag(wrow + (kb0 + j) * wfrag.kstride, wfrag.hstride);
         }
 
         __syncthreads();  // the previous stage's LDS reads are done
@@ -350,6 +345,7 @@ struct WideWave {
     const uint8_t *a;
     uint32_t a_off[kMT][2];        // per lane: m-tile j, row half g
     uint32_t frag_lo, frag_hi;     // per lane: LDS offsets of its fragment halves inside a 2 KB tile
+    uint32_t wfrag_lo, wfrag_hi;   // the same for weight tiles (tiled weights: lane order)
     const float *a_scale;
     int64_t s_stride;  // As elements between K-blocks
     uint32_t s_off;
@@ -443,8 +439,8 @@ struct WideWave {
         }
 #pragma unroll
         for (int t = 0; t < kNS; ++t) {
-            wfs[b][t] = join4(*reinterpret_cast<const v4u32 *>(ws + (2 * t) * P::kSlot + frag_lo),
-                              *reinterpret_cast<const v4u32 *>(ws + (2 * t) * P::kSlot + frag_hi));
+            wfs[b][t] = join4(*reinterpret_cast<const v4u32 *>(ws + (2 * t) * P::kSlot + wfrag_lo),
+                              *reinterpret_cast<const v4u32 *>(ws + (2 * t) * P::kSlot + wfrag_hi));
             if constexpr (!kE8m0)
                 bss[b][t] = ss[kWave + t];  // same address in every lane: broadcast read
         }
@@ -535,13 +531,16 @@ __global__ __launch_bounds__(kWaves * kWave) void block_scaled_fp8_gemm_wide_ker
     // repeat row M - 1: their results are never stored.
     // Weight slot (subtile, row half) = (slot / 2, slot % 2); this wave loads
     // slots (wave + kWaves i) mod 2 kNS, all of row half wave % 2.
-    // A tiled weight holds each (subtile, K-block) tile as exactly this LDS
-    // image: a slot is 1 KB of contiguous bytes.
+    // A tiled weight holds each (subtile, K-block) tile in lane order: its
+    // half g is 1 KB of contiguous bytes, copied to slot g as is, and lane L
+    // reads its fragment at 16 L of each slot (conflict-free).
     {
         const int g = wave & 1;
         w.w_off = p.w_tiled ? static_cast<uint32_t>(g * 1024 + lane * 16)
                             : static_cast<uint32_t>((8 * g + lrow) * K + 16 * (lchunk ^ lrow ^ g));
         w.w_kstride = p.w_tiled ? 16 * kBlk : kBlk;
+        w.wfrag_lo = p.w_tiled ? static_cast<uint32_t>(16 * lane) : w.frag_lo;
+        w.wfrag_hi = p.w_tiled ? static_cast<uint32_t>(1024 + 16 * lane) : w.frag_hi;
     }
 #pragma unroll
     for (int i = 0; i < W::P::kNW; ++i) {
@@ -639,6 +638,307 @@ __global__ __launch_bounds__(kWaves * kWave) void block_scaled_fp8_gemm_wide_ker
         const int64_t m = m_base + row, st = st0 + col / 16;
         const v4u32 v = *reinterpret_cast<const v4u32 *>(tile + row * kCols + col);
         if (m < M && st < S) {  // streaming store: the output is not read back here
+            const SubTile sub = subtile(p, st);
+            __builtin_nontemporal_store(v, reinterpret_cast<v4u32 *>(sub.out + m * sub.ldo + sub.n0 + col % 16));
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Stream variant (M <= 16 kMT <= 64, K/128 = kKB known at compile time).
+//
+// For decode batches the GEMM is a pure weight stream, and what limits it is
+// how the stream is fed, not the matrix cores.  Here the waves of a block
+// never wait for each other inside the K loop:
+//  - the whole activation tile (all M rows, all K-blocks; 96 KB at M = 64,
+//    K = 1536) and its scales are loaded into LDS once, behind one barrier
+//    (rows in the 1 KB slot image of the wide kernel);
+//  - each wave owns kSW 16-row weight subtiles for all M rows, and streams
+//    them through a ring of its own in LDS (kD K-blocks deep) by direct
+//    global -> LDS loads, waiting only for its own loads (exact vmcnt
+//    counts);
+//  - per K-block a wave reads its kSW weight and kMT activation fragments
+//    (the next K-block's during this one's matrix-core work), so each
+//    weight fragment is read from LDS once.
+// (Measured against the same kernel with the weight ring in registers: the
+// LDS ring was faster at every batch size.)
+// ---------------------------------------------------------------------------
+template <int kKB, int kMT, int kSW, int kWaves, int kD, bool kE8m0>
+struct StreamPlan {
+    static constexpr int kSlot = 1024;
+    static constexpr int kASlots = kKB * kMT * 2;                        // activation slots, all K
+    static constexpr int kNA = (kASlots + kWaves - 1) / kWaves;          // per wave (spares repeat a slot)
+    static constexpr int kNS = kE8m0 ? 0 : (kKB + kWaves - 1) / kWaves;  // As loads per wave (one per K-block)
+    static constexpr int kNW = 2 * kSW;                                  // weight loads per wave per K-block
+    static constexpr int kDD = kD < kKB ? kD : kKB;                      // ring depth actually used
+    static constexpr int kAOff = 0;
+    static constexpr int kSOff = kAOff + kASlots * kSlot;
+    static constexpr int kWOff = kSOff + (kE8m0 ? 0 : kKB * kWave * 4);
+    static constexpr int kWaveRing = kDD * kSW * 2 * kSlot;
+    static constexpr int kLds = kWOff + kWaves * kWaveRing;
+    static_assert(kLds <= 160 * 1024, "LDS per CU");
+    static_assert(kNA + kNS + kDD * kNW <= 63, "outstanding loads per wave fit vmcnt");
+    static_assert(16 * kMT * 16 * kSW * 2 <= kWaveRing, "output tile fits the wave's ring");
+    // weight loads this wave issued after the last load of stage st, when
+    // it waits for st (before the K loop for st = 0, else in iteration
+    // st - 1 before that iteration's refill).  Issue order: stage 0,
+    // activations and scales, stages 1 .. kDD - 1, then one refill per
+    // iteration; stage 0 and the activations are waited for before the
+    // barrier, so only weight loads are counted here.
+    static constexpr int vm_wait(int st) {
+        const int issued = st == 0 ? kDD : (kDD + st - 1 < kKB ? kDD + st - 1 : kKB);
+        return (issued - (st + 1)) * kNW;
+    }
+};
+
+template <int kKB, int kMT, int kSW, int kWaves, int kD, bool kE8m0>
+struct StreamWave {
+    using P = StreamPlan<kKB, kMT, kSW, kWaves, kD, kE8m0>;
+    static constexpr int kLag = 2;
+    static constexpr int kRing = kLag + 2;
+
+    uint8_t *lds;
+    uint8_t *ring;                 // this wave's weight ring
+    int lane;
+    const uint8_t *wsrc[kSW];      // uniform: first byte of each owned subtile
+    uint32_t w_off[2];             // per lane: its part of the load of slot half g
+    uint32_t w_kstride;            // uniform: bytes between K-blocks of a subtile
+    uint32_t frag_lo, frag_hi;     // per lane: activation fragment halves in a slot pair
+    uint32_t wfrag_lo, wfrag_hi;   // the same for weight slot pairs
+
+    v4f acc[kMT][kSW];
+    v4f part[kRing];
+    float scl[kRing];
+    float bs[kSW][kKB];                  // fp32 weight block scales (uniform)
+    uint32_t asw[kMT][(kKB + 3) / 4];    // e8m0: this lane's activation rows
+    uint32_t bsw[kSW][(kKB + 3) / 4];    // e8m0: weight scale bytes (uniform)
+
+    v8i af[2][kMT];
+    float asv[2][kMT];
+    v8i wfs[2][kSW];
+
+    __device__ __forceinline__ void issue_w(int s) {
+        uint8_t *dst = ring + (s % P::kDD) * kSW * 2 * P::kSlot;
+#pragma unroll
+        for (int t = 0; t < kSW; ++t)
+#pragma unroll
+            for (int g = 0; g < 2; ++g)
+                __builtin_amdgcn_global_load_lds(wsrc[t] + s * w_kstride + w_off[g], dst + (2 * t + g) * P::kSlot, 16,
+                                                 0, 0);
+    }
+
+    // activation slots (all K-blocks) and As, split over the waves; slot
+    // (kb, j, g) holds rows 16 j + 8 g .. + 7 of K-block kb (rows at or
+    // beyond M repeat row M - 1: their results are never stored).  A member
+    // function, not inline in the kernel: the host pass drops the launch
+    // stub of a kernel whose own body issues direct global -> LDS loads.
+    __device__ __forceinline__ void issue_activations(const GemmParams &p, int wave) {
+        const int lrow = lane >> 3, lchunk = lane & 7;
+        const int64_t M = p.M, K = p.K;
+#pragma unroll
+        for (int i = 0; i < P::kNA; ++i) {
+            const int slot = (wave + kWaves * i) % P::kASlots;
+            const int kb = slot / (2 * kMT), j = (slot / 2) % kMT, g = slot % 2;
+            const int64_t row = min<int64_t>(16 * j + 8 * g + lrow, M - 1);
+            __builtin_amdgcn_global_load_lds(p.a + row * K + kb * kBlk + 16 * (lchunk ^ lrow ^ g),
+                                             lds + P::kAOff + slot * P::kSlot, 16, 0, 0);
+        }
+        if constexpr (!kE8m0) {
+            const int64_t row = min<int64_t>(lane, M - 1);
+#pragma unroll
+            for (int i = 0; i < P::kNS; ++i) {
+                const int kb = (wave + kWaves * i) % kKB;
+                const float *src = p.a_scale + (p.a_scale_transposed ? kb * M + row : row * kKB + kb);
+                __builtin_amdgcn_global_load_lds(src, lds + P::kSOff + kb * kWave * 4, 4, 0, 0);
+            }
+        }
+    }
+
+    __device__ __forceinline__ void fold(int n) {
+        const int j = n % kMT, t = (n / kMT) % kSW, r = n % kRing;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            acc[j][t][i] = fmaf(part[r][i], scl[r], acc[j][t][i]);
+    }
+
+    template <int st>
+    __device__ __forceinline__ void read_frags() {
+        constexpr int b = st & 1;
+#pragma unroll
+        for (int j = 0; j < kMT; ++j) {
+            const uint8_t *sl = lds + P::kAOff + (st * kMT + j) * 2 * P::kSlot;
+            af[b][j] = join4(*reinterpret_cast<const v4u32 *>(sl + frag_lo),
+                             *reinterpret_cast<const v4u32 *>(sl + frag_hi));
+            if constexpr (!kE8m0)
+                asv[b][j] = reinterpret_cast<const float *>(lds + P::kSOff)[st * kWave + 16 * j + (lane & 15)];
+        }
+        const uint8_t *ws = ring + (st % P::kDD) * kSW * 2 * P::kSlot;
+#pragma unroll
+        for (int t = 0; t < kSW; ++t)
+            wfs[b][t] = join4(*reinterpret_cast<const v4u32 *>(ws + 2 * t * P::kSlot + wfrag_lo),
+                              *reinterpret_cast<const v4u32 *>(ws + 2 * t * P::kSlot + wfrag_hi));
+    }
+
+    template <int kb>
+    __device__ __forceinline__ void kblock() {
+        if constexpr (kb + 1 < kKB) {
+            wait_vmcnt<P::vm_wait(kb + 1)>();     // stage kb + 1 of this wave's ring has landed
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's reads of stage kb are done: its slot is free
+            if constexpr (kb + P::kDD < kKB)
+                issue_w(kb + P::kDD);
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags<kb + 1>();
+        }
+        constexpr int b = kb & 1;
+        if constexpr (kE8m0) {
+            constexpr int wd = kb / 4, sh = 8 * (kb % 4);
+#pragma unroll
+            for (int t = 0; t < kSW; ++t)
+#pragma unroll
+                for (int j = 0; j < kMT; ++j)
+                    acc[j][t] = mfma_e4m3_16x16x128_scaled(wfs[b][t], af[b][j], acc[j][t], (bsw[t][wd] >> sh) & 0xFFu,
+                                                           (asw[j][wd] >> sh) & 0xFFu);
+        } else {
+#pragma unroll
+            for (int t = 0; t < kSW; ++t) {
+#pragma unroll
+                for (int j = 0; j < kMT; ++j) {
+                    const int n = (kb * kSW + t) * kMT + j;
+                    part[n % kRing] = mfma_e4m3_16x16x128(wfs[b][t], af[b][j]);
+                    scl[n % kRing] = asv[b][j] * bs[t][kb];
+                    if (n >= kLag) {
+                        fold(n - kLag);
+                        v4f &folded = acc[(n - kLag) % kMT][((n - kLag) / kMT) % kSW];
+                        asm volatile("" : "+v"(af[b][(j + 1) % kMT]), "+v"(folded));
+                    }
+                }
+            }
+        }
+        if constexpr (kb + 1 < kKB)
+            kblock<kb + 1>();
+    }
+};
+
+template <int kKB, int kMT, int kSW, int kWaves, int kD, bool kE8m0>
+__global__ __launch_bounds__(kWaves * kWave) void block_scaled_fp8_gemm_stream_kernel(GemmParams p) {
+    using SW = StreamWave<kKB, kMT, kSW, kWaves, kD, kE8m0>;
+    using P = typename SW::P;
+    extern __shared__ uint4 s_dyn[];
+    SW w;
+    w.lds = reinterpret_cast<uint8_t *>(s_dyn);
+    w.lane = threadIdx.x & (kWave - 1);
+    const int lane = w.lane;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    w.ring = w.lds + P::kWOff + wave * P::kWaveRing;
+    const int64_t M = p.M, K = p.K;
+    const int64_t S = (p.N + p.N2) / 16;
+    const int64_t st0 = (static_cast<int64_t>(blockIdx.x) * kWaves + wave) * kSW;  // this wave's first subtile
+
+    {
+        const int rho = lane & 15, g = rho >> 3, r = rho & 7, q = lane >> 4;
+        w.frag_lo = static_cast<uint32_t>(g * 1024 + r * 128 + (((2 * q) ^ (r ^ g)) * 16));
+        w.frag_hi = static_cast<uint32_t>(g * 1024 + r * 128 + (((2 * q + 1) ^ (r ^ g)) * 16));
+    }
+    // weight slot pairs: row-major weights in the activations' image; a
+    // tiled weight's halves are copied as they are (lane order)
+    const int lrow = lane >> 3, lchunk = lane & 7;
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+        w.w_off[g] = p.w_tiled ? static_cast<uint32_t>(g * 1024 + lane * 16)
+                               : static_cast<uint32_t>((8 * g + lrow) * K + 16 * (lchunk ^ lrow ^ g));
+    w.w_kstride = p.w_tiled ? 16 * kBlk : kBlk;
+    w.wfrag_lo = p.w_tiled ? static_cast<uint32_t>(16 * lane) : w.frag_lo;
+    w.wfrag_hi = p.w_tiled ? static_cast<uint32_t>(1024 + 16 * lane) : w.frag_hi;
+
+    // block scales of the owned subtiles (and, e8m0, the activation scale
+    // bytes): plain loads issued before every direct load; subtiles past the
+    // end repeat the last (never stored)
+#pragma unroll
+    for (int t = 0; t < kSW; ++t) {
+        const SubTile sub = subtile(p, min<int64_t>(st0 + t, S - 1));
+        w.wsrc[t] = sub.w;
+        if constexpr (kE8m0) {
+#pragma unroll
+            for (int i = 0; i < (kKB + 3) / 4; ++i)
+                w.bsw[t][i] = reinterpret_cast<const uint32_t *>(sub.ws8)[i];
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < kKB; ++kb)
+                w.bs[t][kb] = sub.ws[kb];
+        }
+    }
+    if constexpr (kE8m0) {
+#pragma unroll
+        for (int j = 0; j < kMT; ++j) {
+            const int64_t r = min<int64_t>(16 * j + (lane & 15), M - 1);
+#pragma unroll
+            for (int i = 0; i < (kKB + 3) / 4; ++i) {
+                if (p.a_scale_transposed) {
+                    uint32_t v = 0;
+#pragma unroll
+                    for (int qq = 0; qq < 4; ++qq)
+                        v |= static_cast<uint32_t>(p.a_scale8[static_cast<int64_t>(4 * i + qq) * M + r]) << (8 * qq);
+                    w.asw[j][i] = v;
+                } else {
+                    w.asw[j][i] = reinterpret_cast<const uint32_t *>(p.a_scale8 + r * kKB)[i];
+                }
+            }
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // weight stage 0 first (its HBM latency starts at once), then the
+    // activation tile and scales (L2), then the rest of the ring
+    w.issue_w(0);
+    __builtin_amdgcn_sched_barrier(0);
+    w.issue_activations(p, wave);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 1; s < P::kDD; ++s)
+        w.issue_w(s);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < kMT; ++j)
+#pragma unroll
+        for (int t = 0; t < kSW; ++t)
+            w.acc[j][t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // this wave's activation loads and weight stage 0 have landed (only
+    // weight stages 1 .. kDD - 1 are younger); then every wave's have
+    wait_vmcnt<(P::kDD - 1) * P::kNW>();
+    __builtin_amdgcn_s_barrier();
+    w.template read_frags<0>();
+    w.template kblock<0>();
+    if constexpr (!kE8m0) {
+#pragma unroll
+        for (int n = kKB * kSW * kMT - SW::kLag; n < kKB * kSW * kMT; ++n)
+            w.fold(n);
+    }
+
+    // output tile of this wave (16 kMT rows x 16 kSW columns) through its own
+    // ring, then 16-byte row pieces
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    constexpr int kCols = 16 * kSW;
+    uint16_t *tile = reinterpret_cast<uint16_t *>(w.ring);
+#pragma unroll
+    for (int j = 0; j < kMT; ++j)
+#pragma unroll
+        for (int t = 0; t < kSW; ++t)
+            *reinterpret_cast<uint2 *>(tile + (16 * j + (lane & 15)) * kCols + 16 * t + 4 * (lane >> 4)) =
+                make_uint2(pack2_bf16(w.acc[j][t][0], w.acc[j][t][1]), pack2_bf16(w.acc[j][t][2], w.acc[j][t][3]));
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    constexpr int kPieces = 2 * kSW;
+    constexpr int kTilePieces = 16 * kMT * kPieces;
+#pragma unroll
+    for (int i = 0; i < (kTilePieces + kWave - 1) / kWave; ++i) {
+        const int pc = lane + i * kWave;
+        if (kTilePieces % kWave != 0 && pc >= kTilePieces)
+            break;
+        const int row = pc / kPieces, col = 8 * (pc % kPieces);
+        const int64_t m = row, st = st0 + col / 16;
+        const v4u32 v = *reinterpret_cast<const v4u32 *>(tile + row * kCols + col);
+        if (m < M && st < S) {
             const SubTile sub = subtile(p, st);
             __builtin_nontemporal_store(v, reinterpret_cast<v4u32 *>(sub.out + m * sub.ldo + sub.n0 + col % 16));
         }
@@ -760,7 +1060,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void block_scaled_fp8_gemm_de
     float bs[kKB];
 #pragma unroll
     for (int kb = 0; kb < kRingN; ++kb)
-        wf[kb] = load_weight_frag(wrow + kb * wfrag.kstride, wfrag.swap);
+        wf[kb] = load_weight_frag(wrow + kb * wfrag.kstride, wfrag.hstride);
     const float *bs_row = p.w_scale + (st_ld * 16 / kBlk) * kKB;
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb)
@@ -815,7 +1115,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void block_scaled_fp8_gemm_de
         }
         // refill the slot just consumed with K-block kb + kRing
         if (kb + kRingN < kKB)
-            wf[kb % kRingN] = load_weight_frag(wrow + (kb + kRingN) * wfrag.kstride, wfrag.swap);
+            wf[kb % kRingN] = load_weight_frag(wrow + (kb + kRingN) * wfrag.kstride, wfrag.hstride);
 #pragma unroll
         for (int t = 0; t < kMT; ++t) {
 #pragma unroll
@@ -878,6 +1178,69 @@ hipError_t launch_decode_kb(const GemmParams &p, hipStream_t stream) {
     if (p.M <= 48)
         return launch_decode<3, kKB>(p, stream);
     return launch_decode<4, kKB>(p, stream);
+}
+
+// ring depth of the stream kernel: as deep as the LDS left after the
+// activation tile allows, at most 6 K-blocks
+template <int kKB, int kMT, int kSW, int kWaves, bool kE8m0>
+constexpr int stream_depth() {
+    constexpr int fixed = kKB * kMT * 2 * 1024 + (kE8m0 ? 0 : kKB * kWave * 4);
+    constexpr int d = (160 * 1024 - fixed) / (kWaves * kSW * 2 * 1024);
+    return d < 6 ? d : 6;
+}
+
+template <int kKB, int kMT, int kSW, int kWaves, bool kE8m0>
+hipError_t launch_stream_scaled(const GemmParams &p, hipStream_t stream) {
+    constexpr int kD = stream_depth<kKB, kMT, kSW, kWaves, kE8m0>();
+    static_assert(kD >= 2, "at least two ring stages");
+    using P = StreamPlan<kKB, kMT, kSW, kWaves, kD, kE8m0>;
+    const int64_t per_block = kWaves * kSW;
+    const int64_t blocks = ((p.N + p.N2) / 16 + per_block - 1) / per_block;
+    if (blocks > 0x7FFFFFFF || p.M > 16 * kMT)
+        return hipErrorInvalidValue;
+    auto kern = block_scaled_fp8_gemm_stream_kernel<kKB, kMT, kSW, kWaves, kD, kE8m0>;
+    static std::atomic<uint64_t> lds_set{0};
+    const hipError_t e = allow_dynamic_lds(kern, P::kLds, lds_set);
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kWaves * kWave), P::kLds, stream, p);
+    return hipGetLastError();
+}
+
+template <int kKB, int kMT, int kWaves>
+hipError_t launch_stream_w(const GemmParams &p, hipStream_t stream) {
+    return p.scale_e8m0 ? launch_stream_scaled<kKB, kMT, 2, kWaves, true>(p, stream)
+                        : launch_stream_scaled<kKB, kMT, 2, kWaves, false>(p, stream);
+}
+
+template <int kKB>
+hipError_t launch_stream_kb(const GemmParams &p, int waves, hipStream_t stream) {
+    if (p.M <= 16)
+        return waves == 3 ? launch_stream_w<kKB, 1, 3>(p, stream) : launch_stream_w<kKB, 1, 4>(p, stream);
+    if (p.M <= 32)
+        return waves == 3 ? launch_stream_w<kKB, 2, 3>(p, stream) : launch_stream_w<kKB, 2, 4>(p, stream);
+    return waves == 3 ? launch_stream_w<kKB, 4, 3>(p, stream) : launch_stream_w<kKB, 4, 4>(p, stream);
+}
+
+// Decode batches (M <= 64) over at least 6 weight subtiles per CU with K/128
+// in {4, 8, 12}: the stream kernel, 2 subtiles per wave, 3 waves per block
+// at 6 subtiles per CU, else 4.  Returns hipErrorNotSupported otherwise.
+hipError_t launch_stream(const GemmParams &p, hipStream_t stream) {
+    const int64_t S = (p.N + p.N2) / 16, cus = device_cu_count();
+    const int64_t per_cu = (S + cus - 1) / cus;
+    if (p.M > 64 || per_cu < 6)
+        return hipErrorNotSupported;
+    const int waves = per_cu <= 6 ? 3 : 4;
+    switch (p.K / kBlk) {
+    case 4:
+        return launch_stream_kb<4>(p, waves, stream);
+    case 8:
+        return launch_stream_kb<8>(p, waves, stream);
+    case 12:
+        return launch_stream_kb<12>(p, waves, stream);
+    default:
+        return hipErrorNotSupported;
+    }
 }
 
 template <int kKB, int kNS, int kMT, int kWaves, bool kE8m0>
@@ -961,6 +1324,12 @@ hipError_t launch_mt(const GemmParams &p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_block_scaled_gemm(const GemmParams &p, hipStream_t stream) {
+    // decode batches over wide weights: the barrier-free stream kernel
+    {
+        const hipError_t e = launch_stream(p, stream);
+        if (e != hipErrorNotSupported)
+            return e;
+    }
     // Small decode batches over wide weights (more than 4 subtiles per CU):
     // weight ring per wave, activations resident in LDS.
     // (e8m0 scales: the wide kernel, whose matrix cores apply them)
@@ -1007,20 +1376,20 @@ hipError_t launch_block_scaled_gemm(const GemmParams &p, hipStream_t stream) {
 namespace {
 
 // Row-major <-> tiled weight, one thread per 16-byte chunk of the tiled
-// image: a wave covers one 1 KB slot (8 rows x 128 bytes of one K-block),
-// contiguous on the tiled side, 8 whole 128-byte row pieces on the other.
+// image: a wave covers one 1 KB half-tile (lane order), contiguous on the
+// tiled side, 4 alternate 16-byte chunks of each of 16 rows of one K-block
+// on the row-major side.
 __global__ __launch_bounds__(256) void weight_relayout_kernel(const uint8_t *src, uint8_t *dst, int64_t N,
                                                               int64_t K, int to_tiled) {
     const int64_t chunks = N * K / 16;
     const int64_t KB = K / kBlk;
     for (int64_t o = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; o < chunks;
          o += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-        // o = ((st * KB + kb) * 2 + g) * 64 + r * 8 + pos
-        const int pos = static_cast<int>(o & 7), r = static_cast<int>((o >> 3) & 7),
-                  g = static_cast<int>((o >> 6) & 1);
+        // o = ((st * KB + kb) * 2 + h) * 64 + L: lane L = 16 q + rho holds
+        // row rho, chunks 2q (h = 0) and 2q + 1 (h = 1) of the K-block
+        const int L = static_cast<int>(o & 63), h = static_cast<int>((o >> 6) & 1);
         const int64_t tile = o >> 7, st = tile / KB, kb = tile % KB;
-        const int c = pos ^ r ^ g;
-        const int64_t rm = ((st * 16 + 8 * g + r) * K + kb * kBlk) / 16 + c;  // row-major chunk
+        const int64_t rm = ((st * 16 + (L & 15)) * K + kb * kBlk) / 16 + 2 * (L >> 4) + h;  // row-major chunk
         const uint4 *s = reinterpret_cast<const uint4 *>(src);
         uint4 *d = reinterpret_cast<uint4 *>(dst);
         if (to_tiled)
@@ -1043,8 +1412,12 @@ hipError_t launch_weight_relayout(const uint8_t *src, uint8_t *dst, int64_t N, i
 
 hipError_t launch_block_scaled_gemm_pair(const GemmParams &p, hipStream_t stream) {
     // decode batches: one launch over the subtiles of both weights, sharing
-    // the activation stages
+    // the activation tile (the stream kernel where the weights are wide
+    // enough, else the wide kernel)
     if (p.M <= kChunkRows) {
+        const hipError_t e = launch_stream(p, stream);
+        if (e != hipErrorNotSupported)
+            return e;
         switch (p.K / kBlk) {
         case 4:
             return launch_wide_kb<4>(p, stream);

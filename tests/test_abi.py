@@ -45,6 +45,16 @@ def test_library_exports_every_declared_symbol(L):
         assert hasattr(L, name)
 
 
+def test_no_kernel_of_the_library_is_left_undefined():
+    """A kernel whose launch stub the host compiler pass dropped shows up as
+    an undefined symbol of the library's own namespace (the library would
+    then fail to load on a GPU machine)."""
+    out = subprocess.run(["nm", "-D", "--undefined-only", B.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    own = [line.split()[-1] for line in out.splitlines() if "_ZN2mi" in line]
+    assert not own, own[:5]
+
+
 def test_status_strings(L):
     for s in range(8):
         assert mi.mi_status_string(s).startswith(("MI_OK", "MI_ERR"))
