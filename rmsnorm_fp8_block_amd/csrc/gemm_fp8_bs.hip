@@ -645,7 +645,10 @@ __global__ __launch_bounds__(kWaves * kWave) void block_scaled_fp8_gemm_wide_ker
 }
 
 // ---------------------------------------------------------------------------
-// Stream variant (M <= 16 kMT <= 64, K/128 = kKB known at compile time).
+// Stream variant (16 kMT <= 64 rows per block, K/128 = kKB known at compile
+// time; more rows are split into chunks of 16 kMT, one block per chunk and
+// weight slab, the chunks of one slab on one XCD so the slab is fetched into
+// its L2 once).
 //
 // For decode batches the GEMM is a pure weight stream, and what limits it is
 // how the stream is fed, not the matrix cores.  Here the waves of a block
@@ -732,19 +735,19 @@ struct StreamWave {
     // beyond M repeat row M - 1: their results are never stored).  A member
     // function, not inline in the kernel: the host pass drops the launch
     // stub of a kernel whose own body issues direct global -> LDS loads.
-    __device__ __forceinline__ void issue_activations(const GemmParams &p, int wave) {
+    __device__ __forceinline__ void issue_activations(const GemmParams &p, int wave, int64_t m0) {
         const int lrow = lane >> 3, lchunk = lane & 7;
         const int64_t M = p.M, K = p.K;
 #pragma unroll
         for (int i = 0; i < P::kNA; ++i) {
             const int slot = (wave + kWaves * i) % P::kASlots;
             const int kb = slot / (2 * kMT), j = (slot / 2) % kMT, g = slot % 2;
-            const int64_t row = min<int64_t>(16 * j + 8 * g + lrow, M - 1);
+            const int64_t row = min<int64_t>(m0 + 16 * j + 8 * g + lrow, M - 1);
             __builtin_amdgcn_global_load_lds(p.a + row * K + kb * kBlk + 16 * (lchunk ^ lrow ^ g),
                                              lds + P::kAOff + slot * P::kSlot, 16, 0, 0);
         }
         if constexpr (!kE8m0) {
-            const int64_t row = min<int64_t>(lane, M - 1);
+            const int64_t row = min<int64_t>(m0 + lane, M - 1);
 #pragma unroll
             for (int i = 0; i < P::kNS; ++i) {
                 const int kb = (wave + kWaves * i) % kKB;
@@ -832,7 +835,13 @@ __global__ __launch_bounds__(kWaves * kWave) void block_scaled_fp8_gemm_stream_k
     w.ring = w.lds + P::kWOff + wave * P::kWaveRing;
     const int64_t M = p.M, K = p.K;
     const int64_t S = (p.N + p.N2) / 16;
-    const int64_t st0 = (static_cast<int64_t>(blockIdx.x) * kWaves + wave) * kSW;  // this wave's first subtile
+    // block -> (weight slab, row chunk); the chunks of a slab get
+    // consecutive ids, renumbered onto one XCD
+    constexpr int kChunk = 16 * kMT;
+    const int nm = static_cast<int>((M + kChunk - 1) / kChunk);
+    const int b = nm > 1 ? xcd_contiguous_block(blockIdx.x, gridDim.x) : static_cast<int>(blockIdx.x);
+    const int64_t m0 = static_cast<int64_t>(b % nm) * kChunk;
+    const int64_t st0 = (static_cast<int64_t>(b / nm) * kWaves + wave) * kSW;  // this wave's first subtile
 
     {
         const int rho = lane & 15, g = rho >> 3, r = rho & 7, q = lane >> 4;
@@ -870,7 +879,7 @@ __global__ __launch_bounds__(kWaves * kWave) void block_scaled_fp8_gemm_stream_k
     if constexpr (kE8m0) {
 #pragma unroll
         for (int j = 0; j < kMT; ++j) {
-            const int64_t r = min<int64_t>(16 * j + (lane & 15), M - 1);
+            const int64_t r = min<int64_t>(m0 + 16 * j + (lane & 15), M - 1);
 #pragma unroll
             for (int i = 0; i < (kKB + 3) / 4; ++i) {
                 if (p.a_scale_transposed) {
@@ -891,7 +900,7 @@ __global__ __launch_bounds__(kWaves * kWave) void block_scaled_fp8_gemm_stream_k
     // activation tile and scales (L2), then the rest of the ring
     w.issue_w(0);
     __builtin_amdgcn_sched_barrier(0);
-    w.issue_activations(p, wave);
+    w.issue_activations(p, wave, m0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 1; s < P::kDD; ++s)
@@ -936,7 +945,7 @@ __global__ __launch_bounds__(kWaves * kWave) void block_scaled_fp8_gemm_stream_k
         if (kTilePieces % kWave != 0 && pc >= kTilePieces)
             break;
         const int row = pc / kPieces, col = 8 * (pc % kPieces);
-        const int64_t m = row, st = st0 + col / 16;
+        const int64_t m = m0 + row, st = st0 + col / 16;
         const v4u32 v = *reinterpret_cast<const v4u32 *>(tile + row * kCols + col);
         if (m < M && st < S) {
             const SubTile sub = subtile(p, st);
@@ -1195,8 +1204,9 @@ hipError_t launch_stream_scaled(const GemmParams &p, hipStream_t stream) {
     static_assert(kD >= 2, "at least two ring stages");
     using P = StreamPlan<kKB, kMT, kSW, kWaves, kD, kE8m0>;
     const int64_t per_block = kWaves * kSW;
-    const int64_t blocks = ((p.N + p.N2) / 16 + per_block - 1) / per_block;
-    if (blocks > 0x7FFFFFFF || p.M > 16 * kMT)
+    const int64_t nm = (p.M + 16 * kMT - 1) / (16 * kMT);
+    const int64_t blocks = ((p.N + p.N2) / 16 + per_block - 1) / per_block * nm;
+    if (blocks > 0x7FFFFFFF || p.M > 256)
         return hipErrorInvalidValue;
     auto kern = block_scaled_fp8_gemm_stream_kernel<kKB, kMT, kSW, kWaves, kD, kE8m0>;
     static std::atomic<uint64_t> lds_set{0};
@@ -1222,15 +1232,28 @@ hipError_t launch_stream_kb(const GemmParams &p, int waves, hipStream_t stream) 
     return waves == 3 ? launch_stream_w<kKB, 4, 3>(p, stream) : launch_stream_w<kKB, 4, 4>(p, stream);
 }
 
-// Decode batches (M <= 64) over at least 6 weight subtiles per CU with K/128
-// in {4, 8, 12}: the stream kernel, 2 subtiles per wave, 3 waves per block
-// at 6 subtiles per CU, else 4.  Returns hipErrorNotSupported otherwise.
+// The stream kernel, 2 subtiles per wave, where its grid (weight slabs x
+// 64-row chunks) covers the CUs: decode batches (M <= 64) over at least 6
+// weight subtiles per CU (3 waves per block at 6, else 4), and 64 < M <= 256
+// (4 waves).  K/128 in {4, 8, 12}.  Returns hipErrorNotSupported otherwise.
 hipError_t launch_stream(const GemmParams &p, hipStream_t stream) {
     const int64_t S = (p.N + p.N2) / 16, cus = device_cu_count();
     const int64_t per_cu = (S + cus - 1) / cus;
-    if (p.M > 64 || per_cu < 6)
+    if (p.M > 256 || (p.M <= 64 && per_cu < 6))
         return hipErrorNotSupported;
-    const int waves = per_cu <= 6 ? 3 : 4;
+    if (p.M > 64) {
+        // Row chunks re-read their slab's weights (from L2), the wide kernel
+        // re-reads every activation row per block: take the stream kernel only
+        // where it moves fewer bytes from L2 into LDS, and fills the CUs.
+        const int64_t nm = (p.M + 63) / 64, slabs = (S + 7) / 8;
+        const int64_t wbytes = S * 16 * p.K;
+        const int64_t ns_wide = per_cu <= 2 ? 2 : per_cu <= 4 ? 4 : 6;
+        const int64_t wide_bytes = wbytes + (S + ns_wide - 1) / ns_wide * p.M * p.K;
+        const int64_t stream_bytes = nm * wbytes + slabs * nm * 64 * p.K;
+        if (slabs * nm < cus || stream_bytes >= wide_bytes)
+            return hipErrorNotSupported;
+    }
+    const int waves = p.M <= 64 && per_cu <= 6 ? 3 : 4;
     switch (p.K / kBlk) {
     case 4:
         return launch_stream_kb<4>(p, waves, stream);
