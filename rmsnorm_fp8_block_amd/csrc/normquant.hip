@@ -45,11 +45,17 @@ constexpr float kInvE4m3Max = 1.0f / 448.0f;  // rounded to fp32
 constexpr float kScaleFloor = 1e-12f;
 constexpr int kE8m0MinExponent = -39;  // ceil(log2(1e-12)): the floor as a power of two
 
+typedef unsigned v4u32 __attribute__((ext_vector_type(4)));
+
 // 8 consecutive bf16 at p[col, col+8); elements at or beyond n read as zero.
 // kVec: p + col is 16-byte aligned whenever col + 8 <= n.  kFull: the caller
 // guarantees col + 8 <= n (no bounds test, a single 16-byte load).
-template <bool kVec, bool kFull = false>
+template <bool kVec, bool kFull = false, bool kStream = false>
 __device__ __forceinline__ uint4 load8(const uint16_t *p, int col, int n) {
+    if (kFull && kStream) {  // read once: streamed past the caches
+        const v4u32 v = __builtin_nontemporal_load(reinterpret_cast<const v4u32 *>(p + col));
+        return make_uint4(v.x, v.y, v.z, v.w);
+    }
     if (kFull)
         return *reinterpret_cast<const uint4 *>(p + col);
     if (kVec && col + 8 <= n)
@@ -96,7 +102,6 @@ __device__ __forceinline__ void times_gamma8(const uint4 &x, const GammaSlice &g
 
 // Output stores that no kernel of this call reads back: marked non-temporal
 // so they stream to memory instead of displacing cached lines.
-typedef unsigned v4u32 __attribute__((ext_vector_type(4)));
 typedef unsigned v2u32 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void store_streaming(uint16_t *p, const uint4 &v) {
     __builtin_nontemporal_store(v4u32{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u32 *>(p));
@@ -283,7 +288,9 @@ __device__ __forceinline__ void process_row(const NormQuantParams &a, int64_t m,
 // output row is 16-byte aligned and Nkv % 8 == 0.  kRows: consecutive rows
 // per wave; all their loads are issued together, gammas once per wave.
 // kFull: Nq == 512 * kQ and Nkv == 512 * kKv (no bounds tests).
-template <int kQ, int kKv, bool kVec, int kRows, bool kFull, bool kNorm, bool kE8m0>
+// kStream: the rows are read with non-temporal loads (large M: every row is
+// read once; measured slower for a handful of rows).
+template <int kQ, int kKv, bool kVec, int kRows, bool kFull, bool kNorm, bool kE8m0, bool kStream>
 __global__ __launch_bounds__(256) void fused_dual_rmsnorm_group_quant_kernel(NormQuantParams a) {
     constexpr int kKvA = kKv > 0 ? kKv : 1;  // array extents
     const int lane = threadIdx.x & (kWave - 1);
@@ -313,12 +320,12 @@ __global__ __launch_bounds__(256) void fused_dual_rmsnorm_group_quant_kernel(Nor
         const uint16_t *qrow = a.q + m * a.q_stride;
 #pragma unroll
         for (int c = 0; c < kQ; ++c)
-            xq[r][c] = load8<kVec, kFull>(qrow, c * kChunk + lane * 8, a.Nq);
+            xq[r][c] = load8<kVec, kFull, kStream>(qrow, c * kChunk + lane * 8, a.Nq);
         if constexpr (kKv > 0) {
             const uint16_t *krow = a.kv + m * a.kv_stride;
 #pragma unroll
             for (int c = 0; c < kKv; ++c)
-                xk[r][c] = load8<kVec, kFull>(krow, c * kChunk + lane * 8, a.Nkv);
+                xk[r][c] = load8<kVec, kFull, kStream>(krow, c * kChunk + lane * 8, a.Nkv);
         }
     }
     // gammas prepared once per wave, shared by its rows
@@ -403,6 +410,9 @@ __global__ __launch_bounds__(256) void split_row_group_quant_kernel(NormQuantPar
     }
 }
 
+// rows from which the full-width variants stream their row loads
+constexpr int64_t kStreamFromRows = 1024;
+
 template <int kQ, int kKv, bool kVec, int kRows, bool kFull = false, bool kNorm = true, bool kE8m0 = false>
 hipError_t launch_variant(const NormQuantParams &p, hipStream_t stream) {
     const int64_t waves = (p.M + kRows - 1) / kRows;
@@ -410,8 +420,12 @@ hipError_t launch_variant(const NormQuantParams &p, hipStream_t stream) {
     const int64_t blocks = (waves + waves_per_block - 1) / waves_per_block;
     if (blocks > 0x7FFFFFFF)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((fused_dual_rmsnorm_group_quant_kernel<kQ, kKv, kVec, kRows, kFull, kNorm, kE8m0>),
-                       dim3(static_cast<unsigned>(blocks)), dim3(waves_per_block * kWave), 0, stream, p);
+    if (kFull && p.M >= kStreamFromRows)
+        hipLaunchKernelGGL((fused_dual_rmsnorm_group_quant_kernel<kQ, kKv, kVec, kRows, kFull, kNorm, kE8m0, kFull>),
+                           dim3(static_cast<unsigned>(blocks)), dim3(waves_per_block * kWave), 0, stream, p);
+    else
+        hipLaunchKernelGGL((fused_dual_rmsnorm_group_quant_kernel<kQ, kKv, kVec, kRows, kFull, kNorm, kE8m0, false>),
+                           dim3(static_cast<unsigned>(blocks)), dim3(waves_per_block * kWave), 0, stream, p);
     return hipGetLastError();
 }
 
