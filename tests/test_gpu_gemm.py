@@ -234,3 +234,22 @@ def test_gemm_pair_equals_two_gemms(M, N1, N2, K, seed):
             cols = (blocks[:, None] * 128 + np.arange(128)[None, :]).reshape(-1)
             ref = oracle.block_scaled_fp8_gemm(a, As.reshape(-1), False, w[cols], Bs[blocks])
             assert_gemm_close(bf16_to_f64(o)[:, cols], ref, f"{name} M{M} N{w.shape[0]} t{t}")
+
+
+def test_gemm_large_batch_generic_kernel_sampled():
+    """M = 1024 rows (beyond the decode and wide kernels: the generic one)
+    over W_b [8192, 1536], both As layouts bit-identical, sampled columns
+    against the oracle."""
+    dev = gpu_or_skip()
+    M, N, K = 1024, 8192, 1536
+    a, As, w, Bs = random_operands(M, N, K, 91)
+    r = np.random.default_rng(91)
+    blocks = np.unique(np.concatenate([[0, N // 128 - 1], r.choice(N // 128, size=2, replace=False)]))
+    cols = (blocks[:, None] * 128 + np.arange(128)[None, :]).reshape(-1)
+    ref = oracle.block_scaled_fp8_gemm(a, As.reshape(-1), False, w[cols], Bs[blocks])
+    outs = []
+    for t in (False, True):
+        out = run_gemm(a, As, w, Bs, t, dev)
+        assert_gemm_close(bf16_to_f64(out)[:, cols], ref, f"M{M} t{t}")
+        outs.append(host_bf16_bits(out))
+    assert np.array_equal(outs[0], outs[1])

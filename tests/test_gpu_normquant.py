@@ -186,3 +186,31 @@ def test_zero_rows_is_a_noop():
     gk = torch.ones(512, dtype=torch.bfloat16, device=dev)
     codes, scale, kvo = mi.mi_fused_dual_rmsnorm_group_quant(q, kv, g, gk, W.EPS, False)
     assert codes.shape == (0, 1536) and scale.shape == (0, 12) and kvo.shape == (0, 512)
+
+
+def test_largest_batch_sampled_rows():
+    """2^18 + 3 rows of the fused [M, 2048] buffer (65537 four-wave blocks,
+    streamed row loads, both layouts): every output row the oracle checks is
+    one of 512 sampled rows (first, last, random), computed on those rows
+    alone (rows are independent); the scale layout is checked through the
+    sampled rows' positions in the column-major array."""
+    dev = gpu_or_skip()
+    M = (1 << 18) + 3
+    r = np.random.default_rng(77)
+    buf = W.f32_to_bf16_bits(r.standard_normal((M, W.WIDTH), dtype=np.float32))
+    gq, gk = W.gammas()
+    d = dev_u16_as_bf16(buf, dev)
+    rows = np.unique(np.concatenate([[0, 1, M - 2, M - 1], r.choice(M, size=508, replace=False)]))
+    sub = buf[rows]
+    for t in (0, 1):
+        codes, scale, kvo = mi.mi_fused_dual_rmsnorm_group_quant(
+            d[:, :W.NQ], d[:, W.NQ:], dev_u16_as_bf16(gq, dev), dev_u16_as_bf16(gk, dev), W.EPS, t)
+        torch.cuda.synchronize()
+        ref = oracle.dual_rmsnorm_group_quant(sub[:, :W.NQ], sub[:, W.NQ:], gq, gk, W.EPS, False, want_ratio=True)
+        got_q = codes[torch.from_numpy(rows).to(dev)].cpu().numpy()
+        sc = scale[torch.from_numpy(rows).to(dev)].cpu().numpy()      # [rows, 12] logical view, either layout
+        got_kv = host_bf16_bits(kvo[torch.from_numpy(rows).to(dev)])
+        compare_normquant(got_q, sc.reshape(-1), got_kv, ref, label=f"M={M} sampled t{t}")
+        assert scale.stride() == ((1, M) if t else (12, 1))
+        del codes, scale, kvo
+        torch.cuda.empty_cache()
