@@ -6,8 +6,11 @@ One step = one pass of the whole path over one batch of synthetic input:
      [M, 1536] and kv latent [M, 512], strided split views of one [M, 2048]
      bf16 projection buffer), scales in the layout both consumers agreed on;
   2. the block-scaled FP8 GEMMs of the quantised q with W_a [24576, 1536]
-     (attention wq_b) and W_b [8192, 1536] (indexer wq_b), sharing the pair,
-     in one launch (mi_block_scaled_fp8_gemm_pair).
+     (attention wq_b) and W_b [8192, 1536] (indexer wq_b), sharing the pair;
+through mi_fused_normquant_gemm_pair (the default ``--step``): one launch of
+both for decode batches up to 16 rows, above that the norm-quant launch
+followed by one launch of both GEMMs; ``--step two-launch`` calls the two
+entry points (the other form is timed too and reported beside).
 Default M = 64 (a decode batch).  Inputs are resident in HBM before the
 timed region; every step uses the next of several buffer sets (weights,
 activations, outputs) whose total exceeds the 256 MB Infinity Cache, so the
@@ -49,6 +52,9 @@ def parse():
     ap.add_argument("--scale-layout", choices=("row", "col"), default="col")
     ap.add_argument("--weight-layout", choices=("preferred", "row", "tiled"), default="preferred",
                     help="weight byte order (preferred: what mi_preferred_weight_layout says)")
+    ap.add_argument("--step", choices=("library", "two-launch"), default="library",
+                    help="library: mi_fused_normquant_gemm_pair (one launch where the library takes one); "
+                         "two-launch: the norm-quant call, then the GEMM pair call")
     ap.add_argument("--warm", action="store_true", help="reuse one buffer set (cache-warm numbers)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="skip the M=1 / M=8192 / M=256 extras")
@@ -214,6 +220,8 @@ def build_sets(torch, np, mi, W, M, layout, wa, wb, nsets, dev, tiled):
             "gp": mi.prepare_block_scaled_fp8_gemm_pair(oq, scale, wa_c, wa_s0, oa, wb_c, wb_s0, ob),
             "ga": mi.prepare_block_scaled_fp8_gemm(oq, scale, wa_c, wa_s0, oa),
             "gb": mi.prepare_block_scaled_fp8_gemm(oq, scale, wb_c, wb_s0, ob),
+            "fs": mi.prepare_fused_normquant_gemm_pair(q, kv, gq, gk, W.EPS, layout, wa_c, wa_s0, wb_c, wb_s0,
+                                                       oq, osc, okv, oa, ob),
         })
     return sets
 
@@ -452,6 +460,22 @@ def sweep(torch, np, mi, W, wa, wb, dev, cold, tiled):
                                     "GB/s": round(per / us / 1e3, 1)}
         del g, fns
         torch.cuda.empty_cache()
+
+    # the decode step at small batches, in the form the library picks (one
+    # launch up to 16 rows) and as the two calls, back to back
+    for M in (1, 16):
+        per = algorithmic_bytes_normquant(M) + algorithmic_bytes_gemm_pair(M, W.W_A_SHAPE[0], W.W_B_SHAPE[0], W.NQ)
+        nsets = max(2, COLD_BYTES // per + 1) if cold else 1
+        sets = build_sets(torch, np, mi, W, M, 1, wa, wb, nsets, dev, tiled)
+        entry = {"launches": mi.mi_fused_normquant_gemm_pair_launches(M, W.NQ, W.NKV, W.W_A_SHAPE[0],
+                                                                      W.W_B_SHAPE[0])}
+        for name, keys in (("us", ["fs"]), ("two_launch_us", ["nq", "gp"])):
+            g = make_graph(torch, [st[k] for st in sets for k in keys])
+            entry[name] = round(time_graph(torch, g, nsets, max(1, 200 // nsets)), 3)
+            del g
+        res[f"step_M{M}"] = entry
+        del sets
+        torch.cuda.empty_cache()
     return res
 
 
@@ -508,30 +532,38 @@ def main():
 
     if args.kernel_loop:
         # profiling aid: only the named kernel, back to back over the sets
-        key = {"normquant": "nq", "gemm_pair": "gp", "gemm_a": "ga", "gemm_b": "gb"}[args.kernel_loop]
+        key = {"normquant": "nq", "gemm_pair": "gp", "gemm_a": "ga", "gemm_b": "gb",
+               "step": "fs"}[args.kernel_loop]
         fns = [s[key] for s in sets]
         us = time_eager(torch, fns, args.steps)
         print(json.dumps({"kernel_loop": args.kernel_loop, "us_per_launch": us}))
         return
 
     # ---- the timed region: K steps, graph-replayed over the buffer sets ----
-    step_fns = []
-    for s in sets:
-        step_fns += [s["nq"], s["gp"]]
-    g = make_graph(torch, step_fns)
-    replays_warm = max(1, -(-args.warmup // nsets))
-    replays = max(1, -(-args.steps // nsets))
-    steps = replays * nsets
-    for _ in range(replays_warm):
-        g.replay()
-    torch.cuda.synchronize()
-    tm = Timer(torch)
-    tm.start()
-    for _ in range(replays):
-        g.replay()
-    ms = tm.stop_ms()
-    torch.cuda.synchronize()
-    us_step = 1000.0 * ms / steps
+    def time_steps(one_launch):
+        step_fns = []
+        for s in sets:
+            step_fns += [s["fs"]] if one_launch else [s["nq"], s["gp"]]
+        g = make_graph(torch, step_fns)
+        replays_warm = max(1, -(-args.warmup // nsets))
+        replays = max(1, -(-args.steps // nsets))
+        for _ in range(replays_warm):
+            g.replay()
+        torch.cuda.synchronize()
+        tm = Timer(torch)
+        tm.start()
+        for _ in range(replays):
+            g.replay()
+        ms = tm.stop_ms()
+        torch.cuda.synchronize()
+        del g
+        return 1000.0 * ms / (replays * nsets), replays * nsets, replays_warm * nsets
+
+    launches = mi.mi_fused_normquant_gemm_pair_launches(M, W.NQ, W.NKV, W.W_A_SHAPE[0], W.W_B_SHAPE[0])
+    library = args.step == "library"
+    us_step, steps, warmup_steps = time_steps(library)
+    us_other, _, _ = time_steps(not library)
+    one_launch = library and launches == 1
 
     # ---- per-kernel average launch duration (events around back-to-back
     # launches of one kernel over the same buffer sets, same stream) ----
@@ -545,7 +577,11 @@ def main():
                                       gemm_flops(M, *W.W_A_SHAPE), "gemm_fp8_bs.hip"),
         "block_scaled_fp8_gemm_W_b": ("gb", algorithmic_bytes_gemm(M, *W.W_B_SHAPE),
                                       gemm_flops(M, *W.W_B_SHAPE), "gemm_fp8_bs.hip"),
+        "normquant_gemm_pair": ("fs", algorithmic_bytes_normquant(M) + algorithmic_bytes_gemm_pair(M, NA, NB, W.NQ),
+                                gemm_flops(M, NA + NB, W.NQ), "gemm_fp8_bs.hip"),
     }
+    if launches != 1:
+        del specs["normquant_gemm_pair"]  # the call is the two kernels above
     for name, (key, nbytes, flops, src) in specs.items():
         fns = [s[key] for s in sets]
         gk = make_graph(torch, fns)
@@ -560,7 +596,8 @@ def main():
         kernels[name] = k
     # the dominant kernel of the step (the single-consumer GEMMs are listed
     # for reference only: the step runs the pair)
-    dom = max(("fused_dual_rmsnorm_group_quant", "block_scaled_fp8_gemm_pair"), key=lambda n: kernels[n]["us"])
+    dom = ("normquant_gemm_pair" if one_launch else
+           max(("fused_dual_rmsnorm_group_quant", "block_scaled_fp8_gemm_pair"), key=lambda n: kernels[n]["us"]))
     dk = kernels[dom]
     roofline = {"bound": "hbm", "achieved": dk["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": dk["frac_hbm"], "traffic": dk["traffic"],
@@ -572,7 +609,7 @@ def main():
         "unit": "µs/call",
         "n_gpus": 1,
         "steps": steps,
-        "warmup": replays_warm * nsets,
+        "warmup": warmup_steps,
         "ms_per_step": round(us_step / 1000.0, 6),
         "higher_is_better": False,
         "scaling": "weak",
@@ -583,7 +620,12 @@ def main():
             "workload": f"mla_decode_step: fused dual RMSNorm + 1x128 FP8 group quant of M={M} tokens "
                         f"(q [M,1536] and kv [M,512] as strided views of a [M,2048] bf16 buffer), then "
                         f"block-scaled FP8 GEMMs with W_a [24576,1536] and W_b [8192,1536] sharing "
-                        f"the (q_fp8, scale) pair, both in one launch",
+                        f"the (q_fp8, scale) pair, through mi_fused_normquant_gemm_pair: "
+                        + ("all in one launch" if launches == 1 else
+                           "the norm-quant launch then one launch of both GEMMs (its form above 16 rows)"),
+            "step": args.step,
+            "launches": launches if library else 2,
+            "other_step_us": {"two-launch" if library else "library": round(us_other, 3)},
             "M": M, "scale_layout": "column-major" if layout else "row-major",
             "weight_layout": "tiled (relaid out once at load time)" if tiled else "row-major",
             "cache": "warm" if args.warm else f"cold ({nsets} rotating buffer sets, "

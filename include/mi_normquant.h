@@ -295,6 +295,48 @@ mi_status mi_block_scaled_fp8_gemm_pair_ex(
     hipStream_t stream);
 
 /*
+ * mi_fused_normquant_gemm_pair
+ *
+ * The whole decode-step hot path in one call: mi_fused_dual_rmsnorm_group_quant
+ * ([PR53540] "Purpose") followed by mi_block_scaled_fp8_gemm_pair_ex over its
+ * outputs ([D53540]: apply_pre_quantized_block_scaled_mm consumes the
+ * (q_fp8, scale) pair as produced, K = Nq, As in the layout transpose_scale
+ * chose).  All five outputs are bit-identical to those two calls'.
+ *
+ * For decode batches (M <= 16 rows of the MLA latent shape: Nq = 1536,
+ * Nkv = 512, every row slice 16-byte aligned) over wide weights (N1 + N2 >=
+ * 24576) the work is one kernel launch, whose blocks each quantise the rows
+ * they consume while their first weight loads are in flight (no hand-over
+ * between blocks); other shapes run as the two calls, which are faster
+ * there (mi_fused_normquant_gemm_pair_launches tells which).
+ *
+ * Arguments as mi_fused_dual_rmsnorm_group_quant (q ... out_kv; out_q_fp8
+ * 16-byte aligned) and mi_block_scaled_fp8_gemm_pair_ex (w_layout ...
+ * out2_bf16, N2; N1, N2 % 128 == 0).  Errors: as those two calls.
+ */
+mi_status mi_fused_normquant_gemm_pair(
+    const uint16_t *q, int64_t q_row_stride,
+    const uint16_t *kv, int64_t kv_row_stride,
+    const uint16_t *gamma_q, const uint16_t *gamma_kv,
+    float eps, int64_t M, int64_t Nq, int64_t Nkv,
+    int transpose_scale,
+    uint8_t *out_q_fp8, float *out_scale, uint16_t *out_kv,
+    int w_layout,
+    const uint8_t *w1_fp8, const float *w1_scale, uint16_t *out1_bf16, int64_t N1,
+    const uint8_t *w2_fp8, const float *w2_scale, uint16_t *out2_bf16, int64_t N2,
+    hipStream_t stream);
+
+/*
+ * mi_fused_normquant_gemm_pair_launches
+ *
+ * Kernel launches mi_fused_normquant_gemm_pair makes for these sizes on the
+ * current device when every operand meets the alignment above: 1 (one
+ * launch), 2 (the two calls), 0 for M == 0; -1 for sizes the call rejects.
+ * Host only; enqueues nothing.
+ */
+int mi_fused_normquant_gemm_pair_launches(int64_t M, int64_t Nq, int64_t Nkv, int64_t N1, int64_t N2);
+
+/*
  * e8m0 (power-of-two) scales
  *
  * [D56433] "风险与影响" item 3: weight block scales stored as e8m0

@@ -17,6 +17,8 @@ from ._binding import (  # noqa: F401
     mi_block_scaled_fp8_gemm_pair,
     mi_fused_dual_rmsnorm_group_quant,
     mi_fused_dual_rmsnorm_group_quant_e8m0,
+    mi_fused_normquant_gemm_pair,
+    mi_fused_normquant_gemm_pair_launches,
     mi_gemm_capabilities,
     mi_preferred_weight_layout,
     mi_group_quant_1x128,
@@ -27,6 +29,7 @@ from ._binding import (  # noqa: F401
     prepare_block_scaled_fp8_gemm_pair,
     prepare_fused_dual_rmsnorm_group_quant,
     prepare_fused_dual_rmsnorm_group_quant_e8m0,
+    prepare_fused_normquant_gemm_pair,
     prepare_group_quant_1x128,
     prepare_rmsnorm_group_quant,
     relayout_weight,

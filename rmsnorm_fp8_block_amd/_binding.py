@@ -32,6 +32,8 @@ EXPORTED = (
     "mi_block_scaled_fp8_gemm_pair",
     "mi_block_scaled_fp8_gemm_pair_ex",
     "mi_block_scaled_fp8_gemm_pair_e8m0",
+    "mi_fused_normquant_gemm_pair",
+    "mi_fused_normquant_gemm_pair_launches",
     "mi_gemm_capabilities",
     "mi_preferred_weight_layout",
     "mi_relayout_weight",
@@ -80,6 +82,12 @@ def lib() -> ctypes.CDLL:
         L.mi_block_scaled_fp8_gemm_ex.argtypes = [p, p, c_int, p, c_int, p, p, i64, i64, i64, p]
         L.mi_block_scaled_fp8_gemm_pair_ex.restype = c_int
         L.mi_block_scaled_fp8_gemm_pair_ex.argtypes = [p, p, c_int, c_int, p, p, p, i64, p, p, p, i64, i64, i64, p]
+        L.mi_fused_normquant_gemm_pair.restype = c_int
+        L.mi_fused_normquant_gemm_pair.argtypes = [
+            p, i64, p, i64, p, p, ctypes.c_float, i64, i64, i64, c_int, p, p, p,
+            c_int, p, p, p, i64, p, p, p, i64, p]
+        L.mi_fused_normquant_gemm_pair_launches.restype = c_int
+        L.mi_fused_normquant_gemm_pair_launches.argtypes = [i64, i64, i64, i64, i64]
         L.mi_gemm_capabilities.restype = ctypes.c_uint
         L.mi_gemm_capabilities.argtypes = []
         L.mi_preferred_weight_layout.restype = c_int
@@ -395,6 +403,67 @@ def mi_block_scaled_fp8_gemm_pair(a: torch.Tensor, a_scale: torch.Tensor, w1, w1
     return out1, out2
 
 
+def _step_operands(q, kv, gamma_q, gamma_kv, w1, w1_scale, w2, w2_scale):
+    qs = _rows(q, "q", torch.bfloat16)
+    ks = _rows(kv, "kv", torch.bfloat16)
+    M, Nq = q.shape
+    Nkv = kv.shape[1]
+    if kv.shape[0] != M:
+        raise ValueError("q and kv must have the same number of rows")
+    if gamma_q.dtype != torch.bfloat16 or gamma_kv.dtype != torch.bfloat16 or \
+            gamma_q.numel() != Nq or gamma_kv.numel() != Nkv or \
+            not (gamma_q.is_contiguous() and gamma_kv.is_contiguous()):
+        raise ValueError("gammas must be contiguous bf16 of the row widths")
+    ws = []
+    for name, w, w_scale in (("w1", w1, w1_scale), ("w2", w2, w2_scale)):
+        wd, wl, N, K = _weight_arg(w)
+        if K != Nq:
+            raise ValueError(f"{name}: K must equal the q width {Nq}")
+        if w_scale.dtype != torch.float32 or not w_scale.is_contiguous() or \
+                tuple(w_scale.shape) != (N // GROUP, K // GROUP):
+            raise ValueError(f"{name}: scale must be contiguous fp32 [N/128, K/128]")
+        ws.append((wd, wl, N))
+    if ws[0][1] != ws[1][1]:
+        raise ValueError("both weights of a pair must have the same layout")
+    return qs, ks, M, Nq, Nkv, ws
+
+
+def mi_fused_normquant_gemm_pair(q: torch.Tensor, kv: torch.Tensor, gamma_q: torch.Tensor,
+                                 gamma_kv: torch.Tensor, eps: float, transpose_scale: bool,
+                                 w1, w1_scale: torch.Tensor, w2, w2_scale: torch.Tensor,
+                                 out_q=None, out_scale=None, out_kv=None, out1=None, out2=None):
+    """The decode step on the current stream: the fused dual norm-quant of
+    (q, kv) and both block-scaled FP8 GEMMs of its output, in one launch
+    where the shape allows.  Returns ``(q_fp8, scale, kv_out, out1, out2)``,
+    bit-identical to mi_fused_dual_rmsnorm_group_quant followed by
+    mi_block_scaled_fp8_gemm_pair."""
+    qs, ks, M, Nq, Nkv, ((wd1, wl, N1), (wd2, _, N2)) = _step_operands(
+        q, kv, gamma_q, gamma_kv, w1, w1_scale, w2, w2_scale)
+    G = Nq // GROUP
+    dev = q.device
+    out_q = torch.empty((M, Nq), dtype=torch.uint8, device=dev) if out_q is None else out_q
+    out_scale = torch.empty(M * G, dtype=torch.float32, device=dev) if out_scale is None else out_scale
+    out_kv = torch.empty((M, Nkv), dtype=torch.bfloat16, device=dev) if out_kv is None else out_kv
+    if not (out_q.is_contiguous() and out_kv.is_contiguous() and out_scale.is_contiguous()):
+        raise ValueError("outputs must be contiguous")
+    if out_q.numel() < M * Nq or out_scale.numel() < M * G or out_kv.numel() < M * Nkv:
+        raise ValueError("output buffers too small")
+    out1 = _gemm_out(out1, M, N1, dev)
+    out2 = _gemm_out(out2, M, N2, dev)
+    status = lib().mi_fused_normquant_gemm_pair(
+        _ptr(q), qs, _ptr(kv), ks, _ptr(gamma_q), _ptr(gamma_kv), ctypes.c_float(eps), M, Nq, Nkv,
+        int(bool(transpose_scale)), _ptr(out_q), _ptr(out_scale), _ptr(out_kv),
+        wl, _ptr(wd1), _ptr(w1_scale), _ptr(out1), N1, _ptr(wd2), _ptr(w2_scale), _ptr(out2), N2, _stream(q))
+    _check("mi_fused_normquant_gemm_pair", status)
+    return out_q, _scale_view(out_scale, M, G, transpose_scale), out_kv, out1, out2
+
+
+def mi_fused_normquant_gemm_pair_launches(M: int, Nq: int, Nkv: int, N1: int, N2: int) -> int:
+    """Kernel launches mi_fused_normquant_gemm_pair makes for these sizes (1
+    or 2; 0 for M == 0; -1 for sizes it rejects), aligned operands assumed."""
+    return int(lib().mi_fused_normquant_gemm_pair_launches(M, Nq, Nkv, N1, N2))
+
+
 def mi_negotiate_scale_layout(consumer_wants_transposed) -> bool | None:
     """True / False when every consumer wants column-major / row-major
     scales, None when they disagree (do not share one quantised pair)."""
@@ -500,3 +569,22 @@ def prepare_block_scaled_fp8_gemm_pair(a, a_scale, w1, w1_scale, out1, w2, w2_sc
             N1, _ptr(wd2), _ptr(w2_scale), _ptr(out2), N2, M, K)
     fn = "mi_block_scaled_fp8_gemm_pair_e8m0" if a_scale.dtype in E8M0_DTYPES else "mi_block_scaled_fp8_gemm_pair_ex"
     return PreparedCall(fn, args, (a, a_scale, wd1, w1_scale, out1, wd2, w2_scale, out2), a.device)
+
+
+def prepare_fused_normquant_gemm_pair(q, kv, gamma_q, gamma_kv, eps, transpose_scale, w1, w1_scale, w2, w2_scale,
+                                      out_q, out_scale, out_kv, out1, out2) -> PreparedCall:
+    """Marshal the arguments of mi_fused_normquant_gemm_pair once (outputs
+    required)."""
+    qs, ks, M, Nq, Nkv, ((wd1, wl, N1), (wd2, _, N2)) = _step_operands(
+        q, kv, gamma_q, gamma_kv, w1, w1_scale, w2, w2_scale)
+    G = Nq // GROUP
+    if out_q.numel() < M * Nq or out_scale.numel() < M * G or out_kv.numel() < M * Nkv:
+        raise ValueError("output buffers too small")
+    if tuple(out1.shape) != (M, N1) or tuple(out2.shape) != (M, N2):
+        raise ValueError("shape mismatch")
+    args = (_ptr(q), qs, _ptr(kv), ks, _ptr(gamma_q), _ptr(gamma_kv), ctypes.c_float(eps), M, Nq, Nkv,
+            int(bool(transpose_scale)), _ptr(out_q), _ptr(out_scale), _ptr(out_kv),
+            wl, _ptr(wd1), _ptr(w1_scale), _ptr(out1), N1, _ptr(wd2), _ptr(w2_scale), _ptr(out2), N2)
+    return PreparedCall("mi_fused_normquant_gemm_pair", args,
+                        (q, kv, gamma_q, gamma_kv, wd1, w1_scale, wd2, w2_scale, out_q, out_scale, out_kv, out1, out2),
+                        q.device)

@@ -12,23 +12,26 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 
 namespace {
 
-// e8m0: scales to out_scale_e8m0 (exponent bytes), else to out_scale (fp32)
-mi_status dual_normquant(const uint16_t *q, int64_t q_row_stride, const uint16_t *kv, int64_t kv_row_stride,
-                         const uint16_t *gamma_q, const uint16_t *gamma_kv, float eps, int64_t M, int64_t Nq,
-                         int64_t Nkv, int transpose_scale, uint8_t *out_q_fp8, float *out_scale,
-                         uint8_t *out_scale_e8m0, bool e8m0, uint16_t *out_kv, hipStream_t stream) {
+// Shape, pointer and stride checks of the dual norm-quant (MI_OK with
+// *empty set for M == 0), and its kernel parameters.
+mi_status dual_params(const uint16_t *q, int64_t q_row_stride, const uint16_t *kv, int64_t kv_row_stride,
+                      const uint16_t *gamma_q, const uint16_t *gamma_kv, float eps, int64_t M, int64_t Nq,
+                      int64_t Nkv, int transpose_scale, uint8_t *out_q_fp8, float *out_scale,
+                      uint8_t *out_scale_e8m0, bool e8m0, uint16_t *out_kv, mi::NormQuantParams &p, bool &empty) {
+    empty = false;
     if (M < 0 || Nq < MI_GROUP || Nq > MI_MAX_NQ || (Nq % MI_GROUP) != 0 || Nkv < 1 ||
         Nkv > MI_MAX_NKV)
         return MI_ERR_SHAPE;
-    if (M == 0)
+    if (M == 0) {
+        empty = true;
         return MI_OK;
+    }
     if (!q || !kv || !gamma_q || !gamma_kv || !out_q_fp8 || !(e8m0 ? out_scale_e8m0 != nullptr : out_scale != nullptr) ||
         !out_kv)
         return MI_ERR_NULL;
     if (q_row_stride < Nq || kv_row_stride < Nkv)
         return MI_ERR_STRIDE;
 
-    mi::NormQuantParams p;
     p.q = q;
     p.q_stride = q_row_stride;
     p.kv = kv;
@@ -46,6 +49,20 @@ mi_status dual_normquant(const uint16_t *q, int64_t q_row_stride, const uint16_t
     p.out_scale = out_scale;
     p.out_kv = out_kv;
     p.out_scale_e8m0 = out_scale_e8m0;
+    return MI_OK;
+}
+
+// e8m0: scales to out_scale_e8m0 (exponent bytes), else to out_scale (fp32)
+mi_status dual_normquant(const uint16_t *q, int64_t q_row_stride, const uint16_t *kv, int64_t kv_row_stride,
+                         const uint16_t *gamma_q, const uint16_t *gamma_kv, float eps, int64_t M, int64_t Nq,
+                         int64_t Nkv, int transpose_scale, uint8_t *out_q_fp8, float *out_scale,
+                         uint8_t *out_scale_e8m0, bool e8m0, uint16_t *out_kv, hipStream_t stream) {
+    mi::NormQuantParams p;
+    bool empty = false;
+    const mi_status st = dual_params(q, q_row_stride, kv, kv_row_stride, gamma_q, gamma_kv, eps, M, Nq, Nkv,
+                                     transpose_scale, out_q_fp8, out_scale, out_scale_e8m0, e8m0, out_kv, p, empty);
+    if (st != MI_OK || empty)
+        return st;
     const hipError_t e = e8m0 ? mi::launch_normquant_e8m0(p, stream) : mi::launch_normquant(p, stream);
     return e == hipSuccess ? MI_OK : MI_ERR_HIP;
 }
@@ -212,6 +229,67 @@ extern "C" mi_status mi_block_scaled_fp8_gemm_pair(
     hipStream_t stream) {
     return mi_block_scaled_fp8_gemm_pair_ex(a_fp8, a_scale, a_scale_transposed, MI_WEIGHT_ROW_MAJOR, w1_fp8,
                                             w1_scale, out1_bf16, N1, w2_fp8, w2_scale, out2_bf16, N2, M, K, stream);
+}
+
+extern "C" mi_status mi_fused_normquant_gemm_pair(
+    const uint16_t *q, int64_t q_row_stride,
+    const uint16_t *kv, int64_t kv_row_stride,
+    const uint16_t *gamma_q, const uint16_t *gamma_kv,
+    float eps, int64_t M, int64_t Nq, int64_t Nkv,
+    int transpose_scale,
+    uint8_t *out_q_fp8, float *out_scale, uint16_t *out_kv,
+    int w_layout,
+    const uint8_t *w1_fp8, const float *w1_scale, uint16_t *out1_bf16, int64_t N1,
+    const uint8_t *w2_fp8, const float *w2_scale, uint16_t *out2_bf16, int64_t N2,
+    hipStream_t stream) {
+    if (w_layout != MI_WEIGHT_ROW_MAJOR && w_layout != MI_WEIGHT_TILED)
+        return MI_ERR_LAYOUT;
+    if (N1 <= 0 || N2 <= 0 || (N1 % MI_GROUP) != 0 || (N2 % MI_GROUP) != 0)
+        return MI_ERR_SHAPE;
+    mi::NormQuantParams a;
+    bool empty = false;
+    const mi_status st = dual_params(q, q_row_stride, kv, kv_row_stride, gamma_q, gamma_kv, eps, M, Nq, Nkv,
+                                     transpose_scale, out_q_fp8, out_scale, nullptr, false, out_kv, a, empty);
+    if (st != MI_OK || empty)
+        return st;
+    if (!w1_fp8 || !w1_scale || !out1_bf16 || !w2_fp8 || !w2_scale || !out2_bf16)
+        return MI_ERR_NULL;
+    if (!aligned16(out_q_fp8) || !aligned16(w1_fp8) || !aligned16(out1_bf16) || !aligned16(w2_fp8) ||
+        !aligned16(out2_bf16) || (reinterpret_cast<uintptr_t>(out_scale) & 3) ||
+        (reinterpret_cast<uintptr_t>(w1_scale) & 3) || (reinterpret_cast<uintptr_t>(w2_scale) & 3))
+        return MI_ERR_ALIGN;
+
+    mi::GemmParams p;
+    p.a = out_q_fp8;
+    p.a_scale = out_scale;
+    p.a_scale_transposed = a.transpose_scale;
+    p.w = w1_fp8;
+    p.w_scale = w1_scale;
+    p.out = out1_bf16;
+    p.M = M;
+    p.N = N1;
+    p.K = Nq;
+    p.w2 = w2_fp8;
+    p.w_scale2 = w2_scale;
+    p.out2 = out2_bf16;
+    p.N2 = N2;
+    p.w_tiled = w_layout == MI_WEIGHT_TILED ? 1 : 0;
+    hipError_t e = mi::launch_normquant_gemm_pair(a, p, stream);
+    if (e == hipErrorNotSupported) {  // two launches
+        e = mi::launch_normquant(a, stream);
+        if (e == hipSuccess)
+            e = mi::launch_block_scaled_gemm_pair(p, stream);
+    }
+    return e == hipSuccess ? MI_OK : MI_ERR_HIP;
+}
+
+extern "C" int mi_fused_normquant_gemm_pair_launches(int64_t M, int64_t Nq, int64_t Nkv, int64_t N1, int64_t N2) {
+    if (M < 0 || Nq < MI_GROUP || Nq > MI_MAX_NQ || (Nq % MI_GROUP) != 0 || Nkv < 1 || Nkv > MI_MAX_NKV ||
+        N1 <= 0 || N2 <= 0 || (N1 % MI_GROUP) != 0 || (N2 % MI_GROUP) != 0)
+        return -1;
+    if (M == 0)
+        return 0;
+    return mi::normquant_gemm_pair_one_launch(M, Nq, Nkv, N1, N2) ? 1 : 2;
 }
 
 extern "C" mi_status mi_block_scaled_fp8_gemm_e8m0(

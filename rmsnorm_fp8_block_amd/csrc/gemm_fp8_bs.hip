@@ -40,6 +40,7 @@
 
 #include "device.h"
 #include "launch.h"
+#include "normquant_row.h"
 
 namespace mi {
 namespace {
@@ -202,6 +203,22 @@ __global__ __launch_bounds__(256) void block_scaled_fp8_gemm_kernel(GemmParams p
 constexpr int kChunkRows = 64;      // activation rows the decode kernel can hold
 constexpr int kDecodeMaxRows = 32;  // batches it is used for (measured crossover)
 
+// Direct global -> LDS load of kBytes per lane (LDS address: the
+// wave-uniform base plus lane * kBytes).  The builtin takes its size only as
+// a literal constant, and is compiled for the device only: in a template the
+// compiler's host pass takes it for a substitution failure and silently
+// drops the launch stub of any kernel that reaches it.
+template <int kBytes>
+__device__ __forceinline__ void load_to_lds(const void *src, void *dst) {
+    static_assert(kBytes == 16 || kBytes == 4, "supported loads");
+#if defined(__HIP_DEVICE_COMPILE__)
+    if constexpr (kBytes == 16)
+        __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+    else
+        __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
+#endif
+}
+
 // vmcnt-only waits (gfx9 encoding: vmcnt[3:0] + vmcnt[5:4] at bits 15:14,
 // expcnt 6:4 and lgkmcnt 11:8 left at their maxima = no wait)
 template <int kVm>
@@ -326,9 +343,7 @@ __device__ __forceinline__ v8i join4(const v4u32 &lo, const v4u32 &hi) {
 }
 
 // Per-wave state of the wide kernel: load sources, accumulators and the
-// MFMA -> FMA pipeline.  Member functions instead of lambdas: the host pass
-// of the compiler drops a kernel's launch stub when the kernel calls a
-// lambda that issues direct global -> LDS loads.
+// MFMA -> FMA pipeline.
 template <int kKB, int kNS, int kMT, int kWaves, bool kE8m0>
 struct WideWave {
     using P = WidePlan<kKB, kNS, kMT, kWaves, kE8m0>;
@@ -363,7 +378,7 @@ struct WideWave {
         uint8_t *dst = lds + P::kWOff + (s % P::kRW) * P::kWStage;
 #pragma unroll
         for (int i = 0; i < P::kNW; ++i)
-            __builtin_amdgcn_global_load_lds(wbase[i] + s * w_kstride + w_off, dst + wslot[i] * P::kSlot, 16, 0, 0);
+            load_to_lds<16>(wbase[i] + s * w_kstride + w_off, dst + wslot[i] * P::kSlot);
     }
 
     __device__ __forceinline__ void issue_a(int s) {
@@ -371,14 +386,14 @@ struct WideWave {
         const uint8_t *src = a + s * kBlk;
 #pragma unroll
         for (int j = 0; j < kMT; ++j) {
-            __builtin_amdgcn_global_load_lds(src + a_off[j][0], dst + (2 * j) * P::kSlot, 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(src + a_off[j][1], dst + (2 * j + 1) * P::kSlot, 16, 0, 0);
+            load_to_lds<16>(src + a_off[j][0], dst + (2 * j) * P::kSlot);
+            load_to_lds<16>(src + a_off[j][1], dst + (2 * j + 1) * P::kSlot);
         }
         if constexpr (!kE8m0) {
             uint8_t *sdst = lds + P::kSOff + (s % P::kRA) * P::kSStage + wave * 2 * kWave * 4;
             const uint8_t *ssrc = reinterpret_cast<const uint8_t *>(a_scale + s * s_stride);
-            __builtin_amdgcn_global_load_lds(ssrc + s_off, sdst, 4, 0, 0);
-            __builtin_amdgcn_global_load_lds(bsrc + s, sdst + kWave * 4, 4, 0, 0);
+            load_to_lds<4>(ssrc + s_off, sdst);
+            load_to_lds<4>(bsrc + s, sdst + kWave * 4);
         }
     }
 
@@ -726,15 +741,12 @@ struct StreamWave {
         for (int t = 0; t < kSW; ++t)
 #pragma unroll
             for (int g = 0; g < 2; ++g)
-                __builtin_amdgcn_global_load_lds(wsrc[t] + s * w_kstride + w_off[g], dst + (2 * t + g) * P::kSlot, 16,
-                                                 0, 0);
+                load_to_lds<16>(wsrc[t] + s * w_kstride + w_off[g], dst + (2 * t + g) * P::kSlot);
     }
 
     // activation slots (all K-blocks) and As, split over the waves; slot
     // (kb, j, g) holds rows 16 j + 8 g .. + 7 of K-block kb (rows at or
-    // beyond M repeat row M - 1: their results are never stored).  A member
-    // function, not inline in the kernel: the host pass drops the launch
-    // stub of a kernel whose own body issues direct global -> LDS loads.
+    // beyond M repeat row M - 1: their results are never stored).
     __device__ __forceinline__ void issue_activations(const GemmParams &p, int wave, int64_t m0) {
         const int lrow = lane >> 3, lchunk = lane & 7;
         const int64_t M = p.M, K = p.K;
@@ -743,8 +755,7 @@ struct StreamWave {
             const int slot = (wave + kWaves * i) % P::kASlots;
             const int kb = slot / (2 * kMT), j = (slot / 2) % kMT, g = slot % 2;
             const int64_t row = min<int64_t>(m0 + 16 * j + 8 * g + lrow, M - 1);
-            __builtin_amdgcn_global_load_lds(p.a + row * K + kb * kBlk + 16 * (lchunk ^ lrow ^ g),
-                                             lds + P::kAOff + slot * P::kSlot, 16, 0, 0);
+            load_to_lds<16>(p.a + row * K + kb * kBlk + 16 * (lchunk ^ lrow ^ g), lds + P::kAOff + slot * P::kSlot);
         }
         if constexpr (!kE8m0) {
             const int64_t row = min<int64_t>(m0 + lane, M - 1);
@@ -752,7 +763,7 @@ struct StreamWave {
             for (int i = 0; i < P::kNS; ++i) {
                 const int kb = (wave + kWaves * i) % kKB;
                 const float *src = p.a_scale + (p.a_scale_transposed ? kb * M + row : row * kKB + kb);
-                __builtin_amdgcn_global_load_lds(src, lds + P::kSOff + kb * kWave * 4, 4, 0, 0);
+                load_to_lds<4>(src, lds + P::kSOff + kb * kWave * 4);
             }
         }
     }
@@ -820,6 +831,140 @@ struct StreamWave {
         if constexpr (kb + 1 < kKB)
             kblock<kb + 1>();
     }
+    // What issue_w needs for the ring of wave `wave` (owning subtiles st0 ..
+    // st0 + kSW - 1): the ring, this lane's offsets, the subtiles' sources.
+    // Subtiles past the end repeat the last (never stored).
+    __device__ __forceinline__ void setup_ring(const GemmParams &p, int wave, int64_t st0) {
+        const int64_t K = p.K;
+        const int64_t S = (p.N + p.N2) / 16;
+        lane = threadIdx.x & (kWave - 1);
+        ring = lds + P::kWOff + wave * P::kWaveRing;
+        // weight slot pairs: row-major weights in the activations' image; a
+        // tiled weight's halves are copied as they are (lane order)
+        const int lrow = lane >> 3, lchunk = lane & 7;
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+            w_off[g] = p.w_tiled ? static_cast<uint32_t>(g * 1024 + lane * 16)
+                                 : static_cast<uint32_t>((8 * g + lrow) * K + 16 * (lchunk ^ lrow ^ g));
+        w_kstride = p.w_tiled ? 16 * kBlk : kBlk;
+#pragma unroll
+        for (int t = 0; t < kSW; ++t)
+            wsrc[t] = subtile(p, min<int64_t>(st0 + t, S - 1)).w;
+    }
+
+    // Per-lane offsets, the owned subtiles' sources and block scales (and,
+    // e8m0, the activation scale bytes): plain loads, issued before any
+    // direct load of the wave.  Subtiles past the end repeat the last (never
+    // stored).
+    __device__ __forceinline__ void setup(const GemmParams &p, int wave, int64_t m0, int64_t st0) {
+        const int64_t M = p.M, K = p.K;
+        const int64_t S = (p.N + p.N2) / 16;
+        lane = threadIdx.x & (kWave - 1);
+        ring = lds + P::kWOff + wave * P::kWaveRing;
+        {
+            const int rho = lane & 15, g = rho >> 3, r = rho & 7, q = lane >> 4;
+            frag_lo = static_cast<uint32_t>(g * 1024 + r * 128 + (((2 * q) ^ (r ^ g)) * 16));
+            frag_hi = static_cast<uint32_t>(g * 1024 + r * 128 + (((2 * q + 1) ^ (r ^ g)) * 16));
+        }
+        // weight slot pairs: row-major weights in the activations' image; a
+        // tiled weight's halves are copied as they are (lane order)
+        const int lrow = lane >> 3, lchunk = lane & 7;
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+            w_off[g] = p.w_tiled ? static_cast<uint32_t>(g * 1024 + lane * 16)
+                                 : static_cast<uint32_t>((8 * g + lrow) * K + 16 * (lchunk ^ lrow ^ g));
+        w_kstride = p.w_tiled ? 16 * kBlk : kBlk;
+        wfrag_lo = p.w_tiled ? static_cast<uint32_t>(16 * lane) : frag_lo;
+        wfrag_hi = p.w_tiled ? static_cast<uint32_t>(1024 + 16 * lane) : frag_hi;
+#pragma unroll
+        for (int t = 0; t < kSW; ++t) {
+            const SubTile sub = subtile(p, min<int64_t>(st0 + t, S - 1));
+            wsrc[t] = sub.w;
+            if constexpr (kE8m0) {
+#pragma unroll
+                for (int i = 0; i < (kKB + 3) / 4; ++i)
+                    bsw[t][i] = reinterpret_cast<const uint32_t *>(sub.ws8)[i];
+            } else {
+#pragma unroll
+                for (int kb = 0; kb < kKB; ++kb)
+                    bs[t][kb] = sub.ws[kb];
+            }
+        }
+        if constexpr (kE8m0) {
+#pragma unroll
+            for (int j = 0; j < kMT; ++j) {
+                const int64_t r = min<int64_t>(m0 + 16 * j + (lane & 15), M - 1);
+#pragma unroll
+                for (int i = 0; i < (kKB + 3) / 4; ++i) {
+                    if (p.a_scale_transposed) {
+                        uint32_t v = 0;
+#pragma unroll
+                        for (int qq = 0; qq < 4; ++qq)
+                            v |= static_cast<uint32_t>(p.a_scale8[static_cast<int64_t>(4 * i + qq) * M + r])
+                                 << (8 * qq);
+                        asw[j][i] = v;
+                    } else {
+                        asw[j][i] = reinterpret_cast<const uint32_t *>(p.a_scale8 + r * kKB)[i];
+                    }
+                }
+            }
+        }
+    }
+
+    __device__ __forceinline__ void zero_acc() {
+#pragma unroll
+        for (int j = 0; j < kMT; ++j)
+#pragma unroll
+            for (int t = 0; t < kSW; ++t)
+                acc[j][t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+
+    // The K loop, entered once every wave's activation loads and this
+    // wave's weight stage 0 are in LDS, with at most weight stages
+    // 1 .. kDD - 1 of this wave still in flight (vm_wait counts only weight
+    // loads issued after the one waited for).
+    __device__ __forceinline__ void compute() {
+        read_frags<0>();
+        kblock<0>();
+        if constexpr (!kE8m0) {
+#pragma unroll
+            for (int n = kKB * kSW * kMT - kLag; n < kKB * kSW * kMT; ++n)
+                fold(n);
+        }
+    }
+
+    // output tile of this wave (16 kMT rows x 16 kSW columns) through its own
+    // ring, then 16-byte row pieces
+    __device__ __forceinline__ void store_tile(const GemmParams &p, int64_t m0, int64_t st0) {
+        const int64_t M = p.M;
+        const int64_t S = (p.N + p.N2) / 16;
+        wait_vmcnt<0>();
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        constexpr int kCols = 16 * kSW;
+        uint16_t *tile = reinterpret_cast<uint16_t *>(ring);
+#pragma unroll
+        for (int j = 0; j < kMT; ++j)
+#pragma unroll
+            for (int t = 0; t < kSW; ++t)
+                *reinterpret_cast<uint2 *>(tile + (16 * j + (lane & 15)) * kCols + 16 * t + 4 * (lane >> 4)) =
+                    make_uint2(pack2_bf16(acc[j][t][0], acc[j][t][1]), pack2_bf16(acc[j][t][2], acc[j][t][3]));
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        constexpr int kPieces = 2 * kSW;
+        constexpr int kTilePieces = 16 * kMT * kPieces;
+#pragma unroll
+        for (int i = 0; i < (kTilePieces + kWave - 1) / kWave; ++i) {
+            const int pc = lane + i * kWave;
+            if (kTilePieces % kWave != 0 && pc >= kTilePieces)
+                break;
+            const int row = pc / kPieces, col = 8 * (pc % kPieces);
+            const int64_t m = m0 + row, st = st0 + col / 16;
+            const v4u32 v = *reinterpret_cast<const v4u32 *>(tile + row * kCols + col);
+            if (m < M && st < S) {
+                const SubTile sub = subtile(p, st);
+                __builtin_nontemporal_store(v, reinterpret_cast<v4u32 *>(sub.out + m * sub.ldo + sub.n0 + col % 16));
+            }
+        }
+    }
 };
 
 template <int kKB, int kMT, int kSW, int kWaves, int kD, bool kE8m0>
@@ -829,71 +974,15 @@ __global__ __launch_bounds__(kWaves * kWave) void block_scaled_fp8_gemm_stream_k
     extern __shared__ uint4 s_dyn[];
     SW w;
     w.lds = reinterpret_cast<uint8_t *>(s_dyn);
-    w.lane = threadIdx.x & (kWave - 1);
-    const int lane = w.lane;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    w.ring = w.lds + P::kWOff + wave * P::kWaveRing;
-    const int64_t M = p.M, K = p.K;
-    const int64_t S = (p.N + p.N2) / 16;
     // block -> (weight slab, row chunk); the chunks of a slab get
     // consecutive ids, renumbered onto one XCD
     constexpr int kChunk = 16 * kMT;
-    const int nm = static_cast<int>((M + kChunk - 1) / kChunk);
+    const int nm = static_cast<int>((p.M + kChunk - 1) / kChunk);
     const int b = nm > 1 ? xcd_contiguous_block(blockIdx.x, gridDim.x) : static_cast<int>(blockIdx.x);
     const int64_t m0 = static_cast<int64_t>(b % nm) * kChunk;
     const int64_t st0 = (static_cast<int64_t>(b / nm) * kWaves + wave) * kSW;  // this wave's first subtile
-
-    {
-        const int rho = lane & 15, g = rho >> 3, r = rho & 7, q = lane >> 4;
-        w.frag_lo = static_cast<uint32_t>(g * 1024 + r * 128 + (((2 * q) ^ (r ^ g)) * 16));
-        w.frag_hi = static_cast<uint32_t>(g * 1024 + r * 128 + (((2 * q + 1) ^ (r ^ g)) * 16));
-    }
-    // weight slot pairs: row-major weights in the activations' image; a
-    // tiled weight's halves are copied as they are (lane order)
-    const int lrow = lane >> 3, lchunk = lane & 7;
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-        w.w_off[g] = p.w_tiled ? static_cast<uint32_t>(g * 1024 + lane * 16)
-                               : static_cast<uint32_t>((8 * g + lrow) * K + 16 * (lchunk ^ lrow ^ g));
-    w.w_kstride = p.w_tiled ? 16 * kBlk : kBlk;
-    w.wfrag_lo = p.w_tiled ? static_cast<uint32_t>(16 * lane) : w.frag_lo;
-    w.wfrag_hi = p.w_tiled ? static_cast<uint32_t>(1024 + 16 * lane) : w.frag_hi;
-
-    // block scales of the owned subtiles (and, e8m0, the activation scale
-    // bytes): plain loads issued before every direct load; subtiles past the
-    // end repeat the last (never stored)
-#pragma unroll
-    for (int t = 0; t < kSW; ++t) {
-        const SubTile sub = subtile(p, min<int64_t>(st0 + t, S - 1));
-        w.wsrc[t] = sub.w;
-        if constexpr (kE8m0) {
-#pragma unroll
-            for (int i = 0; i < (kKB + 3) / 4; ++i)
-                w.bsw[t][i] = reinterpret_cast<const uint32_t *>(sub.ws8)[i];
-        } else {
-#pragma unroll
-            for (int kb = 0; kb < kKB; ++kb)
-                w.bs[t][kb] = sub.ws[kb];
-        }
-    }
-    if constexpr (kE8m0) {
-#pragma unroll
-        for (int j = 0; j < kMT; ++j) {
-            const int64_t r = min<int64_t>(m0 + 16 * j + (lane & 15), M - 1);
-#pragma unroll
-            for (int i = 0; i < (kKB + 3) / 4; ++i) {
-                if (p.a_scale_transposed) {
-                    uint32_t v = 0;
-#pragma unroll
-                    for (int qq = 0; qq < 4; ++qq)
-                        v |= static_cast<uint32_t>(p.a_scale8[static_cast<int64_t>(4 * i + qq) * M + r]) << (8 * qq);
-                    w.asw[j][i] = v;
-                } else {
-                    w.asw[j][i] = reinterpret_cast<const uint32_t *>(p.a_scale8 + r * kKB)[i];
-                }
-            }
-        }
-    }
+    w.setup(p, wave, m0, st0);
     __builtin_amdgcn_sched_barrier(0);
 
     // weight stage 0 first (its HBM latency starts at once), then the
@@ -906,52 +995,14 @@ __global__ __launch_bounds__(kWaves * kWave) void block_scaled_fp8_gemm_stream_k
     for (int s = 1; s < P::kDD; ++s)
         w.issue_w(s);
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int j = 0; j < kMT; ++j)
-#pragma unroll
-        for (int t = 0; t < kSW; ++t)
-            w.acc[j][t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    w.zero_acc();
 
     // this wave's activation loads and weight stage 0 have landed (only
     // weight stages 1 .. kDD - 1 are younger); then every wave's have
     wait_vmcnt<(P::kDD - 1) * P::kNW>();
     __builtin_amdgcn_s_barrier();
-    w.template read_frags<0>();
-    w.template kblock<0>();
-    if constexpr (!kE8m0) {
-#pragma unroll
-        for (int n = kKB * kSW * kMT - SW::kLag; n < kKB * kSW * kMT; ++n)
-            w.fold(n);
-    }
-
-    // output tile of this wave (16 kMT rows x 16 kSW columns) through its own
-    // ring, then 16-byte row pieces
-    wait_vmcnt<0>();
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    constexpr int kCols = 16 * kSW;
-    uint16_t *tile = reinterpret_cast<uint16_t *>(w.ring);
-#pragma unroll
-    for (int j = 0; j < kMT; ++j)
-#pragma unroll
-        for (int t = 0; t < kSW; ++t)
-            *reinterpret_cast<uint2 *>(tile + (16 * j + (lane & 15)) * kCols + 16 * t + 4 * (lane >> 4)) =
-                make_uint2(pack2_bf16(w.acc[j][t][0], w.acc[j][t][1]), pack2_bf16(w.acc[j][t][2], w.acc[j][t][3]));
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    constexpr int kPieces = 2 * kSW;
-    constexpr int kTilePieces = 16 * kMT * kPieces;
-#pragma unroll
-    for (int i = 0; i < (kTilePieces + kWave - 1) / kWave; ++i) {
-        const int pc = lane + i * kWave;
-        if (kTilePieces % kWave != 0 && pc >= kTilePieces)
-            break;
-        const int row = pc / kPieces, col = 8 * (pc % kPieces);
-        const int64_t m = m0 + row, st = st0 + col / 16;
-        const v4u32 v = *reinterpret_cast<const v4u32 *>(tile + row * kCols + col);
-        if (m < M && st < S) {
-            const SubTile sub = subtile(p, st);
-            __builtin_nontemporal_store(v, reinterpret_cast<v4u32 *>(sub.out + m * sub.ldo + sub.n0 + col % 16));
-        }
-    }
+    w.compute();
+    w.store_tile(p, m0, st0);
 }
 
 // The dynamic-LDS limit is a per-device function attribute: remember, per
@@ -1266,6 +1317,174 @@ hipError_t launch_stream(const GemmParams &p, hipStream_t stream) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Decode step in one launch (M <= 64 rows of the MLA latent shape: Nq = K =
+// 1536, Nkv = 512): the fused dual RMSNorm + 1x128 FP8 group quantisation of
+// the rows and both consumer GEMMs of its output.
+//
+// As two launches, the GEMM's weight stream cannot start before the
+// norm-quant kernel has ended, and the norm-quant of a few rows is a memory
+// round trip of latency with the chip nearly idle.  Handing the quantised
+// rows from the blocks that make them to the blocks that use them inside one
+// launch would need a grid-wide barrier, and on this chip every hop of one
+// (a device-scope atomic or a poll) is a memory round trip of about a
+// microsecond, several of them in a row.  Instead every block of the stream
+// kernel quantises all M rows itself, straight into the LDS image the
+// stream kernel would have loaded (the rows are L2 hits after the first
+// block of an XCD; the VALU work is M rows per block):
+//  - wave kWaves of the block (one extra wave) issues the first kDD stages
+//    of every compute wave's weight ring, so the weight stream starts at
+//    once, and the compute waves' own loads of the rows never queue behind
+//    those direct loads in their vmcnt order;
+//  - compute wave w quantises rows w, w + kWaves, ... (the norm-quant
+//    kernel's arithmetic, so codes and scales are bit-identical) into the
+//    activation slots and the scale area; block b also writes row b's
+//    outputs (codes, scales, kv) to memory with the norm-quant kernel's own
+//    per-row code;
+//  - one barrier, then the stream kernel's K loop and output stores
+//    unchanged (the compute waves have no direct loads in flight).
+// The results are bit-identical to the norm-quant kernel followed by the
+// stream kernel.
+// ---------------------------------------------------------------------------
+
+// Batches the one-launch step takes: each block quantises every row itself,
+// so its VALU and L2 work grows with M; measured, the one launch is ahead of
+// the two up to 16 rows (M = 1: 11.0 against 13.5 us, M = 16: 12.7 against
+// 14.5 us), even at 32 and behind at 64 (23.4 against 16.7 us).
+constexpr int kStepMaxRows = 16;
+
+// Row m of the MLA latent shape (Nq = 1536, Nkv = 512, 16-byte aligned
+// slices) to memory: the norm-quant kernel's loads and per-row code.
+__device__ __forceinline__ void normquant_row_mla(const NormQuantParams &a, int64_t m, int lane) {
+    constexpr int kQ = 3;
+    uint4 gq_raw[kQ], gk_raw[1], xq[kQ], xk[1];
+#pragma unroll
+    for (int c = 0; c < kQ; ++c)
+        gq_raw[c] = row::load8<true, true>(a.gamma_q, c * row::kChunk + lane * 8, a.Nq);
+    gk_raw[0] = row::load8<true, true>(a.gamma_kv, lane * 8, a.Nkv);
+    const uint16_t *qrow = a.q + m * a.q_stride;
+#pragma unroll
+    for (int c = 0; c < kQ; ++c)
+        xq[c] = row::load8<true, true>(qrow, c * row::kChunk + lane * 8, a.Nq);
+    xk[0] = row::load8<true, true>(a.kv + m * a.kv_stride, lane * 8, a.Nkv);
+    row::GammaSlice gq[kQ], gk[1];
+#pragma unroll
+    for (int c = 0; c < kQ; ++c)
+        gq[c] = row::prepare_gamma(gq_raw[c]);
+    gk[0] = row::prepare_gamma(gk_raw[0]);
+    row::process_row<kQ, 1, true, true, true, false>(a, m, lane, xq, xk, gq, gk);
+}
+
+// Rows of q quantised into the stream kernel's LDS image (row r of wave w
+// is row w + r * kWaves, all of a wave's row loads issued first): codes of
+// row m, K-block kb, 16-byte piece c16 at slot (kb * kMT + m / 16) * 2 +
+// (m / 8) % 2, byte 128 (m % 8) + 16 (c16 ^ (m % 8) ^ g) (g: that slot's
+// parity); its scale at the scale area + kb * 256 + 4 m.
+template <int kMT, int kWaves, int kAOff, int kSOff>
+struct RowsToLds {
+    static constexpr int kQ = 3;  // 512-element chunks of a 1536 row
+    static constexpr int kRowsMax = (16 * kMT + kWaves - 1) / kWaves;
+
+    __device__ __forceinline__ static void store(uint8_t *lds, const NormQuantParams &a, int m, int lane,
+                                                 const uint4 (&x)[kQ], const row::GammaSlice (&g)[kQ]) {
+        const float rq = row::row_rstd<kQ>(x, a.inv_nq, a.eps);
+        const int r = m & 7, gp = (m >> 3) & 1, j = m >> 4;
+#pragma unroll
+        for (int c = 0; c < kQ; ++c) {
+            const row::ChunkCodes q = row::quantise_chunk<true, false>(x[c], g[c], rq);
+            const int col = c * row::kChunk + lane * 8;
+            const int kb = col / kBlk, c16 = (col % kBlk) / 16, half = (col % 16) / 8;
+            const int slot = (kb * kMT + j) * 2 + gp;
+            *reinterpret_cast<uint2 *>(lds + kAOff + slot * 1024 + 128 * r + 16 * (c16 ^ r ^ gp) + 8 * half) =
+                make_uint2(q.lo, q.hi);
+            if ((lane & 15) == 0)
+                reinterpret_cast<float *>(lds + kSOff)[kb * kWave + m] = q.s;
+        }
+    }
+
+    __device__ __forceinline__ static void run(uint8_t *lds, const NormQuantParams &a, int wave, int lane) {
+        uint4 graw[kQ], x[kRowsMax][kQ];
+#pragma unroll
+        for (int c = 0; c < kQ; ++c)
+            graw[c] = row::load8<true, true>(a.gamma_q, c * row::kChunk + lane * 8, a.Nq);
+        const int M = static_cast<int>(a.M);
+#pragma unroll
+        for (int i = 0; i < kRowsMax; ++i) {
+            const int m = wave + i * kWaves;
+            if (m < M) {
+                const uint16_t *qrow = a.q + m * a.q_stride;
+#pragma unroll
+                for (int c = 0; c < kQ; ++c)
+                    x[i][c] = row::load8<true, true>(qrow, c * row::kChunk + lane * 8, a.Nq);
+            }
+        }
+        row::GammaSlice g[kQ];
+#pragma unroll
+        for (int c = 0; c < kQ; ++c)
+            g[c] = row::prepare_gamma(graw[c]);
+#pragma unroll
+        for (int i = 0; i < kRowsMax; ++i) {
+            if (wave + i * kWaves >= M)
+                break;  // uniform
+            store(lds, a, wave + i * kWaves, lane, x[i], g);
+        }
+    }
+};
+
+template <int kKB, int kMT, int kSW, int kWaves, int kD>
+__global__ __launch_bounds__((kWaves + 1) * kWave) void normquant_gemm_pair_kernel(NormQuantParams a,
+                                                                                   GemmParams p) {
+    using SW = StreamWave<kKB, kMT, kSW, kWaves, kD, false>;
+    using P = typename SW::P;
+    extern __shared__ uint4 s_dyn[];
+    SW w;
+    w.lds = reinterpret_cast<uint8_t *>(s_dyn);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lane = threadIdx.x & (kWave - 1);
+    if (wave == kWaves) {
+        // the first ring stages of every compute wave; landed before the
+        // barrier, so the compute waves start with nothing in flight
+#pragma unroll
+        for (int cw = 0; cw < kWaves; ++cw) {
+            w.setup_ring(p, cw, (static_cast<int64_t>(blockIdx.x) * kWaves + cw) * kSW);
+#pragma unroll
+            for (int s = 0; s < P::kDD; ++s)
+                w.issue_w(s);
+        }
+        wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        return;
+    }
+    const int64_t st0 = (static_cast<int64_t>(blockIdx.x) * kWaves + wave) * kSW;  // one row chunk: m0 = 0
+    w.setup(p, wave, 0, st0);
+    if (blockIdx.x < a.M && wave == 0)
+        normquant_row_mla(a, blockIdx.x, lane);
+    RowsToLds<kMT, kWaves, P::kAOff, P::kSOff>::run(w.lds, a, wave, lane);
+    w.zero_acc();
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS writes are done
+    __builtin_amdgcn_s_barrier();
+    w.compute();
+    w.store_tile(p, 0, st0);
+}
+
+template <int kMT, int kWaves>
+hipError_t launch_normquant_gemm_pair_mt(const NormQuantParams &a, const GemmParams &p, hipStream_t stream) {
+    constexpr int kKB = 12, kSW = 2;
+    constexpr int kD = stream_depth<kKB, kMT, kSW, kWaves, false>();
+    using P = StreamPlan<kKB, kMT, kSW, kWaves, kD, false>;
+    const int64_t per_block = kWaves * kSW;
+    const int64_t blocks = ((p.N + p.N2) / 16 + per_block - 1) / per_block;
+    if (blocks > 0x7FFFFFFF)
+        return hipErrorInvalidValue;
+    auto kern = normquant_gemm_pair_kernel<kKB, kMT, kSW, kWaves, kD>;
+    static std::atomic<uint64_t> lds_set{0};
+    const hipError_t e = allow_dynamic_lds(kern, P::kLds, lds_set);
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3((kWaves + 1) * kWave), P::kLds, stream, a, p);
+    return hipGetLastError();
+}
+
 template <int kKB, int kNS, int kMT, int kWaves, bool kE8m0>
 hipError_t launch_wide_scaled(const GemmParams &p, hipStream_t stream) {
     using P = WidePlan<kKB, kNS, kMT, kWaves, kE8m0>;
@@ -1431,6 +1650,30 @@ hipError_t launch_weight_relayout(const uint8_t *src, uint8_t *dst, int64_t N, i
     hipLaunchKernelGGL(weight_relayout_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, src, dst,
                        N, K, to_tiled ? 1 : 0);
     return hipGetLastError();
+}
+
+bool normquant_gemm_pair_one_launch(int64_t M, int64_t Nq, int64_t Nkv, int64_t N1, int64_t N2) {
+    // the MLA latent shape, a block for every row (block b writes row b's
+    // outputs), and the stream kernel's shapes (at least 6 weight subtiles
+    // per CU)
+    if (Nq != 1536 || Nkv != 512 || M < 1 || M > kStepMaxRows || N1 <= 0 || N2 <= 0)
+        return false;
+    const int64_t S = (N1 + N2) / 16, cus = device_cu_count();
+    const int64_t per_cu = (S + cus - 1) / cus;
+    return per_cu >= 6 && M <= S / (2 * (per_cu <= 6 ? 3 : 4));
+}
+
+hipError_t launch_normquant_gemm_pair(const NormQuantParams &a, const GemmParams &p, hipStream_t stream) {
+    const auto al16 = [](const void *q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+    const bool vec = al16(a.q) && al16(a.kv) && al16(a.gamma_q) && al16(a.gamma_kv) && al16(a.out_kv) &&
+                     al16(a.out_q) && (a.q_stride % 8) == 0 && (a.kv_stride % 8) == 0;
+    if (!vec || a.out_scale_e8m0 || p.scale_e8m0 || p.K != a.Nq || p.M != a.M ||
+        !normquant_gemm_pair_one_launch(a.M, a.Nq, a.Nkv, p.N, p.N2))
+        return hipErrorNotSupported;
+    const int64_t S = (p.N + p.N2) / 16, cus = device_cu_count();
+    const bool three = (S + cus - 1) / cus <= 6;
+    static_assert(kStepMaxRows <= 16, "one 16-row chunk per block");
+    return three ? launch_normquant_gemm_pair_mt<1, 3>(a, p, stream) : launch_normquant_gemm_pair_mt<1, 4>(a, p, stream);
 }
 
 hipError_t launch_block_scaled_gemm_pair(const GemmParams &p, hipStream_t stream) {

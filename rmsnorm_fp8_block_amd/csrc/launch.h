@@ -70,5 +70,11 @@ hipError_t launch_group_quant(const NormQuantParams &p, bool normalize, hipStrea
 hipError_t launch_block_scaled_gemm(const GemmParams &p, hipStream_t stream);
 // both consumers (p.N2 > 0) in one launch where the shape allows, else two
 hipError_t launch_block_scaled_gemm_pair(const GemmParams &p, hipStream_t stream);
+// the decode step in one launch: the norm-quant of a.M rows and both
+// consumer GEMMs of its outputs (p.a / p.a_scale are a.out_q / a.out_scale).
+// hipErrorNotSupported where the shapes or alignment do not allow it.
+hipError_t launch_normquant_gemm_pair(const NormQuantParams &a, const GemmParams &p, hipStream_t stream);
+// whether launch_normquant_gemm_pair takes these sizes (alignment aside)
+bool normquant_gemm_pair_one_launch(int64_t M, int64_t Nq, int64_t Nkv, int64_t N1, int64_t N2);
 
 }  // namespace mi
