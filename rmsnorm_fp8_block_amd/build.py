@@ -29,10 +29,7 @@ FLAGS = [
 ]
 # device code: matrix-core results in ordinary VGPRs (the scale FMAs read
 # them right away; the accumulation-register form costs a copy per value)
-# the atomic optimizer is off: it would turn the one-lane arrival add of the
-# decode step's grid barrier into a wave-wide form that waits for the add's
-# return at once, before the weight loads behind it are issued
-HIP_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form=true", "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
+HIP_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]
 
 
 def _compile(src: str) -> str:
