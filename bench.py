@@ -41,6 +41,10 @@ FP8_MFMA_PEAK_TFLOPS = 5000.0  # MI355X dense FP8
 MALL_BYTES = 256 << 20
 COLD_BYTES = 1 << 30           # rotate buffer sets past 1 GiB
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# the sources each kernel's code comes from (their hash keys the committed
+# counter figures)
+NORMQUANT_SOURCES = ("normquant.hip", "normquant_row.h", "device.h", "launch.h")
+GEMM_SOURCES = ("gemm_fp8_bs.hip", "normquant_row.h", "device.h", "launch.h")
 
 
 def parse():
@@ -110,10 +114,10 @@ def measured_traffic(kernel, sha, M):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    e = t.get(kernel)
-    if not e or e.get("source_sha") != sha or e.get("M") != M:
-        return None
-    return e.get("bytes_per_launch")
+    for key, e in t.items():
+        if e.get("kernel", key) == kernel and e.get("M") == M and e.get("source_sha") == sha:
+            return e.get("bytes_per_launch")
+    return None
 
 
 class Timer:
@@ -570,15 +574,15 @@ def main():
     kernels = {}
     NA, NB = W.W_A_SHAPE[0], W.W_B_SHAPE[0]
     specs = {
-        "fused_dual_rmsnorm_group_quant": ("nq", algorithmic_bytes_normquant(M), None, "normquant.hip"),
+        "fused_dual_rmsnorm_group_quant": ("nq", algorithmic_bytes_normquant(M), None, NORMQUANT_SOURCES),
         "block_scaled_fp8_gemm_pair": ("gp", algorithmic_bytes_gemm_pair(M, NA, NB, W.NQ),
-                                       gemm_flops(M, NA + NB, W.NQ), "gemm_fp8_bs.hip"),
+                                       gemm_flops(M, NA + NB, W.NQ), GEMM_SOURCES),
         "block_scaled_fp8_gemm_W_a": ("ga", algorithmic_bytes_gemm(M, *W.W_A_SHAPE),
-                                      gemm_flops(M, *W.W_A_SHAPE), "gemm_fp8_bs.hip"),
+                                      gemm_flops(M, *W.W_A_SHAPE), GEMM_SOURCES),
         "block_scaled_fp8_gemm_W_b": ("gb", algorithmic_bytes_gemm(M, *W.W_B_SHAPE),
-                                      gemm_flops(M, *W.W_B_SHAPE), "gemm_fp8_bs.hip"),
+                                      gemm_flops(M, *W.W_B_SHAPE), GEMM_SOURCES),
         "normquant_gemm_pair": ("fs", algorithmic_bytes_normquant(M) + algorithmic_bytes_gemm_pair(M, NA, NB, W.NQ),
-                                gemm_flops(M, NA + NB, W.NQ), "gemm_fp8_bs.hip"),
+                                gemm_flops(M, NA + NB, W.NQ), GEMM_SOURCES),
     }
     if launches != 1:
         del specs["normquant_gemm_pair"]  # the call is the two kernels above
@@ -589,7 +593,7 @@ def main():
         del gk
         gbs = nbytes / us / 1e3
         k = {"us": round(us, 3), "bytes": nbytes, "GB/s": round(gbs, 1),
-             "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "source_sha": source_sha(src)}
+             "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "source_sha": source_sha(*src)}
         if flops:
             k["TFLOP/s"] = round(flops / us / 1e6, 2)
         k["traffic"] = measured_traffic(name, k["source_sha"], M)
