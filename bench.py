@@ -465,15 +465,15 @@ def sweep(torch, np, mi, W, wa, wb, dev, cold, tiled):
         del g, fns
         torch.cuda.empty_cache()
 
-    # the decode step at small batches, in the form the library picks (one
+    # the step at other batch sizes, in the form the library picks (one
     # launch up to 16 rows) and as the two calls, back to back
-    for M in (1, 16):
+    for M in (1, 16, 256):
         per = algorithmic_bytes_normquant(M) + algorithmic_bytes_gemm_pair(M, W.W_A_SHAPE[0], W.W_B_SHAPE[0], W.NQ)
         nsets = max(2, COLD_BYTES // per + 1) if cold else 1
         sets = build_sets(torch, np, mi, W, M, 1, wa, wb, nsets, dev, tiled)
         entry = {"launches": mi.mi_fused_normquant_gemm_pair_launches(M, W.NQ, W.NKV, W.W_A_SHAPE[0],
                                                                       W.W_B_SHAPE[0])}
-        for name, keys in (("us", ["fs"]), ("two_launch_us", ["nq", "gp"])):
+        for name, keys in (("us", ["fs"]), ("two_calls_us", ["nq", "gp"])):
             g = make_graph(torch, [st[k] for st in sets for k in keys])
             entry[name] = round(time_graph(torch, g, nsets, max(1, 200 // nsets)), 3)
             del g
@@ -628,7 +628,7 @@ def main():
                         + ("all in one launch" if launches == 1 else
                            "the norm-quant launch then one launch of both GEMMs (its form above 16 rows)"),
             "step": args.step,
-            "launches": launches if library else 2,
+            "launches": launches if library else 2,   # kernel launches per step
             "other_step_us": {"two-launch" if library else "library": round(us_other, 3)},
             "M": M, "scale_layout": "column-major" if layout else "row-major",
             "weight_layout": "tiled (relaid out once at load time)" if tiled else "row-major",

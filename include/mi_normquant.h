@@ -331,8 +331,9 @@ mi_status mi_fused_normquant_gemm_pair(
  *
  * Kernel launches mi_fused_normquant_gemm_pair makes for these sizes on the
  * current device when every operand meets the alignment above: 1 (one
- * launch), 2 (the two calls), 0 for M == 0; -1 for sizes the call rejects.
- * Host only; enqueues nothing.
+ * launch), else the norm-quant's one plus the pair's (one up to 64 rows with
+ * K / 128 in {4, 8, 12, 16}, else two); 0 for M == 0; -1 for sizes the call
+ * rejects.  Host only; enqueues nothing.
  */
 int mi_fused_normquant_gemm_pair_launches(int64_t M, int64_t Nq, int64_t Nkv, int64_t N1, int64_t N2);
 

@@ -460,7 +460,8 @@ def mi_fused_normquant_gemm_pair(q: torch.Tensor, kv: torch.Tensor, gamma_q: tor
 
 def mi_fused_normquant_gemm_pair_launches(M: int, Nq: int, Nkv: int, N1: int, N2: int) -> int:
     """Kernel launches mi_fused_normquant_gemm_pair makes for these sizes (1
-    or 2; 0 for M == 0; -1 for sizes it rejects), aligned operands assumed."""
+    for one launch, else 2 or 3: the norm-quant's plus the pair's; 0 for
+    M == 0; -1 for sizes it rejects), aligned operands assumed."""
     return int(lib().mi_fused_normquant_gemm_pair_launches(M, Nq, Nkv, N1, N2))
 
 

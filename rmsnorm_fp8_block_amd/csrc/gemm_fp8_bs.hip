@@ -1676,6 +1676,11 @@ hipError_t launch_normquant_gemm_pair(const NormQuantParams &a, const GemmParams
     return three ? launch_normquant_gemm_pair_mt<1, 3>(a, p, stream) : launch_normquant_gemm_pair_mt<1, 4>(a, p, stream);
 }
 
+int gemm_pair_launches(int64_t M, int64_t K) {
+    const int64_t kb = K / kBlk;
+    return M <= kChunkRows && (kb == 4 || kb == 8 || kb == 12 || kb == 16) ? 1 : 2;
+}
+
 hipError_t launch_block_scaled_gemm_pair(const GemmParams &p, hipStream_t stream) {
     // decode batches: one launch over the subtiles of both weights, sharing
     // the activation tile (the stream kernel where the weights are wide

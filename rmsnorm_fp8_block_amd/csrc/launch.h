@@ -70,6 +70,8 @@ hipError_t launch_group_quant(const NormQuantParams &p, bool normalize, hipStrea
 hipError_t launch_block_scaled_gemm(const GemmParams &p, hipStream_t stream);
 // both consumers (p.N2 > 0) in one launch where the shape allows, else two
 hipError_t launch_block_scaled_gemm_pair(const GemmParams &p, hipStream_t stream);
+// kernel launches launch_block_scaled_gemm_pair makes for M rows, depth K
+int gemm_pair_launches(int64_t M, int64_t K);
 // the decode step in one launch: the norm-quant of a.M rows and both
 // consumer GEMMs of its outputs (p.a / p.a_scale are a.out_q / a.out_scale).
 // hipErrorNotSupported where the shapes or alignment do not allow it.

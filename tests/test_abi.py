@@ -270,14 +270,17 @@ def test_fused_step_validation(L):
 
 def test_fused_step_launch_count(L):
     """One launch for decode batches of the MLA shape over wide weights (the
-    CU count taken as 256 where no GPU is visible), two otherwise; 0 / -1 as
-    documented."""
+    CU count taken as 256 where no GPU is visible); otherwise the
+    norm-quant's launch plus the pair's one or two; 0 / -1 as documented."""
     f = mi.mi_fused_normquant_gemm_pair_launches
     assert f(0, 1536, 512, 24576, 8192) == 0
     for M in (1, 7, 16):
         assert f(M, 1536, 512, 24576, 8192) == 1, M
-    for M in (17, 64, 256):
-        assert f(M, 1536, 512, 24576, 8192) == 2, M
+    for M in (17, 64):
+        assert f(M, 1536, 512, 24576, 8192) == 2, M   # norm-quant, then the pair in one launch
+    assert f(65, 1536, 512, 24576, 8192) == 3         # ... the pair as two GEMMs
+    assert f(256, 1536, 512, 24576, 8192) == 3
+    assert f(64, 2560, 512, 24576, 8192) == 3         # K / 128 = 20: two GEMMs
     assert f(1, 1536, 512, 3072, 1024) == 2       # narrow weights
     assert f(1, 1024, 512, 24576, 8192) == 2      # other latent width
     assert f(1, 1536, 448, 24576, 8192) == 2
