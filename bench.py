@@ -247,8 +247,8 @@ def cpu_baseline(np, W, M, layout, wa, wb):
 
 
 def sweep(torch, np, mi, W, wa, wb, dev, cold, tiled):
-    """Extra figures of the metric: norm-quant at M=1 (us/call) and M=8192
-    (GB/s, both layouts); the single-input quantisations at [8192, 1536] and
+    """Extra figures of the metric: norm-quant at M=1 and M=256 (us/call) and
+    M=8192 (GB/s, both layouts); the single-input quantisations at [8192, 1536] and
     [256, 7168] (GB/s); the GEMMs at M=256 (TFLOP/s, % of FP8 MFMA peak) and at
     tensor-parallel shard shapes, with the step's weight layout (``tiled``),
     and the pair / W_a in both layouts, timed back to back."""
@@ -271,6 +271,22 @@ def sweep(torch, np, mi, W, wa, wb, dev, cold, tiled):
     res["normquant_M1_us_per_call_graph"] = round(time_graph(torch, g, len(fns), 20), 3)
     res["normquant_M1_us_per_call_eager"] = round(time_eager(torch, fns, 2000), 3)
     del g, fns
+    # M = 256 (a batch of 256 tokens: the outlier workload's rows),
+    # column-major scales, many buffer sets in one graph
+    case = W.outlier_stress(256)
+    b256 = bf16_dev(torch, np, np.concatenate([case.q, case.kv], axis=1), dev)
+    fns = []
+    for i in range(32):
+        b = b256 if i == 0 else b256.clone()
+        fns.append(mi.prepare_fused_dual_rmsnorm_group_quant(
+            b[:, :W.NQ], b[:, W.NQ:], gq, gk, W.EPS, True,
+            torch.empty((256, 1536), dtype=torch.uint8, device=dev),
+            torch.empty(256 * 12, dtype=torch.float32, device=dev),
+            torch.empty((256, 512), dtype=torch.bfloat16, device=dev)))
+    g = make_graph(torch, fns)
+    us = time_graph(torch, g, len(fns), 20)
+    res["normquant_M256_col"] = {"us": round(us, 3), "GB/s": round(algorithmic_bytes_normquant(256) / us / 1e3, 1)}
+    del g, fns, b256
     # M = 8192 prefill, both layouts
     pre = W.prefill(8192)
     bufp = bf16_dev(torch, np, pre.buffer, dev)
