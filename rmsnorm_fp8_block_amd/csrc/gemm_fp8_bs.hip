@@ -208,14 +208,18 @@ constexpr int kDecodeMaxRows = 32;  // batches it is used for (measured crossove
 // a literal constant, and is compiled for the device only: in a template the
 // compiler's host pass takes it for a substitution failure and silently
 // drops the launch stub of any kernel that reaches it.
+// A 1-byte load writes its byte zero-extended to a dword per lane (LDS
+// address: base + lane * 4).
 template <int kBytes>
 __device__ __forceinline__ void load_to_lds(const void *src, void *dst) {
-    static_assert(kBytes == 16 || kBytes == 4, "supported loads");
+    static_assert(kBytes == 16 || kBytes == 4 || kBytes == 1, "supported loads");
 #if defined(__HIP_DEVICE_COMPILE__)
     if constexpr (kBytes == 16)
         __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
-    else
+    else if constexpr (kBytes == 4)
         __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
+    else
+        __builtin_amdgcn_global_load_lds(src, dst, 1, 0, 0);
 #endif
 }
 
@@ -686,12 +690,12 @@ struct StreamPlan {
     static constexpr int kSlot = 1024;
     static constexpr int kASlots = kKB * kMT * 2;                        // activation slots, all K
     static constexpr int kNA = (kASlots + kWaves - 1) / kWaves;          // per wave (spares repeat a slot)
-    static constexpr int kNS = kE8m0 ? 0 : (kKB + kWaves - 1) / kWaves;  // As loads per wave (one per K-block)
+    static constexpr int kNS = (kKB + kWaves - 1) / kWaves;              // As loads per wave (one per K-block)
     static constexpr int kNW = 2 * kSW;                                  // weight loads per wave per K-block
     static constexpr int kDD = kD < kKB ? kD : kKB;                      // ring depth actually used
     static constexpr int kAOff = 0;
     static constexpr int kSOff = kAOff + kASlots * kSlot;
-    static constexpr int kWOff = kSOff + (kE8m0 ? 0 : kKB * kWave * 4);
+    static constexpr int kWOff = kSOff + kKB * kWave * 4;               // As: a dword per row (e8m0: its byte)
     static constexpr int kWaveRing = kDD * kSW * 2 * kSlot;
     static constexpr int kLds = kWOff + kWaves * kWaveRing;
     static_assert(kLds <= 160 * 1024, "LDS per CU");
@@ -728,11 +732,11 @@ struct StreamWave {
     v4f part[kRing];
     float scl[kRing];
     float bs[kSW][kKB];                  // fp32 weight block scales (uniform)
-    uint32_t asw[kMT][(kKB + 3) / 4];    // e8m0: this lane's activation rows
     uint32_t bsw[kSW][(kKB + 3) / 4];    // e8m0: weight scale bytes (uniform)
 
     v8i af[2][kMT];
     float asv[2][kMT];
+    uint32_t asb[2][kMT];  // e8m0: activation scale bytes of this lane's rows
     v8i wfs[2][kSW];
 
     __device__ __forceinline__ void issue_w(int s) {
@@ -757,14 +761,15 @@ struct StreamWave {
             const int64_t row = min<int64_t>(m0 + 16 * j + 8 * g + lrow, M - 1);
             load_to_lds<16>(p.a + row * K + kb * kBlk + 16 * (lchunk ^ lrow ^ g), lds + P::kAOff + slot * P::kSlot);
         }
-        if constexpr (!kE8m0) {
-            const int64_t row = min<int64_t>(m0 + lane, M - 1);
+        const int64_t row = min<int64_t>(m0 + lane, M - 1);
 #pragma unroll
-            for (int i = 0; i < P::kNS; ++i) {
-                const int kb = (wave + kWaves * i) % kKB;
-                const float *src = p.a_scale + (p.a_scale_transposed ? kb * M + row : row * kKB + kb);
-                load_to_lds<4>(src, lds + P::kSOff + kb * kWave * 4);
-            }
+        for (int i = 0; i < P::kNS; ++i) {
+            const int kb = (wave + kWaves * i) % kKB;
+            const int64_t at = p.a_scale_transposed ? kb * M + row : row * kKB + kb;
+            if constexpr (kE8m0)
+                load_to_lds<1>(p.a_scale8 + at, lds + P::kSOff + kb * kWave * 4);
+            else
+                load_to_lds<4>(p.a_scale + at, lds + P::kSOff + kb * kWave * 4);
         }
     }
 
@@ -783,7 +788,9 @@ struct StreamWave {
             const uint8_t *sl = lds + P::kAOff + (st * kMT + j) * 2 * P::kSlot;
             af[b][j] = join4(*reinterpret_cast<const v4u32 *>(sl + frag_lo),
                              *reinterpret_cast<const v4u32 *>(sl + frag_hi));
-            if constexpr (!kE8m0)
+            if constexpr (kE8m0)
+                asb[b][j] = reinterpret_cast<const uint32_t *>(lds + P::kSOff)[st * kWave + 16 * j + (lane & 15)];
+            else
                 asv[b][j] = reinterpret_cast<const float *>(lds + P::kSOff)[st * kWave + 16 * j + (lane & 15)];
         }
         const uint8_t *ws = ring + (st % P::kDD) * kSW * 2 * P::kSlot;
@@ -811,7 +818,7 @@ struct StreamWave {
 #pragma unroll
                 for (int j = 0; j < kMT; ++j)
                     acc[j][t] = mfma_e4m3_16x16x128_scaled(wfs[b][t], af[b][j], acc[j][t], (bsw[t][wd] >> sh) & 0xFFu,
-                                                           (asw[j][wd] >> sh) & 0xFFu);
+                                                           asb[b][j]);
         } else {
 #pragma unroll
             for (int t = 0; t < kSW; ++t) {
@@ -852,12 +859,11 @@ struct StreamWave {
             wsrc[t] = subtile(p, min<int64_t>(st0 + t, S - 1)).w;
     }
 
-    // Per-lane offsets, the owned subtiles' sources and block scales (and,
-    // e8m0, the activation scale bytes): plain loads, issued before any
-    // direct load of the wave.  Subtiles past the end repeat the last (never
-    // stored).
+    // Per-lane offsets, the owned subtiles' sources and block scales (scalar
+    // loads).  Subtiles past the end repeat the last (never stored).
     __device__ __forceinline__ void setup(const GemmParams &p, int wave, int64_t m0, int64_t st0) {
-        const int64_t M = p.M, K = p.K;
+        const int64_t K = p.K;
+        (void)m0;
         const int64_t S = (p.N + p.N2) / 16;
         lane = threadIdx.x & (kWave - 1);
         ring = lds + P::kWOff + wave * P::kWaveRing;
@@ -888,25 +894,6 @@ struct StreamWave {
 #pragma unroll
                 for (int kb = 0; kb < kKB; ++kb)
                     bs[t][kb] = sub.ws[kb];
-            }
-        }
-        if constexpr (kE8m0) {
-#pragma unroll
-            for (int j = 0; j < kMT; ++j) {
-                const int64_t r = min<int64_t>(m0 + 16 * j + (lane & 15), M - 1);
-#pragma unroll
-                for (int i = 0; i < (kKB + 3) / 4; ++i) {
-                    if (p.a_scale_transposed) {
-                        uint32_t v = 0;
-#pragma unroll
-                        for (int qq = 0; qq < 4; ++qq)
-                            v |= static_cast<uint32_t>(p.a_scale8[static_cast<int64_t>(4 * i + qq) * M + r])
-                                 << (8 * qq);
-                        asw[j][i] = v;
-                    } else {
-                        asw[j][i] = reinterpret_cast<const uint32_t *>(p.a_scale8 + r * kKB)[i];
-                    }
-                }
             }
         }
     }
@@ -1244,7 +1231,7 @@ hipError_t launch_decode_kb(const GemmParams &p, hipStream_t stream) {
 // activation tile allows, at most 6 K-blocks
 template <int kKB, int kMT, int kSW, int kWaves, bool kE8m0>
 constexpr int stream_depth() {
-    constexpr int fixed = kKB * kMT * 2 * 1024 + (kE8m0 ? 0 : kKB * kWave * 4);
+    constexpr int fixed = kKB * kMT * 2 * 1024 + kKB * kWave * 4;
     constexpr int d = (160 * 1024 - fixed) / (kWaves * kSW * 2 * 1024);
     return d < 6 ? d : 6;
 }
