@@ -290,7 +290,9 @@ struct WidePlan {
     static constexpr int kSlot = 1024;                         // 8 rows x 128 bytes
     static constexpr int kWStage = kNS * 2 * kSlot;            // weight bytes per K-block
     static constexpr int kAStage = kWaves * kMT * 2 * kSlot;   // activation bytes per K-block
-    static constexpr int kSStage = kE8m0 ? 0 : kWaves * 2 * kWave * 4;  // per wave: As (one per lane), Bs
+    // per wave: As (a dword per lane; e8m0: its byte, zero-extended) and,
+    // with fp32 scales, Bs
+    static constexpr int kSStage = kWaves * (kE8m0 ? 1 : 2) * kWave * 4;
     static constexpr int kRA = cmin(kKB, 3);                   // activation stages
     // weight stages: as many as the rest of the 160 KB allows, up to 6
     static constexpr int kRW = cmin(kKB, cmin(6, (160 * 1024 - kRA * (kAStage + kSStage)) / kWStage));
@@ -298,7 +300,7 @@ struct WidePlan {
     // the extra loads repeat a slot of the same row half (same bytes to the
     // same place: harmless, and every wave then counts the same loads)
     static constexpr int kNW = (2 * kNS + kWaves - 1) / kWaves;
-    static constexpr int kNA = 2 * kMT + (kE8m0 ? 0 : 2);      // activation, As and Bs loads
+    static constexpr int kNA = 2 * kMT + (kE8m0 ? 1 : 2);      // activation, As and (fp32) Bs loads
     static constexpr int kWOff = 0;
     static constexpr int kAOff = kWOff + kRW * kWStage;
     static constexpr int kSOff = kAOff + kRA * kAStage;
@@ -365,17 +367,17 @@ struct WideWave {
     uint32_t a_off[kMT][2];        // per lane: m-tile j, row half g
     uint32_t frag_lo, frag_hi;     // per lane: LDS offsets of its fragment halves inside a 2 KB tile
     uint32_t wfrag_lo, wfrag_hi;   // the same for weight tiles (tiled weights: lane order)
-    const float *a_scale;
-    int64_t s_stride;  // As elements between K-blocks
+    static constexpr int kSBytes = kE8m0 ? 1 : 4;  // bytes per As element
+    const uint8_t *a_scale;
+    int64_t s_stride;  // As bytes between K-blocks
     uint32_t s_off;
     const float *bsrc;  // per lane: block-scale row of subtile lane (lanes >= kNS repeat the last)
 
     v4f acc[kMT][kNS];
     v4f part[kRing];   // MFMA n -> part[n % kRing]
     float scl[kRing];  // its As * Bs
-    // e8m0: scale bytes of every K-block, 4 per word (loaded once):
-    // asw: this lane's activation row of m-tile j; bsw: subtile t (uniform)
-    uint32_t asw[kMT][(kKB + 3) / 4];
+    // e8m0: weight scale bytes of every K-block, 4 per word, of subtile t
+    // (uniform, loaded once)
     uint32_t bsw[kNS][(kKB + 3) / 4];
 
     __device__ __forceinline__ void issue_w(int s) {
@@ -393,9 +395,11 @@ struct WideWave {
             load_to_lds<16>(src + a_off[j][0], dst + (2 * j) * P::kSlot);
             load_to_lds<16>(src + a_off[j][1], dst + (2 * j + 1) * P::kSlot);
         }
-        if constexpr (!kE8m0) {
-            uint8_t *sdst = lds + P::kSOff + (s % P::kRA) * P::kSStage + wave * 2 * kWave * 4;
-            const uint8_t *ssrc = reinterpret_cast<const uint8_t *>(a_scale + s * s_stride);
+        uint8_t *sdst = lds + P::kSOff + (s % P::kRA) * P::kSStage + wave * (kE8m0 ? 1 : 2) * kWave * 4;
+        const uint8_t *ssrc = a_scale + s * s_stride;
+        if constexpr (kE8m0) {
+            load_to_lds<1>(ssrc + s_off, sdst);
+        } else {
             load_to_lds<4>(ssrc + s_off, sdst);
             load_to_lds<4>(bsrc + s, sdst + kWave * 4);
         }
@@ -429,6 +433,7 @@ struct WideWave {
     // so LDS latency hides behind a whole K-block of matrix-core work.
     v8i af[2][kMT];
     float asv[2][kMT];
+    uint32_t asb[2][kMT];  // e8m0: activation scale bytes of this lane's rows
     v8i wfs[2][kNS];
     float bss[2][kNS];
 
@@ -448,12 +453,14 @@ struct WideWave {
         const uint8_t *ws = lds + P::kWOff + (st % P::kRW) * P::kWStage;
         const uint8_t *as = lds + P::kAOff + (st % P::kRA) * P::kAStage + wave * kMT * 2 * P::kSlot;
         const float *ss = reinterpret_cast<const float *>(lds + P::kSOff + (st % P::kRA) * P::kSStage) +
-                          wave * 2 * kWave;
+                          wave * (kE8m0 ? 1 : 2) * kWave;
 #pragma unroll
         for (int j = 0; j < kMT; ++j) {
             af[b][j] = join4(*reinterpret_cast<const v4u32 *>(as + (2 * j) * P::kSlot + frag_lo),
                              *reinterpret_cast<const v4u32 *>(as + (2 * j) * P::kSlot + frag_hi));
-            if constexpr (!kE8m0)
+            if constexpr (kE8m0)
+                asb[b][j] = reinterpret_cast<const uint32_t *>(ss)[16 * j + (lane & 15)];
+            else
                 asv[b][j] = ss[16 * j + (lane & 15)];
         }
 #pragma unroll
@@ -487,7 +494,7 @@ struct WideWave {
 #pragma unroll
                 for (int j = 0; j < kMT; ++j)
                     acc[j][t] = mfma_e4m3_16x16x128_scaled(wfs[b][t], af[b][j], acc[j][t], (bsw[t][wd] >> sh) & 0xFFu,
-                                                           (asw[j][wd] >> sh) & 0xFFu);
+                                                           asb[b][j]);
         } else {
 #pragma unroll
         for (int t = 0; t < kNS; ++t) {
@@ -577,34 +584,17 @@ __global__ __launch_bounds__(kWaves * kWave) void block_scaled_fp8_gemm_wide_ker
         }
     // lane l: As of row m_base + l (rows past this wave's or past M repeat)
     const int64_t srow = min<int64_t>(m_base + min(lane, 16 * kMT - 1), M - 1);
-    w.a_scale = p.a_scale;
-    w.s_off = static_cast<uint32_t>(4 * (p.a_scale_transposed ? srow : srow * kKB));
-    w.s_stride = p.a_scale_transposed ? M : 1;
+    w.a_scale = kE8m0 ? p.a_scale8 : reinterpret_cast<const uint8_t *>(p.a_scale);
+    w.s_off = static_cast<uint32_t>(W::kSBytes * (p.a_scale_transposed ? srow : srow * kKB));
+    w.s_stride = W::kSBytes * (p.a_scale_transposed ? M : 1);
     // lane t < kNS: the 128x128 block-scale row of subtile t (other lanes
     // repeat the last subtile)
     w.bsrc = subtile(p, min<int64_t>(st0 + min(lane, kNS - 1), S - 1)).ws;
 
     if constexpr (kE8m0) {
-        // every K-block's scale bytes into registers, before the rings start
-        // (these loads are older than every ring load, so each ring wait
-        // also covers them)
+        // the weight scale bytes of every K-block (uniform: scalar loads);
+        // the activation scale bytes ride in the scale stages
         constexpr int kWords = (kKB + 3) / 4;
-#pragma unroll
-        for (int j = 0; j < kMT; ++j) {
-            const int64_t r = min<int64_t>(m_base + 16 * j + (lane & 15), M - 1);
-#pragma unroll
-            for (int i = 0; i < kWords; ++i) {
-                if (p.a_scale_transposed) {
-                    uint32_t v = 0;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        v |= static_cast<uint32_t>(p.a_scale8[static_cast<int64_t>(4 * i + q) * M + r]) << (8 * q);
-                    w.asw[j][i] = v;
-                } else {
-                    w.asw[j][i] = reinterpret_cast<const uint32_t *>(p.a_scale8 + r * kKB)[i];
-                }
-            }
-        }
 #pragma unroll
         for (int t = 0; t < kNS; ++t) {
             const uint32_t *src =
