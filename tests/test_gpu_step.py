@@ -187,3 +187,34 @@ def test_step_graph_replays(weights):
         got = (outs[0], outs[1].view(12, M).T, outs[2], outs[3], outs[4])
         torch.cuda.synchronize()
         assert_same(got, want, f"replay {i}")
+
+
+def test_step_unaligned_views_take_two_launches(weights):
+    """q and kv as views of a [16, 2049] buffer one element in (rows and
+    slices not 16-byte aligned): the call takes the two launches (whose
+    kernels handle any alignment) and equals the two calls."""
+    dev = gpu_or_skip()
+    M = 16
+    r = np.random.default_rng(81)
+    buf = dev_u16_as_bf16(W.f32_to_bf16_bits(r.standard_normal((M, 2049), dtype=np.float32)), dev)
+    q, kv = buf[:, 1:1537], buf[:, 1537:]
+    gq, gk = (dev_u16_as_bf16(g, dev) for g in W.gammas())
+    wa, wb = weights["W_a"], weights["W_b"]
+    for t in (0, 1):
+        args = (wa["tiled"], wa["scale"], wb["tiled"], wb["scale"])
+        got = mi.mi_fused_normquant_gemm_pair(q, kv, gq, gk, W.EPS, t, *args)
+        want = two_calls(q, kv, gq, gk, t, *args)
+        torch.cuda.synchronize()
+        assert_same(got, want, f"unaligned t{t}")
+
+
+def test_step_zero_rows(weights):
+    dev = gpu_or_skip()
+    q = torch.zeros((0, 1536), dtype=torch.bfloat16, device=dev)
+    kv = torch.zeros((0, 512), dtype=torch.bfloat16, device=dev)
+    gq, gk = (dev_u16_as_bf16(g, dev) for g in W.gammas())
+    wa, wb = weights["W_a"], weights["W_b"]
+    codes, scale, kvo, o1, o2 = mi.mi_fused_normquant_gemm_pair(q, kv, gq, gk, W.EPS, True, wa["tiled"], wa["scale"],
+                                                                wb["tiled"], wb["scale"])
+    assert codes.shape == (0, 1536) and scale.shape == (0, 12) and kvo.shape == (0, 512)
+    assert o1.shape == (0, 24576) and o2.shape == (0, 8192)
