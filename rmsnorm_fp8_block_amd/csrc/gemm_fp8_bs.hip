@@ -851,9 +851,8 @@ struct StreamWave {
 
     // Per-lane offsets, the owned subtiles' sources and block scales (scalar
     // loads).  Subtiles past the end repeat the last (never stored).
-    __device__ __forceinline__ void setup(const GemmParams &p, int wave, int64_t m0, int64_t st0) {
+    __device__ __forceinline__ void setup(const GemmParams &p, int wave, int64_t st0) {
         const int64_t K = p.K;
-        (void)m0;
         const int64_t S = (p.N + p.N2) / 16;
         lane = threadIdx.x & (kWave - 1);
         ring = lds + P::kWOff + wave * P::kWaveRing;
@@ -959,7 +958,7 @@ __global__ __launch_bounds__(kWaves * kWave) void block_scaled_fp8_gemm_stream_k
     const int b = nm > 1 ? xcd_contiguous_block(blockIdx.x, gridDim.x) : static_cast<int>(blockIdx.x);
     const int64_t m0 = static_cast<int64_t>(b % nm) * kChunk;
     const int64_t st0 = (static_cast<int64_t>(b / nm) * kWaves + wave) * kSW;  // this wave's first subtile
-    w.setup(p, wave, m0, st0);
+    w.setup(p, wave, st0);
     __builtin_amdgcn_sched_barrier(0);
 
     // weight stage 0 first (its HBM latency starts at once), then the
@@ -1433,7 +1432,7 @@ __global__ __launch_bounds__((kWaves + 1) * kWave) void normquant_gemm_pair_kern
         return;
     }
     const int64_t st0 = (static_cast<int64_t>(blockIdx.x) * kWaves + wave) * kSW;  // one row chunk: m0 = 0
-    w.setup(p, wave, 0, st0);
+    w.setup(p, wave, st0);
     if (blockIdx.x < a.M && wave == 0)
         normquant_row_mla(a, blockIdx.x, lane);
     RowsToLds<kMT, kWaves, P::kAOff, P::kSOff>::run(w.lds, a, wave, lane);
