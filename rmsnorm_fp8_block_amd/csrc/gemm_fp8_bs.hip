@@ -1000,17 +1000,17 @@ hipError_t allow_dynamic_lds(Kern kern, size_t lds, std::atomic<uint64_t> &done)
 }
 
 int device_cu_count() {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[64] = {};  // per device; calls may come from several host threads
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
         return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
             n = 256;
-        cached[dev] = n;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
 }
 
 // ---------------------------------------------------------------------------
