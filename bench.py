@@ -437,6 +437,37 @@ def sweep(torch, np, mi, W, wa, wb, dev, cold, tiled):
                             "frac_hbm": round(pb / us / 1e3 / HBM_PEAK_GBS, 4)}
     del g, step_fns, pair_fns
     torch.cuda.empty_cache()
+    # ... and at M = 16 through the one-call step (one launch) and as the two calls
+    M = 16
+    case = W.producer_activations(M)
+    buf0 = bf16_dev(torch, np, case.buffer, dev)
+    per = algorithmic_bytes_normquant(M) - 3 * M * 12 + algorithmic_bytes_gemm_pair(M, NA, NB, 1536) - \
+        3 * (M * 12 + (NA + NB) // 128 * 12)
+    nsets = max(2, COLD_BYTES // per + 1) if cold else 1
+    one_fns, two_fns = [], []
+    for i in range(nsets):
+        b = buf0 if i == 0 else buf0.clone()
+        oq = torch.empty((M, W.NQ), dtype=torch.uint8, device=dev)
+        osc = torch.empty(M * 12, dtype=torch.uint8, device=dev)
+        okv = torch.empty((M, W.NKV), dtype=torch.bfloat16, device=dev)
+        wac = eac0 if i == 0 else copy_weight(eac0)
+        wbc = ebc0 if i == 0 else copy_weight(ebc0)
+        oa = torch.empty((M, NA), dtype=torch.bfloat16, device=dev)
+        ob = torch.empty((M, NB), dtype=torch.bfloat16, device=dev)
+        one_fns.append(mi.prepare_fused_normquant_gemm_pair(b[:, :W.NQ], b[:, W.NQ:], gq, gk, W.EPS, True, wac, eas,
+                                                            wbc, ebs, oq, osc, okv, oa, ob))
+        two_fns += [mi.prepare_fused_dual_rmsnorm_group_quant_e8m0(b[:, :W.NQ], b[:, W.NQ:], gq, gk, W.EPS, True,
+                                                                   oq, osc, okv),
+                    mi.prepare_block_scaled_fp8_gemm_pair(oq, osc.as_strided((M, 12), (1, M)), wac, eas, oa, wbc,
+                                                          ebs, ob)]
+    entry = {"launches": mi.mi_fused_normquant_gemm_pair_launches(M, W.NQ, W.NKV, NA, NB)}
+    for name, fns in (("us", one_fns), ("two_calls_us", two_fns)):
+        g = make_graph(torch, fns)
+        entry[name] = round(time_graph(torch, g, nsets, max(1, 200 // nsets)), 3)
+        del g
+    res["e8m0_step_M16"] = entry
+    del one_fns, two_fns
+    torch.cuda.empty_cache()
     M = 256
     a = torch.randint(0, 0x78, (M, 1536), dtype=torch.uint8, device=dev)
     asc = torch.randint(118, 127, (12, M), dtype=torch.uint8, device=dev).T

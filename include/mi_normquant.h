@@ -396,6 +396,28 @@ mi_status mi_block_scaled_fp8_gemm_pair_e8m0(
     hipStream_t stream);
 
 /*
+ * mi_fused_normquant_gemm_pair_e8m0: mi_fused_normquant_gemm_pair with e8m0
+ * scales on both sides: the step of mi_fused_dual_rmsnorm_group_quant_e8m0
+ * followed by mi_block_scaled_fp8_gemm_pair_e8m0 over its outputs (the
+ * exponent bytes written to out_scale_e8m0 are the GEMM's As).  All five
+ * outputs are bit-identical to those two calls', and the launch count is
+ * the one mi_fused_normquant_gemm_pair_launches gives.  out_scale_e8m0 and
+ * w*_scale_e8m0 4-byte aligned; other arguments and errors as
+ * mi_fused_normquant_gemm_pair.
+ */
+mi_status mi_fused_normquant_gemm_pair_e8m0(
+    const uint16_t *q, int64_t q_row_stride,
+    const uint16_t *kv, int64_t kv_row_stride,
+    const uint16_t *gamma_q, const uint16_t *gamma_kv,
+    float eps, int64_t M, int64_t Nq, int64_t Nkv,
+    int transpose_scale,
+    uint8_t *out_q_fp8, uint8_t *out_scale_e8m0, uint16_t *out_kv,
+    int w_layout,
+    const uint8_t *w1_fp8, const uint8_t *w1_scale_e8m0, uint16_t *out1_bf16, int64_t N1,
+    const uint8_t *w2_fp8, const uint8_t *w2_scale_e8m0, uint16_t *out2_bf16, int64_t N2,
+    hipStream_t stream);
+
+/*
  * mi_negotiate_scale_layout
  *
  * [D56433] item 4: the producer writes one scale buffer for several

@@ -33,6 +33,7 @@ EXPORTED = (
     "mi_block_scaled_fp8_gemm_pair_ex",
     "mi_block_scaled_fp8_gemm_pair_e8m0",
     "mi_fused_normquant_gemm_pair",
+    "mi_fused_normquant_gemm_pair_e8m0",
     "mi_fused_normquant_gemm_pair_launches",
     "mi_gemm_capabilities",
     "mi_preferred_weight_layout",
@@ -86,6 +87,8 @@ def lib() -> ctypes.CDLL:
         L.mi_fused_normquant_gemm_pair.argtypes = [
             p, i64, p, i64, p, p, ctypes.c_float, i64, i64, i64, c_int, p, p, p,
             c_int, p, p, p, i64, p, p, p, i64, p]
+        L.mi_fused_normquant_gemm_pair_e8m0.restype = c_int
+        L.mi_fused_normquant_gemm_pair_e8m0.argtypes = L.mi_fused_normquant_gemm_pair.argtypes
         L.mi_fused_normquant_gemm_pair_launches.restype = c_int
         L.mi_fused_normquant_gemm_pair_launches.argtypes = [i64, i64, i64, i64, i64]
         L.mi_gemm_capabilities.restype = ctypes.c_uint
@@ -414,18 +417,20 @@ def _step_operands(q, kv, gamma_q, gamma_kv, w1, w1_scale, w2, w2_scale):
             gamma_q.numel() != Nq or gamma_kv.numel() != Nkv or \
             not (gamma_q.is_contiguous() and gamma_kv.is_contiguous()):
         raise ValueError("gammas must be contiguous bf16 of the row widths")
+    e8m0 = w1_scale.dtype in E8M0_DTYPES
     ws = []
     for name, w, w_scale in (("w1", w1, w1_scale), ("w2", w2, w2_scale)):
         wd, wl, N, K = _weight_arg(w)
         if K != Nq:
             raise ValueError(f"{name}: K must equal the q width {Nq}")
-        if w_scale.dtype != torch.float32 or not w_scale.is_contiguous() or \
-                tuple(w_scale.shape) != (N // GROUP, K // GROUP):
-            raise ValueError(f"{name}: scale must be contiguous fp32 [N/128, K/128]")
-        ws.append((wd, wl, N))
+        ok_dtype = (w_scale.dtype in E8M0_DTYPES) if e8m0 else w_scale.dtype == torch.float32
+        if not ok_dtype or not w_scale.is_contiguous() or tuple(w_scale.shape) != (N // GROUP, K // GROUP):
+            raise ValueError(f"{name}: scale must be contiguous {'e8m0' if e8m0 else 'fp32'} [N/128, K/128]"
+                             " (both weights' scales of one type)")
+        ws.append((wd, wl, N, w_scale if not e8m0 else _u8(w_scale)))
     if ws[0][1] != ws[1][1]:
         raise ValueError("both weights of a pair must have the same layout")
-    return qs, ks, M, Nq, Nkv, ws
+    return qs, ks, M, Nq, Nkv, e8m0, ws
 
 
 def mi_fused_normquant_gemm_pair(q: torch.Tensor, kv: torch.Tensor, gamma_q: torch.Tensor,
@@ -436,13 +441,20 @@ def mi_fused_normquant_gemm_pair(q: torch.Tensor, kv: torch.Tensor, gamma_q: tor
     (q, kv) and both block-scaled FP8 GEMMs of its output, in one launch
     where the shape allows.  Returns ``(q_fp8, scale, kv_out, out1, out2)``,
     bit-identical to mi_fused_dual_rmsnorm_group_quant followed by
-    mi_block_scaled_fp8_gemm_pair."""
-    qs, ks, M, Nq, Nkv, ((wd1, wl, N1), (wd2, _, N2)) = _step_operands(
+    mi_block_scaled_fp8_gemm_pair.  With e8m0 weight scales (uint8 /
+    float8_e8m0fnu) the step is the e8m0 one
+    (mi_fused_dual_rmsnorm_group_quant_e8m0, then the e8m0 pair) and
+    ``scale`` holds exponent bytes."""
+    qs, ks, M, Nq, Nkv, e8m0, ((wd1, wl, N1, ws1), (wd2, _, N2, ws2)) = _step_operands(
         q, kv, gamma_q, gamma_kv, w1, w1_scale, w2, w2_scale)
     G = Nq // GROUP
     dev = q.device
+    sdt = torch.uint8 if e8m0 else torch.float32
     out_q = torch.empty((M, Nq), dtype=torch.uint8, device=dev) if out_q is None else out_q
-    out_scale = torch.empty(M * G, dtype=torch.float32, device=dev) if out_scale is None else out_scale
+    out_scale = torch.empty(M * G, dtype=sdt, device=dev) if out_scale is None else out_scale
+    if (out_scale.dtype in E8M0_DTYPES) != e8m0 or (not e8m0 and out_scale.dtype != torch.float32):
+        raise ValueError("out_scale must have the weight scales' type")
+    out_scale = _u8(out_scale) if e8m0 else out_scale
     out_kv = torch.empty((M, Nkv), dtype=torch.bfloat16, device=dev) if out_kv is None else out_kv
     if not (out_q.is_contiguous() and out_kv.is_contiguous() and out_scale.is_contiguous()):
         raise ValueError("outputs must be contiguous")
@@ -450,11 +462,12 @@ def mi_fused_normquant_gemm_pair(q: torch.Tensor, kv: torch.Tensor, gamma_q: tor
         raise ValueError("output buffers too small")
     out1 = _gemm_out(out1, M, N1, dev)
     out2 = _gemm_out(out2, M, N2, dev)
-    status = lib().mi_fused_normquant_gemm_pair(
+    fn = "mi_fused_normquant_gemm_pair_e8m0" if e8m0 else "mi_fused_normquant_gemm_pair"
+    status = getattr(lib(), fn)(
         _ptr(q), qs, _ptr(kv), ks, _ptr(gamma_q), _ptr(gamma_kv), ctypes.c_float(eps), M, Nq, Nkv,
         int(bool(transpose_scale)), _ptr(out_q), _ptr(out_scale), _ptr(out_kv),
-        wl, _ptr(wd1), _ptr(w1_scale), _ptr(out1), N1, _ptr(wd2), _ptr(w2_scale), _ptr(out2), N2, _stream(q))
-    _check("mi_fused_normquant_gemm_pair", status)
+        wl, _ptr(wd1), _ptr(ws1), _ptr(out1), N1, _ptr(wd2), _ptr(ws2), _ptr(out2), N2, _stream(q))
+    _check(fn, status)
     return out_q, _scale_view(out_scale, M, G, transpose_scale), out_kv, out1, out2
 
 
@@ -574,18 +587,22 @@ def prepare_block_scaled_fp8_gemm_pair(a, a_scale, w1, w1_scale, out1, w2, w2_sc
 
 def prepare_fused_normquant_gemm_pair(q, kv, gamma_q, gamma_kv, eps, transpose_scale, w1, w1_scale, w2, w2_scale,
                                       out_q, out_scale, out_kv, out1, out2) -> PreparedCall:
-    """Marshal the arguments of mi_fused_normquant_gemm_pair once (outputs
-    required)."""
-    qs, ks, M, Nq, Nkv, ((wd1, wl, N1), (wd2, _, N2)) = _step_operands(
+    """Marshal the arguments of mi_fused_normquant_gemm_pair (or its e8m0
+    form, chosen by the weight scales' type) once (outputs required)."""
+    qs, ks, M, Nq, Nkv, e8m0, ((wd1, wl, N1, ws1), (wd2, _, N2, ws2)) = _step_operands(
         q, kv, gamma_q, gamma_kv, w1, w1_scale, w2, w2_scale)
     G = Nq // GROUP
+    if (out_scale.dtype in E8M0_DTYPES) != e8m0:
+        raise ValueError("out_scale must have the weight scales' type")
+    out_scale = _u8(out_scale) if e8m0 else out_scale
     if out_q.numel() < M * Nq or out_scale.numel() < M * G or out_kv.numel() < M * Nkv:
         raise ValueError("output buffers too small")
     if tuple(out1.shape) != (M, N1) or tuple(out2.shape) != (M, N2):
         raise ValueError("shape mismatch")
     args = (_ptr(q), qs, _ptr(kv), ks, _ptr(gamma_q), _ptr(gamma_kv), ctypes.c_float(eps), M, Nq, Nkv,
             int(bool(transpose_scale)), _ptr(out_q), _ptr(out_scale), _ptr(out_kv),
-            wl, _ptr(wd1), _ptr(w1_scale), _ptr(out1), N1, _ptr(wd2), _ptr(w2_scale), _ptr(out2), N2)
-    return PreparedCall("mi_fused_normquant_gemm_pair", args,
-                        (q, kv, gamma_q, gamma_kv, wd1, w1_scale, wd2, w2_scale, out_q, out_scale, out_kv, out1, out2),
+            wl, _ptr(wd1), _ptr(ws1), _ptr(out1), N1, _ptr(wd2), _ptr(ws2), _ptr(out2), N2)
+    fn = "mi_fused_normquant_gemm_pair_e8m0" if e8m0 else "mi_fused_normquant_gemm_pair"
+    return PreparedCall(fn, args,
+                        (q, kv, gamma_q, gamma_kv, wd1, ws1, wd2, ws2, out_q, out_scale, out_kv, out1, out2),
                         q.device)

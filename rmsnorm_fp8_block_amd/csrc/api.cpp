@@ -231,6 +231,70 @@ extern "C" mi_status mi_block_scaled_fp8_gemm_pair(
                                             w1_scale, out1_bf16, N1, w2_fp8, w2_scale, out2_bf16, N2, M, K, stream);
 }
 
+namespace {
+
+// the whole step; e8m0 selects exponent-byte scales on both sides (out_scale_e8m0, w*_scale8),
+// else fp32 scales (out_scale, w*_scale)
+mi_status fused_step(const uint16_t *q, int64_t q_row_stride, const uint16_t *kv, int64_t kv_row_stride,
+                     const uint16_t *gamma_q, const uint16_t *gamma_kv, float eps, int64_t M, int64_t Nq,
+                     int64_t Nkv, int transpose_scale, uint8_t *out_q_fp8, float *out_scale,
+                     uint8_t *out_scale_e8m0, bool e8m0, uint16_t *out_kv, int w_layout, const uint8_t *w1_fp8,
+                     const float *w1_scale, const uint8_t *w1_scale8, uint16_t *out1_bf16, int64_t N1,
+                     const uint8_t *w2_fp8, const float *w2_scale, const uint8_t *w2_scale8, uint16_t *out2_bf16,
+                     int64_t N2, hipStream_t stream) {
+    if (w_layout != MI_WEIGHT_ROW_MAJOR && w_layout != MI_WEIGHT_TILED)
+        return MI_ERR_LAYOUT;
+    if (N1 <= 0 || N2 <= 0 || (N1 % MI_GROUP) != 0 || (N2 % MI_GROUP) != 0)
+        return MI_ERR_SHAPE;
+    mi::NormQuantParams a;
+    bool empty = false;
+    const mi_status st = dual_params(q, q_row_stride, kv, kv_row_stride, gamma_q, gamma_kv, eps, M, Nq, Nkv,
+                                     transpose_scale, out_q_fp8, out_scale, out_scale_e8m0, e8m0, out_kv, a, empty);
+    if (st != MI_OK || empty)
+        return st;
+    const void *ws1 = e8m0 ? static_cast<const void *>(w1_scale8) : static_cast<const void *>(w1_scale);
+    const void *ws2 = e8m0 ? static_cast<const void *>(w2_scale8) : static_cast<const void *>(w2_scale);
+    const void *as = e8m0 ? static_cast<const void *>(out_scale_e8m0) : static_cast<const void *>(out_scale);
+    if (!w1_fp8 || !ws1 || !out1_bf16 || !w2_fp8 || !ws2 || !out2_bf16)
+        return MI_ERR_NULL;
+    if (!aligned16(out_q_fp8) || !aligned16(w1_fp8) || !aligned16(out1_bf16) || !aligned16(w2_fp8) ||
+        !aligned16(out2_bf16) || (reinterpret_cast<uintptr_t>(as) & 3) || (reinterpret_cast<uintptr_t>(ws1) & 3) ||
+        (reinterpret_cast<uintptr_t>(ws2) & 3))
+        return MI_ERR_ALIGN;
+
+    mi::GemmParams p = {};
+    p.a = out_q_fp8;
+    p.a_scale_transposed = a.transpose_scale;
+    p.w = w1_fp8;
+    p.out = out1_bf16;
+    p.M = M;
+    p.N = N1;
+    p.K = Nq;
+    p.w2 = w2_fp8;
+    p.out2 = out2_bf16;
+    p.N2 = N2;
+    p.w_tiled = w_layout == MI_WEIGHT_TILED ? 1 : 0;
+    if (e8m0) {
+        p.scale_e8m0 = 1;
+        p.a_scale8 = out_scale_e8m0;
+        p.w_scale8 = w1_scale8;
+        p.w_scale8_2 = w2_scale8;
+    } else {
+        p.a_scale = out_scale;
+        p.w_scale = w1_scale;
+        p.w_scale2 = w2_scale;
+    }
+    hipError_t e = mi::launch_normquant_gemm_pair(a, p, stream);
+    if (e == hipErrorNotSupported) {  // two launches
+        e = e8m0 ? mi::launch_normquant_e8m0(a, stream) : mi::launch_normquant(a, stream);
+        if (e == hipSuccess)
+            e = mi::launch_block_scaled_gemm_pair(p, stream);
+    }
+    return e == hipSuccess ? MI_OK : MI_ERR_HIP;
+}
+
+}  // namespace
+
 extern "C" mi_status mi_fused_normquant_gemm_pair(
     const uint16_t *q, int64_t q_row_stride,
     const uint16_t *kv, int64_t kv_row_stride,
@@ -242,45 +306,25 @@ extern "C" mi_status mi_fused_normquant_gemm_pair(
     const uint8_t *w1_fp8, const float *w1_scale, uint16_t *out1_bf16, int64_t N1,
     const uint8_t *w2_fp8, const float *w2_scale, uint16_t *out2_bf16, int64_t N2,
     hipStream_t stream) {
-    if (w_layout != MI_WEIGHT_ROW_MAJOR && w_layout != MI_WEIGHT_TILED)
-        return MI_ERR_LAYOUT;
-    if (N1 <= 0 || N2 <= 0 || (N1 % MI_GROUP) != 0 || (N2 % MI_GROUP) != 0)
-        return MI_ERR_SHAPE;
-    mi::NormQuantParams a;
-    bool empty = false;
-    const mi_status st = dual_params(q, q_row_stride, kv, kv_row_stride, gamma_q, gamma_kv, eps, M, Nq, Nkv,
-                                     transpose_scale, out_q_fp8, out_scale, nullptr, false, out_kv, a, empty);
-    if (st != MI_OK || empty)
-        return st;
-    if (!w1_fp8 || !w1_scale || !out1_bf16 || !w2_fp8 || !w2_scale || !out2_bf16)
-        return MI_ERR_NULL;
-    if (!aligned16(out_q_fp8) || !aligned16(w1_fp8) || !aligned16(out1_bf16) || !aligned16(w2_fp8) ||
-        !aligned16(out2_bf16) || (reinterpret_cast<uintptr_t>(out_scale) & 3) ||
-        (reinterpret_cast<uintptr_t>(w1_scale) & 3) || (reinterpret_cast<uintptr_t>(w2_scale) & 3))
-        return MI_ERR_ALIGN;
+    return fused_step(q, q_row_stride, kv, kv_row_stride, gamma_q, gamma_kv, eps, M, Nq, Nkv, transpose_scale,
+                      out_q_fp8, out_scale, nullptr, false, out_kv, w_layout, w1_fp8, w1_scale, nullptr, out1_bf16,
+                      N1, w2_fp8, w2_scale, nullptr, out2_bf16, N2, stream);
+}
 
-    mi::GemmParams p;
-    p.a = out_q_fp8;
-    p.a_scale = out_scale;
-    p.a_scale_transposed = a.transpose_scale;
-    p.w = w1_fp8;
-    p.w_scale = w1_scale;
-    p.out = out1_bf16;
-    p.M = M;
-    p.N = N1;
-    p.K = Nq;
-    p.w2 = w2_fp8;
-    p.w_scale2 = w2_scale;
-    p.out2 = out2_bf16;
-    p.N2 = N2;
-    p.w_tiled = w_layout == MI_WEIGHT_TILED ? 1 : 0;
-    hipError_t e = mi::launch_normquant_gemm_pair(a, p, stream);
-    if (e == hipErrorNotSupported) {  // two launches
-        e = mi::launch_normquant(a, stream);
-        if (e == hipSuccess)
-            e = mi::launch_block_scaled_gemm_pair(p, stream);
-    }
-    return e == hipSuccess ? MI_OK : MI_ERR_HIP;
+extern "C" mi_status mi_fused_normquant_gemm_pair_e8m0(
+    const uint16_t *q, int64_t q_row_stride,
+    const uint16_t *kv, int64_t kv_row_stride,
+    const uint16_t *gamma_q, const uint16_t *gamma_kv,
+    float eps, int64_t M, int64_t Nq, int64_t Nkv,
+    int transpose_scale,
+    uint8_t *out_q_fp8, uint8_t *out_scale_e8m0, uint16_t *out_kv,
+    int w_layout,
+    const uint8_t *w1_fp8, const uint8_t *w1_scale_e8m0, uint16_t *out1_bf16, int64_t N1,
+    const uint8_t *w2_fp8, const uint8_t *w2_scale_e8m0, uint16_t *out2_bf16, int64_t N2,
+    hipStream_t stream) {
+    return fused_step(q, q_row_stride, kv, kv_row_stride, gamma_q, gamma_kv, eps, M, Nq, Nkv, transpose_scale,
+                      out_q_fp8, nullptr, out_scale_e8m0, true, out_kv, w_layout, w1_fp8, nullptr, w1_scale_e8m0,
+                      out1_bf16, N1, w2_fp8, nullptr, w2_scale_e8m0, out2_bf16, N2, stream);
 }
 
 extern "C" int mi_fused_normquant_gemm_pair_launches(int64_t M, int64_t Nq, int64_t Nkv, int64_t N1, int64_t N2) {

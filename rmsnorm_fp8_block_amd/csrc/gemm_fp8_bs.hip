@@ -1331,6 +1331,7 @@ constexpr int kStepMaxRows = 16;
 
 // Row m of the MLA latent shape (Nq = 1536, Nkv = 512, 16-byte aligned
 // slices) to memory: the norm-quant kernel's loads and per-row code.
+template <bool kE8m0>
 __device__ __forceinline__ void normquant_row_mla(const NormQuantParams &a, int64_t m, int lane) {
     constexpr int kQ = 3;
     uint4 gq_raw[kQ], gk_raw[1], xq[kQ], xk[1];
@@ -1348,15 +1349,16 @@ __device__ __forceinline__ void normquant_row_mla(const NormQuantParams &a, int6
     for (int c = 0; c < kQ; ++c)
         gq[c] = row::prepare_gamma(gq_raw[c]);
     gk[0] = row::prepare_gamma(gk_raw[0]);
-    row::process_row<kQ, 1, true, true, true, false>(a, m, lane, xq, xk, gq, gk);
+    row::process_row<kQ, 1, true, true, true, kE8m0>(a, m, lane, xq, xk, gq, gk);
 }
 
 // Rows of q quantised into the stream kernel's LDS image (row r of wave w
 // is row w + r * kWaves, all of a wave's row loads issued first): codes of
 // row m, K-block kb, 16-byte piece c16 at slot (kb * kMT + m / 16) * 2 +
 // (m / 8) % 2, byte 128 (m % 8) + 16 (c16 ^ (m % 8) ^ g) (g: that slot's
-// parity); its scale at the scale area + kb * 256 + 4 m.
-template <int kMT, int kWaves, int kAOff, int kSOff>
+// parity); its scale at the scale area + kb * 256 + 4 m (e8m0: the
+// exponent byte, zero-extended, as the stream kernel's 1-byte loads leave it).
+template <int kMT, int kWaves, int kAOff, int kSOff, bool kE8m0>
 struct RowsToLds {
     static constexpr int kQ = 3;  // 512-element chunks of a 1536 row
     static constexpr int kRowsMax = (16 * kMT + kWaves - 1) / kWaves;
@@ -1367,14 +1369,15 @@ struct RowsToLds {
         const int r = m & 7, gp = (m >> 3) & 1, j = m >> 4;
 #pragma unroll
         for (int c = 0; c < kQ; ++c) {
-            const row::ChunkCodes q = row::quantise_chunk<true, false>(x[c], g[c], rq);
+            const row::ChunkCodes q = row::quantise_chunk<true, kE8m0>(x[c], g[c], rq);
             const int col = c * row::kChunk + lane * 8;
             const int kb = col / kBlk, c16 = (col % kBlk) / 16, half = (col % 16) / 8;
             const int slot = (kb * kMT + j) * 2 + gp;
             *reinterpret_cast<uint2 *>(lds + kAOff + slot * 1024 + 128 * r + 16 * (c16 ^ r ^ gp) + 8 * half) =
                 make_uint2(q.lo, q.hi);
             if ((lane & 15) == 0)
-                reinterpret_cast<float *>(lds + kSOff)[kb * kWave + m] = q.s;
+                reinterpret_cast<uint32_t *>(lds + kSOff)[kb * kWave + m] =
+                    kE8m0 ? static_cast<uint32_t>(q.e + 127) : __float_as_uint(q.s);
         }
     }
 
@@ -1407,10 +1410,10 @@ struct RowsToLds {
     }
 };
 
-template <int kKB, int kMT, int kSW, int kWaves, int kD>
+template <int kKB, int kMT, int kSW, int kWaves, int kD, bool kE8m0>
 __global__ __launch_bounds__((kWaves + 1) * kWave) void normquant_gemm_pair_kernel(NormQuantParams a,
                                                                                    GemmParams p) {
-    using SW = StreamWave<kKB, kMT, kSW, kWaves, kD, false>;
+    using SW = StreamWave<kKB, kMT, kSW, kWaves, kD, kE8m0>;
     using P = typename SW::P;
     extern __shared__ uint4 s_dyn[];
     SW w;
@@ -1434,8 +1437,8 @@ __global__ __launch_bounds__((kWaves + 1) * kWave) void normquant_gemm_pair_kern
     const int64_t st0 = (static_cast<int64_t>(blockIdx.x) * kWaves + wave) * kSW;  // one row chunk: m0 = 0
     w.setup(p, wave, st0);
     if (blockIdx.x < a.M && wave == 0)
-        normquant_row_mla(a, blockIdx.x, lane);
-    RowsToLds<kMT, kWaves, P::kAOff, P::kSOff>::run(w.lds, a, wave, lane);
+        normquant_row_mla<kE8m0>(a, blockIdx.x, lane);
+    RowsToLds<kMT, kWaves, P::kAOff, P::kSOff, kE8m0>::run(w.lds, a, wave, lane);
     w.zero_acc();
     __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS writes are done
     __builtin_amdgcn_s_barrier();
@@ -1443,16 +1446,16 @@ __global__ __launch_bounds__((kWaves + 1) * kWave) void normquant_gemm_pair_kern
     w.store_tile(p, 0, st0);
 }
 
-template <int kMT, int kWaves>
+template <int kMT, int kWaves, bool kE8m0>
 hipError_t launch_normquant_gemm_pair_mt(const NormQuantParams &a, const GemmParams &p, hipStream_t stream) {
     constexpr int kKB = 12, kSW = 2;
-    constexpr int kD = stream_depth<kKB, kMT, kSW, kWaves, false>();
-    using P = StreamPlan<kKB, kMT, kSW, kWaves, kD, false>;
+    constexpr int kD = stream_depth<kKB, kMT, kSW, kWaves, kE8m0>();
+    using P = StreamPlan<kKB, kMT, kSW, kWaves, kD, kE8m0>;
     const int64_t per_block = kWaves * kSW;
     const int64_t blocks = ((p.N + p.N2) / 16 + per_block - 1) / per_block;
     if (blocks > 0x7FFFFFFF)
         return hipErrorInvalidValue;
-    auto kern = normquant_gemm_pair_kernel<kKB, kMT, kSW, kWaves, kD>;
+    auto kern = normquant_gemm_pair_kernel<kKB, kMT, kSW, kWaves, kD, kE8m0>;
     static std::atomic<uint64_t> lds_set{0};
     const hipError_t e = allow_dynamic_lds(kern, P::kLds, lds_set);
     if (e != hipSuccess)
@@ -1643,13 +1646,19 @@ hipError_t launch_normquant_gemm_pair(const NormQuantParams &a, const GemmParams
     const auto al16 = [](const void *q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
     const bool vec = al16(a.q) && al16(a.kv) && al16(a.gamma_q) && al16(a.gamma_kv) && al16(a.out_kv) &&
                      al16(a.out_q) && (a.q_stride % 8) == 0 && (a.kv_stride % 8) == 0;
-    if (!vec || a.out_scale_e8m0 || p.scale_e8m0 || p.K != a.Nq || p.M != a.M ||
+    // both in fp32 scales or both in e8m0 (the norm-quant's exponent bytes are the GEMM's As)
+    const bool e8m0 = a.out_scale_e8m0 != nullptr;
+    if (!vec || e8m0 != (p.scale_e8m0 != 0) || p.K != a.Nq || p.M != a.M ||
         !normquant_gemm_pair_one_launch(a.M, a.Nq, a.Nkv, p.N, p.N2))
         return hipErrorNotSupported;
     const int64_t S = (p.N + p.N2) / 16, cus = device_cu_count();
     const bool three = (S + cus - 1) / cus <= 6;
     static_assert(kStepMaxRows <= 16, "one 16-row chunk per block");
-    return three ? launch_normquant_gemm_pair_mt<1, 3>(a, p, stream) : launch_normquant_gemm_pair_mt<1, 4>(a, p, stream);
+    if (e8m0)
+        return three ? launch_normquant_gemm_pair_mt<1, 3, true>(a, p, stream)
+                     : launch_normquant_gemm_pair_mt<1, 4, true>(a, p, stream);
+    return three ? launch_normquant_gemm_pair_mt<1, 3, false>(a, p, stream)
+                 : launch_normquant_gemm_pair_mt<1, 4, false>(a, p, stream);
 }
 
 int gemm_pair_launches(int64_t M, int64_t K) {

@@ -136,3 +136,40 @@ def bf16_to_f64(t: torch.Tensor) -> np.ndarray:
 def run_oracle_case(case, transpose, want_ratio=True):
     return oracle.dual_rmsnorm_group_quant(case.q, case.kv, case.gamma_q, case.gamma_kv,
                                            case.eps, transpose, want_ratio=want_ratio)
+
+
+# e8m0 scales: relative distance of amax / 448 to a power of two within which
+# the exponent byte may differ by one from the oracle's
+BOUNDARY = 2.0 ** -20
+
+
+def compare_e8m0(codes, sbytes, ref, M, G, transpose, label):
+    """e8m0 norm-quant bar: exponent bytes equal to the oracle's except, by
+    one, where the group's amax / 448 lies within BOUNDARY of a power of two
+    (those groups' codes are not compared); other codes within 1 e4m3 ULP,
+    any difference next to a rounding midpoint, >= CODE_EXACT_FRACTION
+    identical, no NaN code.  Returns (exact fraction, groups whose exponent
+    differs)."""
+    rs = ref["scale"].astype(np.int64)
+    gs = sbytes.astype(np.int64)
+    to_mg = (lambda a: a.reshape(G, M).T) if transpose else (lambda a: a.reshape(M, G))
+    rs, gs = to_mg(rs), to_mg(gs)
+    diff = rs != gs
+    ratio = ref["ratio"].reshape(M, G, 128)
+    rmax = np.abs(ratio).max(axis=2)                 # amax / s_oracle, in (224, 448] for live groups
+    if diff.any():
+        assert np.all(np.abs(gs[diff] - rs[diff]) == 1), f"{label}: exponent off by more than one"
+        near = np.minimum(np.abs(rmax[diff] / 448 - 1), np.abs(rmax[diff] / 224 - 1))
+        assert np.all(near <= BOUNDARY), f"{label}: exponent differs away from a power-of-two boundary"
+    keep = np.repeat(~diff, 128, axis=1).reshape(M, G * 128)
+    got, want = codes[keep], ref["q"][keep]
+    assert not np.any((got & 0x7F) == 0x7F), f"{label}: NaN code"
+    d = np.abs(e4m3_ord(got) - e4m3_ord(want))
+    assert d.max(initial=0) <= 1, f"{label}: code off by {d.max()} ULP"
+    if (d != 0).any():
+        near = e4m3_midpoint_distance(ref["ratio"][keep][d != 0])
+        assert np.all(near <= MIDPOINT_WINDOW), f"{label}: code mismatch away from a midpoint"
+    exact = float((d == 0).mean()) if d.size else 1.0
+    if d.size >= 10_000:
+        assert exact >= CODE_EXACT_FRACTION, f"{label}: only {exact:.5f} exact"
+    return exact, int(diff.sum())

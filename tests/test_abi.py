@@ -243,29 +243,32 @@ def test_e8m0_entry_validation(L):
     assert p8(Bs1=NULL) == B.MI_ERR_NULL
 
 
-def step(L, **kw):
+def step(L, e8m0=False, **kw):
     a = dict(q=FAKE, qs=2048, kv=FAKE, ks=2048, gq=FAKE, gk=FAKE, eps=1e-6, M=4, Nq=1536, Nkv=512, t=1,
              oq=FAKE, os_=FAKE, okv=FAKE, wl=B.MI_WEIGHT_TILED, w1=FAKE, Bs1=FAKE, out1=FAKE, N1=24576,
              w2=FAKE, Bs2=FAKE, out2=FAKE, N2=8192)
     a.update(kw)
-    return L.mi_fused_normquant_gemm_pair(
+    fn = L.mi_fused_normquant_gemm_pair_e8m0 if e8m0 else L.mi_fused_normquant_gemm_pair
+    return fn(
         a["q"], a["qs"], a["kv"], a["ks"], a["gq"], a["gk"], ctypes.c_float(a["eps"]), a["M"], a["Nq"], a["Nkv"],
         a["t"], a["oq"], a["os_"], a["okv"], a["wl"], a["w1"], a["Bs1"], a["out1"], a["N1"], a["w2"], a["Bs2"],
         a["out2"], a["N2"], NULL)
 
 
-def test_fused_step_validation(L):
-    """The one-call decode step checks what both of its parts check."""
-    assert step(L, wl=2) == B.MI_ERR_LAYOUT
+@pytest.mark.parametrize("e8m0", [False, True])
+def test_fused_step_validation(L, e8m0):
+    """The one-call decode step (fp32 or e8m0 scales) checks what both of
+    its parts check."""
+    assert step(L, e8m0, wl=2) == B.MI_ERR_LAYOUT
     for k, v in (("M", -1), ("Nq", 1500), ("Nkv", 0), ("N1", 1000), ("N2", 0)):
-        assert step(L, **{k: v}) == B.MI_ERR_SHAPE, k
-    assert step(L, M=0) == B.MI_OK
-    assert step(L, M=0, q=NULL) == B.MI_OK
+        assert step(L, e8m0, **{k: v}) == B.MI_ERR_SHAPE, k
+    assert step(L, e8m0, M=0) == B.MI_OK
+    assert step(L, e8m0, M=0, q=NULL) == B.MI_OK
     for k in ("q", "kv", "gq", "gk", "oq", "os_", "okv", "w1", "Bs1", "out1", "w2", "Bs2", "out2"):
-        assert step(L, **{k: NULL}) == B.MI_ERR_NULL, k
-    assert step(L, qs=1535) == B.MI_ERR_STRIDE
+        assert step(L, e8m0, **{k: NULL}) == B.MI_ERR_NULL, k
+    assert step(L, e8m0, qs=1535) == B.MI_ERR_STRIDE
     for k, v in (("oq", 0x1008), ("w1", 0x1004), ("out2", 0x1002), ("os_", 0x1002), ("Bs2", 0x1001)):
-        assert step(L, **{k: ctypes.c_void_p(v)}) == B.MI_ERR_ALIGN, k
+        assert step(L, e8m0, **{k: ctypes.c_void_p(v)}) == B.MI_ERR_ALIGN, k
 
 
 def test_fused_step_launch_count(L):

@@ -22,47 +22,10 @@ import oracle
 import rmsnorm_fp8_block_amd as mi
 from rmsnorm_fp8_block_amd import workloads as W
 
-from helpers import (CODE_EXACT_FRACTION, MIDPOINT_WINDOW, assert_gemm_close, bf16_to_f64, dev_f32, dev_u8,
-                     dev_u16_as_bf16, e4m3_midpoint_distance, e4m3_ord, gpu_or_skip, host_bf16_bits)
+from helpers import (assert_gemm_close, bf16_to_f64, compare_e8m0, dev_f32, dev_u8, dev_u16_as_bf16, gpu_or_skip,
+                     host_bf16_bits, scale_buffer)
 
 pytestmark = pytest.mark.gpu
-
-BOUNDARY = 2.0 ** -20    # relative distance of amax / 448 to a power of two
-
-
-def scale_bytes(scale: torch.Tensor) -> np.ndarray:
-    M, G = scale.shape
-    if scale.stride() == (1, M) and M > 1:
-        return scale.T.contiguous().reshape(-1).cpu().numpy()
-    return scale.contiguous().reshape(-1).cpu().numpy()
-
-
-def compare_e8m0(codes, sbytes, ref, M, G, transpose, label):
-    """Assert the bar above; return (exact fraction, groups whose exponent differs)."""
-    rs = ref["scale"].astype(np.int64)
-    gs = sbytes.astype(np.int64)
-    to_mg = (lambda a: a.reshape(G, M).T) if transpose else (lambda a: a.reshape(M, G))
-    rs, gs = to_mg(rs), to_mg(gs)
-    diff = rs != gs
-    ratio = ref["ratio"].reshape(M, G, 128)
-    rmax = np.abs(ratio).max(axis=2)                 # amax / s_oracle, in (224, 448] for live groups
-    if diff.any():
-        assert np.all(np.abs(gs[diff] - rs[diff]) == 1), f"{label}: exponent off by more than one"
-        near = np.minimum(np.abs(rmax[diff] / 448 - 1), np.abs(rmax[diff] / 224 - 1))
-        assert np.all(near <= BOUNDARY), f"{label}: exponent differs away from a power-of-two boundary"
-    keep = np.repeat(~diff, 128, axis=1).reshape(M, G * 128)
-    got, want = codes[keep], ref["q"][keep]
-    assert not np.any((got & 0x7F) == 0x7F), f"{label}: NaN code"
-    d = np.abs(e4m3_ord(got) - e4m3_ord(want))
-    assert d.max(initial=0) <= 1, f"{label}: code off by {d.max()} ULP"
-    if (d != 0).any():
-        near = e4m3_midpoint_distance(ref["ratio"][keep][d != 0])
-        assert np.all(near <= MIDPOINT_WINDOW), f"{label}: code mismatch away from a midpoint"
-    exact = float((d == 0).mean()) if d.size else 1.0
-    if d.size >= 10_000:
-        assert exact >= CODE_EXACT_FRACTION, f"{label}: only {exact:.5f} exact"
-    return exact, int(diff.sum())
-
 
 def run_case(case, transpose, dev):
     if case.buffer is not None:
@@ -75,7 +38,7 @@ def run_case(case, transpose, dev):
     _, _, kv32 = mi.mi_fused_dual_rmsnorm_group_quant(q, kv, gq, gk, case.eps, transpose)
     torch.cuda.synchronize()
     assert torch.equal(kvo, kv32), "kv must equal the fp32-scale call's"
-    return codes.cpu().numpy(), scale_bytes(scale), scale
+    return codes.cpu().numpy(), scale_buffer(scale), scale
 
 
 WORKLOADS = {
@@ -227,7 +190,7 @@ def test_producer_and_two_consumers_e8m0(M):
                                               dev_u8(wa.scale, dev), mi.relayout_weight(dev_u8(wb.codes, dev)),
                                               dev_u8(wb.scale, dev))
     torch.cuda.synchronize()
-    compare_e8m0(codes.cpu().numpy(), scale_bytes(scale), qref, M, 12, True, f"producer M{M}")
+    compare_e8m0(codes.cpu().numpy(), scale_buffer(scale), qref, M, 12, True, f"producer M{M}")
     # the oracle GEMM on the oracle's own quantised pair
     asf = oracle.e8m0_decode_array(qref["scale"]).astype(np.float32)
     for o, wt, name in ((o1, wa, "W_a"), (o2, wb, "W_b")):

@@ -21,8 +21,8 @@ import oracle
 import rmsnorm_fp8_block_amd as mi
 from rmsnorm_fp8_block_amd import workloads as W
 
-from helpers import (assert_gemm_close, bf16_to_f64, compare_normquant, dev_f32, dev_u16_as_bf16, dev_u8,
-                     gpu_or_skip, host_bf16_bits, scale_buffer)
+from helpers import (assert_gemm_close, bf16_to_f64, compare_e8m0, compare_normquant, dev_f32, dev_u16_as_bf16,
+                     dev_u8, gpu_or_skip, host_bf16_bits, scale_buffer)
 
 pytestmark = pytest.mark.gpu
 
@@ -218,3 +218,84 @@ def test_step_zero_rows(weights):
                                                                 wb["tiled"], wb["scale"])
     assert codes.shape == (0, 1536) and scale.shape == (0, 12) and kvo.shape == (0, 512)
     assert o1.shape == (0, 24576) and o2.shape == (0, 8192)
+
+
+# ---------------------------------------------------------------------------
+# the step with e8m0 (power-of-two) scales on both sides: the e8m0 norm-quant
+# (exponent bytes) feeding the e8m0 pair, whose matrix cores apply the
+# activation and weight exponents (PRHub digest of vLLM PR #56560)
+
+
+@pytest.fixture(scope="module")
+def weights_e8m0():
+    dev = gpu_or_skip()
+    out = {}
+    for name, (shape, seed) in (("W_a", (W.W_A_SHAPE, W.W_A_SEED)), ("W_b", (W.W_B_SHAPE, W.W_B_SEED))):
+        wt = W.block_fp8_weight_e8m0(*shape, seed)
+        d = dev_u8(wt.codes, dev)
+        out[name] = dict(host=wt, row=d, tiled=mi.relayout_weight(d), scale=dev_u8(wt.scale, dev))
+    return out
+
+
+def two_calls_e8m0(q, kv, gq, gk, t, w1, s1, w2, s2):
+    codes, scale, kvo = mi.mi_fused_dual_rmsnorm_group_quant_e8m0(q, kv, gq, gk, W.EPS, t)
+    o1, o2 = mi.mi_block_scaled_fp8_gemm_pair(codes, scale, w1, s1, w2, s2)
+    return codes, scale, kvo, o1, o2
+
+
+@pytest.mark.parametrize("layout", ["tiled", "row"])
+@pytest.mark.parametrize("M", [1, 7, 16, 33])
+def test_step_e8m0_equals_the_two_calls(M, layout, weights_e8m0):
+    """e8m0 scales: one launch up to 16 rows, two above; both scale layouts:
+    bit-identical to the e8m0 norm-quant followed by the e8m0 pair."""
+    dev = gpu_or_skip()
+    q, kv, gq, gk = device_case(W.producer_activations(M), dev)
+    wa, wb = weights_e8m0["W_a"], weights_e8m0["W_b"]
+    for t in (0, 1):
+        args = (wa[layout], wa["scale"], wb[layout], wb["scale"])
+        got = mi.mi_fused_normquant_gemm_pair(q, kv, gq, gk, W.EPS, t, *args)
+        assert got[1].dtype == torch.uint8
+        want = two_calls_e8m0(q, kv, gq, gk, t, *args)
+        torch.cuda.synchronize()
+        assert_same(got, want, f"e8m0 M{M} {layout} t{t}")
+
+
+def test_step_e8m0_vs_oracle(weights_e8m0):
+    """M = 16 (one launch), column-major exponent bytes: the norm-quant
+    outputs to the e8m0 bar against the e8m0 oracle, both GEMM outputs on
+    sampled column blocks against the fp64 oracle GEMM on the decoded
+    scales of the oracle's own quantised pair."""
+    dev = gpu_or_skip()
+    case = W.strided_batch(16)
+    q, kv, gq, gk = device_case(case, dev)
+    wa, wb = weights_e8m0["W_a"], weights_e8m0["W_b"]
+    codes, scale, kvo, o1, o2 = mi.mi_fused_normquant_gemm_pair(
+        q, kv, gq, gk, case.eps, True, wa["tiled"], wa["scale"], wb["tiled"], wb["scale"])
+    _, _, kv32 = mi.mi_fused_dual_rmsnorm_group_quant(q, kv, gq, gk, case.eps, True)
+    torch.cuda.synchronize()
+    assert torch.equal(kvo, kv32), "kv must equal the fp32-scale call's"
+    ref = oracle.dual_rmsnorm_group_quant_e8m0(case.q, case.kv, case.gamma_q, case.gamma_kv, case.eps, True,
+                                               want_ratio=True)
+    compare_e8m0(codes.cpu().numpy(), scale_buffer(scale), ref, 16, 12, True, "e8m0 step M16")
+    asf = oracle.e8m0_decode_array(ref["scale"]).astype(np.float32)
+    for name, out in (("W_a", o1), ("W_b", o2)):
+        wt = weights_e8m0[name]["host"]
+        nb = wt.codes.shape[0] // 128
+        blocks = np.unique([0, 1, nb // 2, nb - 1])
+        cols = (blocks[:, None] * 128 + np.arange(128)[None, :]).reshape(-1)
+        bsf = oracle.e8m0_decode_array(wt.scale[blocks]).astype(np.float32)
+        gref = oracle.block_scaled_fp8_gemm(ref["q"], asf, True, wt.codes[cols], bsf)
+        assert_gemm_close(bf16_to_f64(out)[:, cols], gref, f"e8m0 step {name}")
+
+
+def test_step_refuses_mixed_scale_types(weights, weights_e8m0):
+    """Both weights' scales, and a given out_scale, must be of one type."""
+    dev = gpu_or_skip()
+    q, kv, gq, gk = device_case(W.producer_activations(4), dev)
+    wa, wb = weights["W_a"], weights_e8m0["W_b"]
+    with pytest.raises(ValueError):
+        mi.mi_fused_normquant_gemm_pair(q, kv, gq, gk, W.EPS, True, wa["tiled"], wa["scale"], wb["tiled"],
+                                        wb["scale"])
+    with pytest.raises(ValueError):
+        mi.mi_fused_normquant_gemm_pair(q, kv, gq, gk, W.EPS, True, wa["tiled"], wa["scale"], wa["tiled"],
+                                        wa["scale"], out_scale=torch.empty(48, dtype=torch.uint8, device=dev))
