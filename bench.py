@@ -226,24 +226,59 @@ def build_sets(torch, np, mi, W, M, layout, wa, wb, nsets, dev, tiled):
             "gb": mi.prepare_block_scaled_fp8_gemm(oq, scale, wb_c, wb_s0, ob),
             "fs": mi.prepare_fused_normquant_gemm_pair(q, kv, gq, gk, W.EPS, layout, wa_c, wa_s0, wb_c, wb_s0,
                                                        oq, osc, okv, oa, ob),
+            "out": (oq, osc, okv, oa, ob),
         })
     return sets
 
 
 def cpu_baseline(np, W, M, layout, wa, wb):
     """The oracle as it stands, on this host: one full step (norm-quant of
-    the same M rows, then both GEMMs over all their columns)."""
+    the same M rows, then both GEMMs over all their columns).  Returns the
+    bench entry and the oracle's outputs (q codes, scales in storage order,
+    kv bf16 bits, both GEMM outputs in fp64)."""
     import oracle
     case = W.producer_activations(M) if M <= 256 else W.strided_batch(M)
     t0 = time.perf_counter()
     r = oracle.dual_rmsnorm_group_quant(case.q, case.kv, case.gamma_q, case.gamma_kv, W.EPS, layout)
-    oracle.block_scaled_fp8_gemm(r["q"], r["scale"], layout, wa.codes, wa.scale)
-    oracle.block_scaled_fp8_gemm(r["q"], r["scale"], layout, wb.codes, wb.scale)
+    o1 = oracle.block_scaled_fp8_gemm(r["q"], r["scale"], layout, wa.codes, wa.scale)
+    o2 = oracle.block_scaled_fp8_gemm(r["q"], r["scale"], layout, wb.codes, wb.scale)
     dt = time.perf_counter() - t0
-    return {"value": round(dt * 1e6, 1), "unit": "µs/step", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"one full step at M={M}: fp64 norm-quant of {M} rows + both GEMMs over all "
-                      f"{wa.codes.shape[0] + wb.codes.shape[0]} output columns ({dt:.1f} s wall)"}
+    entry = {"value": round(dt * 1e6, 1), "unit": "µs/step", "cores": oracle.num_threads(),
+             "kind": "oracle",
+             "sample": f"one full step at M={M}: fp64 norm-quant of {M} rows + both GEMMs over all "
+                       f"{wa.codes.shape[0] + wb.codes.shape[0]} output columns ({dt:.1f} s wall)"}
+    return entry, (r["q"], r["scale"], r["kv"], o1, o2)
+
+
+def sign_magnitude_ord(bits, np, sign_bit):
+    """Signed-magnitude bit patterns (e4m3 codes, bf16 bits) mapped to
+    integers in value order, so that neighbouring representable values
+    differ by 1 (+0 and -0 both map to 0)."""
+    b = bits.astype(np.int64)
+    mag = b & (sign_bit - 1)
+    return np.where(b & sign_bit, -mag, mag)
+
+
+def parity_stats(np, got, ref):
+    """The step's outputs on the device (buffer set 0, the same inputs as
+    the oracle's) against the oracle's: fraction of identical q codes and
+    the largest e4m3 step between them, the largest relative scale error,
+    the largest kv difference in bf16 steps, and each GEMM output's relative
+    Frobenius and max errors (max |out - ref| / max |ref|)."""
+    gq, gs, gkv, g1, g2 = got
+    rq, rs, rkv, r1, r2 = ref
+    dq = np.abs(sign_magnitude_ord(gq, np, 0x80) - sign_magnitude_ord(rq, np, 0x80))
+    dk = np.abs(sign_magnitude_ord(gkv, np, 0x8000) - sign_magnitude_ord(rkv, np, 0x8000))
+    rel = np.abs(gs.astype(np.float64) / rs.astype(np.float64) - 1.0)
+    out = {"q_codes_exact": round(float((dq == 0).mean()), 6), "q_codes_max_ulp": int(dq.max()),
+           "scale_max_rel": float(rel.max()), "kv_exact": round(float((dk == 0).mean()), 6),
+           "kv_max_ulp": int(dk.max())}
+    for name, o, r in (("W_a", g1, r1), ("W_b", g2, r2)):
+        fro = float(np.linalg.norm(o - r) / max(np.linalg.norm(r), 1e-300))
+        mx = float(np.abs(o - r).max() / max(np.abs(r).max(), 1e-300))
+        out[f"gemm_{name}_rel_fro"] = float(f"{fro:.3e}")
+        out[f"gemm_{name}_rel_max"] = float(f"{mx:.3e}")
+    return out
 
 
 def sweep(torch, np, mi, W, wa, wb, dev, cold, tiled):
@@ -692,7 +727,15 @@ def main():
     if not args.no_sweep:
         line["sweep"] = sweep(torch, np, mi, W, wa, wb, dev, cold=not args.warm, tiled=tiled)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(np, W, M, layout, wa, wb)
+        # set 0 once more through the library's step (its outputs were last
+        # written by the single-GEMM timing loops), then to the host
+        sets[0]["fs"]()
+        torch.cuda.synchronize()
+        oq, osc, okv, oa, ob = sets[0]["out"]
+        got = (oq.cpu().numpy(), osc.cpu().numpy(), okv.view(torch.int16).cpu().numpy().view(np.uint16),
+               oa.float().cpu().numpy().astype(np.float64), ob.float().cpu().numpy().astype(np.float64))
+        line["cpu_baseline"], ref = cpu_baseline(np, W, M, layout, wa, wb)
+        line["parity"] = parity_stats(np, got, ref)
     print(json.dumps(line), flush=True)
 
 
