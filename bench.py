@@ -724,6 +724,18 @@ def main():
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", "?"),
                    "cus": props.multi_processor_count},
     }
+    if not args.warm:
+        # labelled warm figures: one buffer set reused, so the weights come
+        # from the Infinity Cache / L2 instead of HBM (not the headline)
+        warm = {"cache": "warm (buffer set 0 reused every step)"}
+        for name, keys, nbytes in (("step", ["fs"] if library else ["nq", "gp"], step_bytes),
+                                   ("pair", ["gp"], kernels["block_scaled_fp8_gemm_pair"]["bytes"])):
+            gw = make_graph(torch, [sets[0][k] for k in keys] * 20)   # 20 steps per replay
+            us = time_graph(torch, gw, 20, 20)
+            del gw
+            warm[f"{name}_us"] = round(us, 3)
+            warm[f"{name}_GB/s"] = round(nbytes / us / 1e3, 1)
+        line["warm"] = warm
     if not args.no_sweep:
         line["sweep"] = sweep(torch, np, mi, W, wa, wb, dev, cold=not args.warm, tiled=tiled)
     if not args.no_cpu_baseline:
