@@ -676,6 +676,12 @@ def main():
         gbs = nbytes / us / 1e3
         k = {"us": round(us, 3), "bytes": nbytes, "GB/s": round(gbs, 1),
              "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "source_sha": source_sha(*src)}
+        # what this loop's rotation touches: under the Infinity Cache size,
+        # its operands stay cache-resident (the step itself stays cold: the
+        # weights rotate past 1 GiB)
+        footprint = len(fns) * nbytes
+        k["cache"] = "cold" if footprint > 2 * MALL_BYTES else \
+            f"warm ({len(fns)} sets, {footprint / 2**20:.1f} MiB in all: Infinity Cache resident)"
         if flops:
             k["TFLOP/s"] = round(flops / us / 1e6, 2)
         k["traffic"] = measured_traffic(name, k["source_sha"], M)
