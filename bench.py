@@ -583,8 +583,8 @@ def calibrate_copy(torch, steps):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); "
-              "the path has no cross-GPU step to measure", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the path has no cross-GPU step "
+              "to measure (norm-quant rows and GEMM columns shard with no exchange)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(L):
 def test_no_kernel_of_the_library_is_left_undefined():
     """A kernel whose launch stub the host compiler pass dropped shows up as
     an undefined symbol of the library's own namespace (the library would
-    then fail to load on a GPU machine)."""
+    then fail to load on any machine with a GPU)."""
     out = subprocess.run(["nm", "-D", "--undefined-only", B.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
     own = [line.split()[-1] for line in out.splitlines() if "_ZN2mi" in line]
