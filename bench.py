@@ -680,10 +680,10 @@ def main():
         # its operands stay cache-resident (the step itself stays cold: the
         # weights rotate past 1 GiB)
         footprint = len(fns) * nbytes
-        sets = f"{len(fns)} sets, {footprint / 2**20:.1f} MiB in all"
+        rotation = f"{len(fns)} sets, {footprint / 2**20:.1f} MiB in all"
         k["cache"] = ("cold" if footprint > 2 * MALL_BYTES else
-                      f"partly warm ({sets}: within twice the 256 MiB Infinity Cache)" if footprint > MALL_BYTES else
-                      f"warm ({sets}: Infinity Cache resident)")
+                      f"partly warm ({rotation}: within twice the 256 MiB Infinity Cache)" if footprint > MALL_BYTES
+                      else f"warm ({rotation}: Infinity Cache resident)")
         if flops:
             k["TFLOP/s"] = round(flops / us / 1e6, 2)
         k["traffic"] = measured_traffic(name, k["source_sha"], M)
