@@ -299,3 +299,41 @@ def test_step_refuses_mixed_scale_types(weights, weights_e8m0):
     with pytest.raises(ValueError):
         mi.mi_fused_normquant_gemm_pair(q, kv, gq, gk, W.EPS, True, wa["tiled"], wa["scale"], wa["tiled"],
                                         wa["scale"], out_scale=torch.empty(48, dtype=torch.uint8, device=dev))
+
+
+def test_step_e8m0_graph_replays(weights_e8m0):
+    """The e8m0 one-launch step captured in a HIP graph: three replays with
+    the input rewritten by eager work between them, each equal to the eager
+    e8m0 two calls on that input."""
+    dev = gpu_or_skip()
+    wa, wb = weights_e8m0["W_a"], weights_e8m0["W_b"]
+    M = 16
+    case = W.strided_batch(M)
+    q, kv, gq, gk = device_case(case, dev)
+    buf = q._base
+    assert buf is not None and buf.shape == (M, 2048)
+    outs = (torch.empty((M, 1536), dtype=torch.uint8, device=dev), torch.empty(M * 12, dtype=torch.uint8, device=dev),
+            torch.empty((M, 512), dtype=torch.bfloat16, device=dev),
+            torch.empty((M, 24576), dtype=torch.bfloat16, device=dev),
+            torch.empty((M, 8192), dtype=torch.bfloat16, device=dev))
+    call = mi.prepare_fused_normquant_gemm_pair(q, kv, gq, gk, W.EPS, True, wa["tiled"], wa["scale"], wb["tiled"],
+                                                wb["scale"], *outs)
+    assert call.name == "mi_fused_normquant_gemm_pair_e8m0"
+    s = torch.cuda.Stream(device=dev)
+    s.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(s):
+        call()  # warm-up outside the capture (sets the kernel's LDS attribute)
+    torch.cuda.current_stream(dev).wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for i in range(3):
+        r = np.random.default_rng(90 + i)
+        buf.copy_(dev_u16_as_bf16(W.f32_to_bf16_bits(r.standard_normal((M, 2048), dtype=np.float32)), dev))
+        g.replay()
+        torch.cuda.synchronize()
+        want = two_calls_e8m0(q, kv, gq, gk, True, wa["tiled"], wa["scale"], wb["tiled"], wb["scale"])
+        got = (outs[0], outs[1].view(12, M).T, outs[2], outs[3], outs[4])
+        torch.cuda.synchronize()
+        assert_same(got, want, f"e8m0 replay {i}")
