@@ -1349,7 +1349,7 @@ __device__ __forceinline__ void normquant_row_mla(const NormQuantParams &a, int6
     for (int c = 0; c < kQ; ++c)
         gq[c] = row::prepare_gamma(gq_raw[c]);
     gk[0] = row::prepare_gamma(gk_raw[0]);
-    row::process_row<kQ, 1, true, true, true, kE8m0>(a, m, lane, xq, xk, gq, gk);
+    row::process_row<kQ, 1, true, true, true, kE8m0, false>(a, m, lane, xq, xk, gq, gk);
 }
 
 // Rows of q quantised into the stream kernel's LDS image (row r of wave w

@@ -45,8 +45,9 @@ namespace {
 // output row is 16-byte aligned and Nkv % 8 == 0.  kRows: consecutive rows
 // per wave; all their loads are issued together, gammas once per wave.
 // kFull: Nq == 512 * kQ and Nkv == 512 * kKv (no bounds tests).
-// kStream: the rows are read with non-temporal loads (large M: every row is
-// read once; measured slower for a handful of rows).
+// kStream: the rows are read, and the outputs written, with non-temporal
+// loads and stores (large M: every row is read once; measured slower for a
+// handful of rows).
 template <int kQ, int kKv, bool kVec, int kRows, bool kFull, bool kNorm, bool kE8m0, bool kStream>
 __global__ __launch_bounds__(256) void fused_dual_rmsnorm_group_quant_kernel(NormQuantParams a) {
     constexpr int kKvA = kKv > 0 ? kKv : 1;  // array extents
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(256) void fused_dual_rmsnorm_group_quant_kernel(Nor
         const int64_t m = row0 + r;
         if (m >= a.M)
             break;
-        process_row<kQ, kKv, kVec, kFull, kNorm, kE8m0>(a, m, lane, xq[r], xk[r], gq, gk);
+        process_row<kQ, kKv, kVec, kFull, kNorm, kE8m0, kStream>(a, m, lane, xq[r], xk[r], gq, gk);
     }
 }
 
