@@ -50,8 +50,8 @@ GEMM_SOURCES = ("gemm_fp8_bs.hip", "normquant_row.h", "device.h", "launch.h")
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--M", type=int, default=64, help="tokens per step")
     ap.add_argument("--scale-layout", choices=("row", "col"), default="col")
     ap.add_argument("--weight-layout", choices=("preferred", "row", "tiled"), default="preferred",
@@ -62,6 +62,7 @@ def parse():
     ap.add_argument("--warm", action="store_true", help="reuse one buffer set (cache-warm numbers)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="skip the M=1 / M=8192 / M=256 extras")
+    ap.add_argument("--no-warm", action="store_true", help="skip the labelled warm-cache figures")
     ap.add_argument("--kernel-loop", default="", help="only launch this kernel in a loop (profiling)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 64 MiB device copy in a loop (scales the HBM byte counters)")
@@ -732,7 +733,7 @@ def main():
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", "?"),
                    "cus": props.multi_processor_count},
     }
-    if not args.warm:
+    if not args.warm and not args.no_warm:
         # labelled warm figures: one buffer set reused, so the weights come
         # from the Infinity Cache / L2 instead of HBM (not the headline)
         warm = {"cache": "warm (buffer set 0 reused every step)"}
