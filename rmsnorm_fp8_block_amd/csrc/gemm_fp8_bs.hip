@@ -210,11 +210,14 @@ constexpr int kDecodeMaxRows = 32;  // batches it is used for (measured crossove
 // drops the launch stub of any kernel that reaches it.
 // A 1-byte load writes its byte zero-extended to a dword per lane (LDS
 // address: base + lane * 4).
-template <int kBytes>
+template <int kBytes, int kCpol = 0>
 __device__ __forceinline__ void load_to_lds(const void *src, void *dst) {
     static_assert(kBytes == 16 || kBytes == 4 || kBytes == 1, "supported loads");
+    static_assert(kCpol == 0 || (kBytes == 16 && kCpol == 2), "cache policy: default, or non-temporal 16-byte loads");
 #if defined(__HIP_DEVICE_COMPILE__)
-    if constexpr (kBytes == 16)
+    if constexpr (kBytes == 16 && kCpol == 2)
+        __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 2);
+    else if constexpr (kBytes == 16)
         __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
     else if constexpr (kBytes == 4)
         __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
@@ -384,7 +387,7 @@ struct WideWave {
         uint8_t *dst = lds + P::kWOff + (s % P::kRW) * P::kWStage;
 #pragma unroll
         for (int i = 0; i < P::kNW; ++i)
-            load_to_lds<16>(wbase[i] + s * w_kstride + w_off, dst + wslot[i] * P::kSlot);
+            load_to_lds<16, 2>(wbase[i] + s * w_kstride + w_off, dst + wslot[i] * P::kSlot);
     }
 
     __device__ __forceinline__ void issue_a(int s) {
@@ -735,7 +738,7 @@ struct StreamWave {
         for (int t = 0; t < kSW; ++t)
 #pragma unroll
             for (int g = 0; g < 2; ++g)
-                load_to_lds<16>(wsrc[t] + s * w_kstride + w_off[g], dst + (2 * t + g) * P::kSlot);
+                load_to_lds<16, 2>(wsrc[t] + s * w_kstride + w_off[g], dst + (2 * t + g) * P::kSlot);
     }
 
     // activation slots (all K-blocks) and As, split over the waves; slot
