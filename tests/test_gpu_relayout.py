@@ -62,13 +62,16 @@ def test_same_layout_is_a_copy():
     assert torch.equal(dst, w)
 
 
-# (M, N, K): decode kernel (M <= 32 over a wide weight), wide kernel (M <= 256,
-# K/128 in {4, 8, 12, 16}), row-split wide kernel (few slabs, M > 64), v0
-# (M > 256, or K/128 = 5)
+# (M, N, K): stream kernel (M <= 64 over at least 6 subtiles per CU, K/128 in
+# {4, 8, 12}); decode kernel (M <= 32 over more than 4 subtiles per CU where
+# the stream kernel does not apply: K/128 = 16, or 5 subtiles per CU); wide
+# kernel (M <= 256, K/128 in {4, 8, 12, 16}); row-split wide kernel (few
+# slabs, M > 64); v0 (M > 256, or K/128 = 5)
 @pytest.mark.parametrize("M,N,K,seed", [(1, 24576, 1536, 1), (16, 24576, 1536, 2), (32, 16384, 1024, 3),
                                         (64, 8192, 1536, 4), (100, 1536, 1536, 5), (256, 3072, 1536, 6),
                                         (256, 24576, 1536, 7), (300, 1280, 1536, 8), (40, 1280, 640, 9),
-                                        (5, 256, 2048, 10)])
+                                        (5, 256, 2048, 10), (16, 24576, 2048, 11), (8, 20480, 1536, 12),
+                                        (32, 20480, 1024, 13)])
 def test_tiled_gemm_equals_row_major(M, N, K, seed):
     dev = gpu_or_skip()
     a, As, w, Bs = operands(M, N, K, seed)
