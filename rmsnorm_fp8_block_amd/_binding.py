@@ -122,13 +122,88 @@ def _ptr(t: torch.Tensor) -> ctypes.c_void_p:
     return ctypes.c_void_p(t.data_ptr())
 
 
+E8M0_DTYPES = (torch.uint8, getattr(torch, "float8_e8m0fnu", torch.uint8))
+
+
+def _u8(t: torch.Tensor) -> torch.Tensor:
+    """An e8m0 scale tensor as uint8 bytes (float8_e8m0fnu is viewed)."""
+    return t if t.dtype == torch.uint8 else t.view(torch.uint8)
+
+
 def _rows(t: torch.Tensor, name: str, dtype: torch.dtype) -> int:
-    """Row stride (elements) of a 2-D tensor with unit inner stride."""
-    if t.dim() != 2 or t.dtype != dtype:
-        raise ValueError(f"{name}: expected a 2-D {dtype} tensor, got {tuple(t.shape)} {t.dtype}")
-    if t.shape[0] > 1 and t.stride(1) != 1:
+    """Row stride (elements) of a 2-D tensor with unit inner stride (checked
+    for every row count: the kernels read each row as contiguous elements)."""
+    if not isinstance(t, torch.Tensor) or t.dim() != 2 or t.dtype != dtype:
+        raise ValueError(f"{name}: expected a 2-D {dtype} tensor, got "
+                         f"{tuple(t.shape) if isinstance(t, torch.Tensor) else type(t)} "
+                         f"{getattr(t, 'dtype', '')}")
+    if t.shape[1] > 1 and t.stride(1) != 1:
         raise ValueError(f"{name}: inner stride must be 1, got {t.stride()}")
     return t.stride(0) if t.shape[0] > 1 else t.shape[1]
+
+
+def _vector(t, name: str, dtype: torch.dtype, n: int) -> None:
+    """A contiguous 1-D-able tensor of exactly n elements of the given dtype
+    (the RMSNorm weights)."""
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_contiguous() or t.numel() != n:
+        raise ValueError(f"{name}: expected a contiguous {dtype} tensor of {n} elements, got "
+                         f"{tuple(getattr(t, 'shape', ()))} {getattr(t, 'dtype', type(t))}")
+
+
+def _output(t, name: str, dtypes, n: int) -> None:
+    """A contiguous output buffer of at least n elements of one of dtypes."""
+    if not isinstance(t, torch.Tensor) or t.dtype not in dtypes:
+        raise ValueError(f"{name}: expected a tensor of {' / '.join(map(str, dtypes))}, got "
+                         f"{getattr(t, 'dtype', type(t))}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: output must be contiguous, got strides {t.stride()}")
+    if t.numel() < n:
+        raise ValueError(f"{name}: output buffer too small ({t.numel()} < {n} elements)")
+
+
+def _same_gpu(ref: torch.Tensor, ref_name: str, **tensors) -> None:
+    """Every tensor on the GPU that ``ref`` is on: the library dereferences
+    each pointer on that device (a host pointer there is a memory fault)."""
+    if not ref.is_cuda:
+        raise ValueError(f"{ref_name}: expected a GPU tensor, got one on {ref.device}")
+    for name, t in tensors.items():
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{name}: on {t.device}, expected {ref.device} (the device of {ref_name})")
+
+
+Q_DTYPES = (torch.uint8,) + ((torch.float8_e4m3fn,) if hasattr(torch, "float8_e4m3fn") else ())
+
+
+def _dual_args(q, kv, gamma_q, gamma_kv, out_q, out_scale, out_kv, e8m0: bool, alloc: bool,
+               devices: bool = True):
+    """Checks of the dual norm-quant's operands, shared by the eager and
+    prepared calls and the one-call step.  With ``alloc`` missing outputs
+    are allocated on q's device.  Returns (q row stride, kv row stride, M,
+    Nq, Nkv, out_q, out_scale (uint8 view for e8m0), out_kv)."""
+    qs = _rows(q, "q", torch.bfloat16)
+    ks = _rows(kv, "kv", torch.bfloat16)
+    M, Nq = q.shape
+    Nkv = kv.shape[1]
+    if kv.shape[0] != M:
+        raise ValueError(f"q and kv must have the same number of rows ({M} vs {kv.shape[0]})")
+    if Nq % GROUP:
+        raise ValueError(f"q width {Nq} is not a multiple of {GROUP}")
+    _vector(gamma_q, "gamma_q", torch.bfloat16, Nq)
+    _vector(gamma_kv, "gamma_kv", torch.bfloat16, Nkv)
+    G = Nq // GROUP
+    sdt = E8M0_DTYPES if e8m0 else (torch.float32,)
+    if alloc:
+        dev = q.device
+        out_q = torch.empty((M, Nq), dtype=torch.uint8, device=dev) if out_q is None else out_q
+        out_scale = torch.empty(M * G, dtype=sdt[0], device=dev) if out_scale is None else out_scale
+        out_kv = torch.empty((M, Nkv), dtype=torch.bfloat16, device=dev) if out_kv is None else out_kv
+    _output(out_q, "out_q", Q_DTYPES, M * Nq)
+    _output(out_scale, "out_scale", sdt, M * G)
+    _output(out_kv, "out_kv", (torch.bfloat16,), M * Nkv)
+    if devices:
+        _same_gpu(q, "q", kv=kv, gamma_q=gamma_q, gamma_kv=gamma_kv, out_q=out_q, out_scale=out_scale,
+                  out_kv=out_kv)
+    return qs, ks, M, Nq, Nkv, out_q, (_u8(out_scale) if e8m0 else out_scale), out_kv
 
 
 def mi_fused_dual_rmsnorm_group_quant(q: torch.Tensor, kv: torch.Tensor,
@@ -145,44 +220,15 @@ def mi_fused_dual_rmsnorm_group_quant(q: torch.Tensor, kv: torch.Tensor,
     ``scale`` fp32 with logical shape [M, Nq/128] whose strides give the
     layout ((G, 1) row-major, or (1, M) when ``transpose_scale``), and
     ``kv_out`` bf16 [M, Nkv], contiguous."""
-    qs = _rows(q, "q", torch.bfloat16)
-    ks = _rows(kv, "kv", torch.bfloat16)
-    M, Nq = q.shape
-    Nkv = kv.shape[1]
-    if kv.shape[0] != M:
-        raise ValueError("q and kv must have the same number of rows")
-    if gamma_q.dtype != torch.bfloat16 or gamma_kv.dtype != torch.bfloat16:
-        raise ValueError("gammas must be bf16")
-    if not (gamma_q.is_contiguous() and gamma_kv.is_contiguous()):
-        raise ValueError("gammas must be contiguous")
-    if gamma_q.numel() != Nq or gamma_kv.numel() != Nkv:
-        raise ValueError("gamma sizes must match the row widths")
+    qs, ks, M, Nq, Nkv, out_q, out_scale, out_kv = _dual_args(
+        q, kv, gamma_q, gamma_kv, out_q, out_scale, out_kv, e8m0=False, alloc=True)
     G = Nq // GROUP
-    dev = q.device
-    if out_q is None:
-        out_q = torch.empty((M, Nq), dtype=torch.uint8, device=dev)
-    if out_scale is None:
-        out_scale = torch.empty(M * G, dtype=torch.float32, device=dev)
-    if out_kv is None:
-        out_kv = torch.empty((M, Nkv), dtype=torch.bfloat16, device=dev)
-    if not (out_q.is_contiguous() and out_kv.is_contiguous()):
-        raise ValueError("outputs must be contiguous")
-    if out_q.numel() < M * Nq or out_scale.numel() < M * G or out_kv.numel() < M * Nkv:
-        raise ValueError("output buffers too small")
     status = lib().mi_fused_dual_rmsnorm_group_quant(
         _ptr(q), qs, _ptr(kv), ks, _ptr(gamma_q), _ptr(gamma_kv), ctypes.c_float(eps),
         M, Nq, Nkv, int(bool(transpose_scale)), _ptr(out_q), _ptr(out_scale), _ptr(out_kv),
         _stream(q))
     _check("mi_fused_dual_rmsnorm_group_quant", status)
     return out_q, _scale_view(out_scale, M, G, transpose_scale), out_kv
-
-
-E8M0_DTYPES = (torch.uint8, getattr(torch, "float8_e8m0fnu", torch.uint8))
-
-
-def _u8(t: torch.Tensor) -> torch.Tensor:
-    """An e8m0 scale tensor as uint8 bytes (float8_e8m0fnu is viewed)."""
-    return t if t.dtype == torch.uint8 else t.view(torch.uint8)
 
 
 def mi_fused_dual_rmsnorm_group_quant_e8m0(q: torch.Tensor, kv: torch.Tensor,
@@ -194,19 +240,9 @@ def mi_fused_dual_rmsnorm_group_quant_e8m0(q: torch.Tensor, kv: torch.Tensor,
     """As :func:`mi_fused_dual_rmsnorm_group_quant` with e8m0 (power-of-two)
     scales: ``scale`` is a uint8 tensor of exponent bytes with logical shape
     [M, Nq/128] and the requested layout."""
-    qs = _rows(q, "q", torch.bfloat16)
-    ks = _rows(kv, "kv", torch.bfloat16)
-    M, Nq = q.shape
-    Nkv = kv.shape[1]
-    if kv.shape[0] != M or gamma_q.numel() != Nq or gamma_kv.numel() != Nkv:
-        raise ValueError("shape mismatch")
+    qs, ks, M, Nq, Nkv, out_q, out_scale, out_kv = _dual_args(
+        q, kv, gamma_q, gamma_kv, out_q, out_scale, out_kv, e8m0=True, alloc=True)
     G = Nq // GROUP
-    dev = q.device
-    out_q = torch.empty((M, Nq), dtype=torch.uint8, device=dev) if out_q is None else out_q
-    out_scale = torch.empty(M * G, dtype=torch.uint8, device=dev) if out_scale is None else _u8(out_scale)
-    out_kv = torch.empty((M, Nkv), dtype=torch.bfloat16, device=dev) if out_kv is None else out_kv
-    if out_q.numel() < M * Nq or out_scale.numel() < M * G or out_kv.numel() < M * Nkv:
-        raise ValueError("output buffers too small")
     status = lib().mi_fused_dual_rmsnorm_group_quant_e8m0(
         _ptr(q), qs, _ptr(kv), ks, _ptr(gamma_q), _ptr(gamma_kv), ctypes.c_float(eps),
         M, Nq, Nkv, int(bool(transpose_scale)), _ptr(out_q), _ptr(out_scale), _ptr(out_kv), _stream(q))
@@ -214,17 +250,23 @@ def mi_fused_dual_rmsnorm_group_quant_e8m0(q: torch.Tensor, kv: torch.Tensor,
     return out_q, _scale_view(out_scale, M, G, transpose_scale), out_kv
 
 
-def _quant_outputs(M: int, N: int, out_q, out_scale, device):
+def _single_args(x, gamma, out_q, out_scale, normalize: bool, alloc: bool):
+    """Checks of the single-input quantisations' operands (eager and
+    prepared).  Returns (row stride, M, N, out_q, out_scale)."""
+    xs = _rows(x, "x", torch.bfloat16)
+    M, N = x.shape
+    if N % GROUP:
+        raise ValueError(f"x width {N} is not a multiple of {GROUP}")
+    if normalize:
+        _vector(gamma, "gamma", torch.bfloat16, N)
     G = N // GROUP
-    if out_q is None:
-        out_q = torch.empty((M, N), dtype=torch.uint8, device=device)
-    if out_scale is None:
-        out_scale = torch.empty(M * G, dtype=torch.float32, device=device)
-    if not out_q.is_contiguous():
-        raise ValueError("out_q must be contiguous")
-    if out_q.numel() < M * N or out_scale.numel() < M * G:
-        raise ValueError("output buffers too small")
-    return out_q, out_scale
+    if alloc:
+        out_q = torch.empty((M, N), dtype=torch.uint8, device=x.device) if out_q is None else out_q
+        out_scale = torch.empty(M * G, dtype=torch.float32, device=x.device) if out_scale is None else out_scale
+    _output(out_q, "out_q", Q_DTYPES, M * N)
+    _output(out_scale, "out_scale", (torch.float32,), M * G)
+    _same_gpu(x, "x", gamma=gamma if normalize else None, out_q=out_q, out_scale=out_scale)
+    return xs, M, N, out_q, out_scale
 
 
 def _scale_view(out_scale: torch.Tensor, M: int, G: int, transpose_scale: bool) -> torch.Tensor:
@@ -237,11 +279,7 @@ def mi_rmsnorm_group_quant(x: torch.Tensor, gamma: torch.Tensor, eps: float, tra
     """Single-input RMSNorm + per-1x128 FP8 group quant on the current
     stream.  ``x`` [M, N] bf16 with unit inner stride; returns ``(x_fp8,
     scale)`` laid out as in :func:`mi_fused_dual_rmsnorm_group_quant`."""
-    xs = _rows(x, "x", torch.bfloat16)
-    M, N = x.shape
-    if gamma.dtype != torch.bfloat16 or not gamma.is_contiguous() or gamma.numel() != N:
-        raise ValueError("gamma must be a contiguous bf16 tensor of the row width")
-    out_q, out_scale = _quant_outputs(M, N, out_q, out_scale, x.device)
+    xs, M, N, out_q, out_scale = _single_args(x, gamma, out_q, out_scale, normalize=True, alloc=True)
     status = lib().mi_rmsnorm_group_quant(_ptr(x), xs, _ptr(gamma), ctypes.c_float(eps), M, N,
                                           int(bool(transpose_scale)), _ptr(out_q), _ptr(out_scale), _stream(x))
     _check("mi_rmsnorm_group_quant", status)
@@ -252,9 +290,7 @@ def mi_group_quant_1x128(x: torch.Tensor, transpose_scale: bool,
                          out_q: torch.Tensor | None = None, out_scale: torch.Tensor | None = None):
     """Per-1x128 dynamic FP8 quant of a bf16 activation (no normalisation)
     on the current stream; returns ``(x_fp8, scale)``."""
-    xs = _rows(x, "x", torch.bfloat16)
-    M, N = x.shape
-    out_q, out_scale = _quant_outputs(M, N, out_q, out_scale, x.device)
+    xs, M, N, out_q, out_scale = _single_args(x, None, out_q, out_scale, normalize=False, alloc=True)
     status = lib().mi_group_quant_1x128(_ptr(x), xs, M, N, int(bool(transpose_scale)), _ptr(out_q),
                                         _ptr(out_scale), _stream(x))
     _check("mi_group_quant_1x128", status)
@@ -262,13 +298,16 @@ def mi_group_quant_1x128(x: torch.Tensor, transpose_scale: bool,
 
 
 def scale_is_transposed(a_scale: torch.Tensor) -> bool:
-    """Layout of a [M, K/128] scale tensor, read from its strides."""
+    """Layout of a [M, K/128] scale tensor, read from its strides: False for
+    row-major (strides (K/128, 1)), True for column-major ((1, M)).  With one
+    row or one column both layouts hold the same bytes (False).  Any other
+    strides raise."""
     M, KB = a_scale.shape
-    if M == 1 or KB == 1:
-        return False          # both layouts hold the same bytes
-    if a_scale.stride() == (KB, 1):
+    row = (KB == 1 or a_scale.stride(1) == 1) and (M == 1 or a_scale.stride(0) == KB)
+    col = (M == 1 or a_scale.stride(0) == 1) and (KB == 1 or a_scale.stride(1) == M)
+    if row:
         return False
-    if a_scale.stride() == (1, M):
+    if col:
         return True
     raise ValueError(f"a_scale strides {a_scale.stride()} are neither row- nor column-major")
 
@@ -310,6 +349,7 @@ def relayout_weight(w: torch.Tensor) -> TiledWeight:
         raise TypeError("weight is already tiled: relaying it out again would permute it twice")
     if w.dtype != torch.uint8 or w.dim() != 2 or not w.is_contiguous():
         raise ValueError("w: expected a contiguous 2-D uint8 tensor")
+    _same_gpu(w, "w")
     N, K = w.shape
     dst = torch.empty(N * K, dtype=torch.uint8, device=w.device)
     status = lib().mi_relayout_weight(_ptr(w), MI_WEIGHT_ROW_MAJOR, _ptr(dst), MI_WEIGHT_TILED, N, K, _stream(w))
@@ -321,6 +361,7 @@ def untile_weight(tw: TiledWeight) -> torch.Tensor:
     """TiledWeight -> a new row-major uint8 [N, K] tensor."""
     if not isinstance(tw, TiledWeight):
         raise TypeError("expected a TiledWeight")
+    _same_gpu(tw.data, "tw.data")
     dst = torch.empty((tw.N, tw.K), dtype=torch.uint8, device=tw.device)
     status = lib().mi_relayout_weight(_ptr(tw.data), MI_WEIGHT_TILED, _ptr(dst), MI_WEIGHT_ROW_MAJOR, tw.N, tw.K,
                                       _stream(dst))
@@ -353,14 +394,16 @@ def _check_gemm_operands(a, a_scale, w, w_scale):
     M, K = a.shape
     if Kw != K or tuple(a_scale.shape) != (M, K // GROUP) or tuple(w_scale.shape) != (N // GROUP, K // GROUP):
         raise ValueError("shape mismatch between a, a_scale, w, w_scale")
+    scale_is_transposed(a_scale)  # raises unless row- or column-major
     return M, N, K, wd, wl
 
 
-def _gemm_out(out, M, N, device):
+def _gemm_out(out, M, N, device, name="out"):
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=device)
-    if out.dtype != torch.bfloat16 or not out.is_contiguous() or tuple(out.shape) != (M, N):
-        raise ValueError("out must be a contiguous bf16 [M, N] tensor")
+    if not isinstance(out, torch.Tensor) or out.dtype != torch.bfloat16 or not out.is_contiguous() or \
+            tuple(out.shape) != (M, N):
+        raise ValueError(f"{name} must be a contiguous bf16 [{M}, {N}] tensor")
     return out
 
 
@@ -377,6 +420,7 @@ def mi_block_scaled_fp8_gemm(a: torch.Tensor, a_scale: torch.Tensor, w, w_scale:
     if a_scale_transposed is not None and M > 1 and bool(a_scale_transposed) != layout:
         raise ValueError("a_scale_transposed disagrees with the strides of a_scale")
     out = _gemm_out(out, M, N, a.device)
+    _same_gpu(a, "a", a_scale=a_scale, w=wd, w_scale=w_scale, out=out)
     fn = "mi_block_scaled_fp8_gemm_e8m0" if a_scale.dtype in E8M0_DTYPES else "mi_block_scaled_fp8_gemm_ex"
     status = getattr(lib(), fn)(
         _ptr(a), _ptr(a_scale), int(layout), _ptr(wd), wl, _ptr(w_scale), _ptr(out), M, N, K, _stream(a))
@@ -396,8 +440,9 @@ def mi_block_scaled_fp8_gemm_pair(a: torch.Tensor, a_scale: torch.Tensor, w1, w1
     _, N2, _, wd2, wl2 = _check_gemm_operands(a, a_scale, w2, w2_scale)
     if wl1 != wl2:
         raise ValueError("both weights of a pair must have the same layout")
-    out1 = _gemm_out(out1, M, N1, a.device)
-    out2 = _gemm_out(out2, M, N2, a.device)
+    out1 = _gemm_out(out1, M, N1, a.device, "out1")
+    out2 = _gemm_out(out2, M, N2, a.device, "out2")
+    _same_gpu(a, "a", a_scale=a_scale, w1=wd1, w1_scale=w1_scale, w2=wd2, w2_scale=w2_scale, out1=out1, out2=out2)
     fn = "mi_block_scaled_fp8_gemm_pair_e8m0" if a_scale.dtype in E8M0_DTYPES else "mi_block_scaled_fp8_gemm_pair_ex"
     status = getattr(lib(), fn)(
         _ptr(a), _ptr(a_scale), int(scale_is_transposed(a_scale)), wl1, _ptr(wd1), _ptr(w1_scale), _ptr(out1), N1,
@@ -406,31 +451,31 @@ def mi_block_scaled_fp8_gemm_pair(a: torch.Tensor, a_scale: torch.Tensor, w1, w1
     return out1, out2
 
 
-def _step_operands(q, kv, gamma_q, gamma_kv, w1, w1_scale, w2, w2_scale):
-    qs = _rows(q, "q", torch.bfloat16)
-    ks = _rows(kv, "kv", torch.bfloat16)
-    M, Nq = q.shape
-    Nkv = kv.shape[1]
-    if kv.shape[0] != M:
-        raise ValueError("q and kv must have the same number of rows")
-    if gamma_q.dtype != torch.bfloat16 or gamma_kv.dtype != torch.bfloat16 or \
-            gamma_q.numel() != Nq or gamma_kv.numel() != Nkv or \
-            not (gamma_q.is_contiguous() and gamma_kv.is_contiguous()):
-        raise ValueError("gammas must be contiguous bf16 of the row widths")
-    e8m0 = w1_scale.dtype in E8M0_DTYPES
+def _step_operands(q, kv, gamma_q, gamma_kv, w1, w1_scale, w2, w2_scale, out_q, out_scale, out_kv, alloc):
+    """Checks of the one-call step (the dual norm-quant's, then both
+    weights'); returns the norm-quant's marshalled operands and outputs, the
+    scale type and (weight data, layout, N, scale) of both weights."""
+    e8m0 = isinstance(w1_scale, torch.Tensor) and w1_scale.dtype in E8M0_DTYPES
+    if out_scale is not None and isinstance(out_scale, torch.Tensor) and (out_scale.dtype in E8M0_DTYPES) != e8m0:
+        raise ValueError("out_scale must have the weight scales' type")
+    qs, ks, M, Nq, Nkv, out_q, out_scale, out_kv = _dual_args(
+        q, kv, gamma_q, gamma_kv, out_q, out_scale, out_kv, e8m0=e8m0, alloc=alloc, devices=False)
     ws = []
     for name, w, w_scale in (("w1", w1, w1_scale), ("w2", w2, w2_scale)):
         wd, wl, N, K = _weight_arg(w)
         if K != Nq:
             raise ValueError(f"{name}: K must equal the q width {Nq}")
-        ok_dtype = (w_scale.dtype in E8M0_DTYPES) if e8m0 else w_scale.dtype == torch.float32
+        ok_dtype = isinstance(w_scale, torch.Tensor) and (
+            (w_scale.dtype in E8M0_DTYPES) if e8m0 else w_scale.dtype == torch.float32)
         if not ok_dtype or not w_scale.is_contiguous() or tuple(w_scale.shape) != (N // GROUP, K // GROUP):
             raise ValueError(f"{name}: scale must be contiguous {'e8m0' if e8m0 else 'fp32'} [N/128, K/128]"
                              " (both weights' scales of one type)")
         ws.append((wd, wl, N, w_scale if not e8m0 else _u8(w_scale)))
     if ws[0][1] != ws[1][1]:
         raise ValueError("both weights of a pair must have the same layout")
-    return qs, ks, M, Nq, Nkv, e8m0, ws
+    _same_gpu(q, "q", kv=kv, gamma_q=gamma_q, gamma_kv=gamma_kv, out_q=out_q, out_scale=out_scale, out_kv=out_kv,
+              w1=ws[0][0], w1_scale=ws[0][3], w2=ws[1][0], w2_scale=ws[1][3])
+    return (qs, ks, M, Nq, Nkv, out_q, out_scale, out_kv), e8m0, ws
 
 
 def mi_fused_normquant_gemm_pair(q: torch.Tensor, kv: torch.Tensor, gamma_q: torch.Tensor,
@@ -445,23 +490,12 @@ def mi_fused_normquant_gemm_pair(q: torch.Tensor, kv: torch.Tensor, gamma_q: tor
     float8_e8m0fnu) the step is the e8m0 one
     (mi_fused_dual_rmsnorm_group_quant_e8m0, then the e8m0 pair) and
     ``scale`` holds exponent bytes."""
-    qs, ks, M, Nq, Nkv, e8m0, ((wd1, wl, N1, ws1), (wd2, _, N2, ws2)) = _step_operands(
-        q, kv, gamma_q, gamma_kv, w1, w1_scale, w2, w2_scale)
+    (qs, ks, M, Nq, Nkv, out_q, out_scale, out_kv), e8m0, ((wd1, wl, N1, ws1), (wd2, _, N2, ws2)) = \
+        _step_operands(q, kv, gamma_q, gamma_kv, w1, w1_scale, w2, w2_scale, out_q, out_scale, out_kv, alloc=True)
     G = Nq // GROUP
-    dev = q.device
-    sdt = torch.uint8 if e8m0 else torch.float32
-    out_q = torch.empty((M, Nq), dtype=torch.uint8, device=dev) if out_q is None else out_q
-    out_scale = torch.empty(M * G, dtype=sdt, device=dev) if out_scale is None else out_scale
-    if (out_scale.dtype in E8M0_DTYPES) != e8m0 or (not e8m0 and out_scale.dtype != torch.float32):
-        raise ValueError("out_scale must have the weight scales' type")
-    out_scale = _u8(out_scale) if e8m0 else out_scale
-    out_kv = torch.empty((M, Nkv), dtype=torch.bfloat16, device=dev) if out_kv is None else out_kv
-    if not (out_q.is_contiguous() and out_kv.is_contiguous() and out_scale.is_contiguous()):
-        raise ValueError("outputs must be contiguous")
-    if out_q.numel() < M * Nq or out_scale.numel() < M * G or out_kv.numel() < M * Nkv:
-        raise ValueError("output buffers too small")
-    out1 = _gemm_out(out1, M, N1, dev)
-    out2 = _gemm_out(out2, M, N2, dev)
+    out1 = _gemm_out(out1, M, N1, q.device, "out1")
+    out2 = _gemm_out(out2, M, N2, q.device, "out2")
+    _same_gpu(q, "q", out1=out1, out2=out2)
     fn = "mi_fused_normquant_gemm_pair_e8m0" if e8m0 else "mi_fused_normquant_gemm_pair"
     status = getattr(lib(), fn)(
         _ptr(q), qs, _ptr(kv), ks, _ptr(gamma_q), _ptr(gamma_kv), ctypes.c_float(eps), M, Nq, Nkv,
@@ -509,14 +543,9 @@ class PreparedCall:
 def prepare_fused_dual_rmsnorm_group_quant(q, kv, gamma_q, gamma_kv, eps, transpose_scale,
                                            out_q, out_scale, out_kv) -> PreparedCall:
     """Marshal the arguments of mi_fused_dual_rmsnorm_group_quant once (same
-    rules as :func:`mi_fused_dual_rmsnorm_group_quant`; outputs required)."""
-    qs = _rows(q, "q", torch.bfloat16)
-    ks = _rows(kv, "kv", torch.bfloat16)
-    M, Nq = q.shape
-    Nkv = kv.shape[1]
-    G = Nq // GROUP
-    if out_q.numel() < M * Nq or out_scale.numel() < M * G or out_kv.numel() < M * Nkv:
-        raise ValueError("output buffers too small")
+    checks as :func:`mi_fused_dual_rmsnorm_group_quant`; outputs required)."""
+    qs, ks, M, Nq, Nkv, out_q, out_scale, out_kv = _dual_args(
+        q, kv, gamma_q, gamma_kv, out_q, out_scale, out_kv, e8m0=False, alloc=False)
     args = (_ptr(q), qs, _ptr(kv), ks, _ptr(gamma_q), _ptr(gamma_kv), ctypes.c_float(eps),
             M, Nq, Nkv, int(bool(transpose_scale)), _ptr(out_q), _ptr(out_scale), _ptr(out_kv))
     return PreparedCall("mi_fused_dual_rmsnorm_group_quant", args,
@@ -525,9 +554,7 @@ def prepare_fused_dual_rmsnorm_group_quant(q, kv, gamma_q, gamma_kv, eps, transp
 
 def prepare_rmsnorm_group_quant(x, gamma, eps, transpose_scale, out_q, out_scale) -> PreparedCall:
     """Marshal the arguments of mi_rmsnorm_group_quant once (outputs required)."""
-    xs = _rows(x, "x", torch.bfloat16)
-    M, N = x.shape
-    _quant_outputs(M, N, out_q, out_scale, x.device)
+    xs, M, N, out_q, out_scale = _single_args(x, gamma, out_q, out_scale, normalize=True, alloc=False)
     args = (_ptr(x), xs, _ptr(gamma), ctypes.c_float(eps), M, N, int(bool(transpose_scale)), _ptr(out_q),
             _ptr(out_scale))
     return PreparedCall("mi_rmsnorm_group_quant", args, (x, gamma, out_q, out_scale), x.device)
@@ -535,9 +562,7 @@ def prepare_rmsnorm_group_quant(x, gamma, eps, transpose_scale, out_q, out_scale
 
 def prepare_group_quant_1x128(x, transpose_scale, out_q, out_scale) -> PreparedCall:
     """Marshal the arguments of mi_group_quant_1x128 once (outputs required)."""
-    xs = _rows(x, "x", torch.bfloat16)
-    M, N = x.shape
-    _quant_outputs(M, N, out_q, out_scale, x.device)
+    xs, M, N, out_q, out_scale = _single_args(x, None, out_q, out_scale, normalize=False, alloc=False)
     args = (_ptr(x), xs, M, N, int(bool(transpose_scale)), _ptr(out_q), _ptr(out_scale))
     return PreparedCall("mi_group_quant_1x128", args, (x, out_q, out_scale), x.device)
 
@@ -545,13 +570,8 @@ def prepare_group_quant_1x128(x, transpose_scale, out_q, out_scale) -> PreparedC
 def prepare_fused_dual_rmsnorm_group_quant_e8m0(q, kv, gamma_q, gamma_kv, eps, transpose_scale,
                                                 out_q, out_scale, out_kv) -> PreparedCall:
     """Marshal the arguments of mi_fused_dual_rmsnorm_group_quant_e8m0 once."""
-    qs = _rows(q, "q", torch.bfloat16)
-    ks = _rows(kv, "kv", torch.bfloat16)
-    M, Nq = q.shape
-    Nkv = kv.shape[1]
-    out_scale = _u8(out_scale)
-    if out_q.numel() < M * Nq or out_scale.numel() < M * (Nq // GROUP) or out_kv.numel() < M * Nkv:
-        raise ValueError("output buffers too small")
+    qs, ks, M, Nq, Nkv, out_q, out_scale, out_kv = _dual_args(
+        q, kv, gamma_q, gamma_kv, out_q, out_scale, out_kv, e8m0=True, alloc=False)
     args = (_ptr(q), qs, _ptr(kv), ks, _ptr(gamma_q), _ptr(gamma_kv), ctypes.c_float(eps),
             M, Nq, Nkv, int(bool(transpose_scale)), _ptr(out_q), _ptr(out_scale), _ptr(out_kv))
     return PreparedCall("mi_fused_dual_rmsnorm_group_quant_e8m0", args,
@@ -559,12 +579,14 @@ def prepare_fused_dual_rmsnorm_group_quant_e8m0(q, kv, gamma_q, gamma_kv, eps, t
 
 
 def prepare_block_scaled_fp8_gemm(a, a_scale, w, w_scale, out) -> PreparedCall:
-    """Marshal the arguments of mi_block_scaled_fp8_gemm_ex once; the As
-    layout is read from the strides of ``a_scale`` ([M, K/128]), the weight
-    layout from the type of ``w``."""
+    """Marshal the arguments of mi_block_scaled_fp8_gemm_ex (or its e8m0
+    form) once; the As layout is read from the strides of ``a_scale`` ([M,
+    K/128]), the weight layout from the type of ``w``."""
     M, N, K, wd, wl = _check_gemm_operands(a, a_scale, w, w_scale)
-    if tuple(out.shape) != (M, N):
-        raise ValueError("shape mismatch")
+    if out is None:
+        raise ValueError("out is required")
+    out = _gemm_out(out, M, N, a.device)
+    _same_gpu(a, "a", a_scale=a_scale, w=wd, w_scale=w_scale, out=out)
     args = (_ptr(a), _ptr(a_scale), int(scale_is_transposed(a_scale)), _ptr(wd), wl, _ptr(w_scale),
             _ptr(out), M, N, K)
     fn = "mi_block_scaled_fp8_gemm_e8m0" if a_scale.dtype in E8M0_DTYPES else "mi_block_scaled_fp8_gemm_ex"
@@ -572,13 +594,17 @@ def prepare_block_scaled_fp8_gemm(a, a_scale, w, w_scale, out) -> PreparedCall:
 
 
 def prepare_block_scaled_fp8_gemm_pair(a, a_scale, w1, w1_scale, out1, w2, w2_scale, out2) -> PreparedCall:
-    """Marshal the arguments of mi_block_scaled_fp8_gemm_pair_ex once."""
+    """Marshal the arguments of mi_block_scaled_fp8_gemm_pair_ex (or its
+    e8m0 form) once."""
     M, N1, K, wd1, wl1 = _check_gemm_operands(a, a_scale, w1, w1_scale)
     _, N2, _, wd2, wl2 = _check_gemm_operands(a, a_scale, w2, w2_scale)
     if wl1 != wl2:
         raise ValueError("both weights of a pair must have the same layout")
-    if tuple(out1.shape) != (M, N1) or tuple(out2.shape) != (M, N2):
-        raise ValueError("shape mismatch")
+    if out1 is None or out2 is None:
+        raise ValueError("out1 and out2 are required")
+    out1 = _gemm_out(out1, M, N1, a.device, "out1")
+    out2 = _gemm_out(out2, M, N2, a.device, "out2")
+    _same_gpu(a, "a", a_scale=a_scale, w1=wd1, w1_scale=w1_scale, w2=wd2, w2_scale=w2_scale, out1=out1, out2=out2)
     args = (_ptr(a), _ptr(a_scale), int(scale_is_transposed(a_scale)), wl1, _ptr(wd1), _ptr(w1_scale), _ptr(out1),
             N1, _ptr(wd2), _ptr(w2_scale), _ptr(out2), N2, M, K)
     fn = "mi_block_scaled_fp8_gemm_pair_e8m0" if a_scale.dtype in E8M0_DTYPES else "mi_block_scaled_fp8_gemm_pair_ex"
@@ -588,17 +614,15 @@ def prepare_block_scaled_fp8_gemm_pair(a, a_scale, w1, w1_scale, out1, w2, w2_sc
 def prepare_fused_normquant_gemm_pair(q, kv, gamma_q, gamma_kv, eps, transpose_scale, w1, w1_scale, w2, w2_scale,
                                       out_q, out_scale, out_kv, out1, out2) -> PreparedCall:
     """Marshal the arguments of mi_fused_normquant_gemm_pair (or its e8m0
-    form, chosen by the weight scales' type) once (outputs required)."""
-    qs, ks, M, Nq, Nkv, e8m0, ((wd1, wl, N1, ws1), (wd2, _, N2, ws2)) = _step_operands(
-        q, kv, gamma_q, gamma_kv, w1, w1_scale, w2, w2_scale)
-    G = Nq // GROUP
-    if (out_scale.dtype in E8M0_DTYPES) != e8m0:
-        raise ValueError("out_scale must have the weight scales' type")
-    out_scale = _u8(out_scale) if e8m0 else out_scale
-    if out_q.numel() < M * Nq or out_scale.numel() < M * G or out_kv.numel() < M * Nkv:
-        raise ValueError("output buffers too small")
-    if tuple(out1.shape) != (M, N1) or tuple(out2.shape) != (M, N2):
-        raise ValueError("shape mismatch")
+    form, chosen by the weight scales' type) once (outputs required; the
+    same checks as :func:`mi_fused_normquant_gemm_pair`)."""
+    if out_q is None or out_scale is None or out_kv is None or out1 is None or out2 is None:
+        raise ValueError("all five outputs are required")
+    (qs, ks, M, Nq, Nkv, out_q, out_scale, out_kv), e8m0, ((wd1, wl, N1, ws1), (wd2, _, N2, ws2)) = \
+        _step_operands(q, kv, gamma_q, gamma_kv, w1, w1_scale, w2, w2_scale, out_q, out_scale, out_kv, alloc=False)
+    out1 = _gemm_out(out1, M, N1, q.device, "out1")
+    out2 = _gemm_out(out2, M, N2, q.device, "out2")
+    _same_gpu(q, "q", out1=out1, out2=out2)
     args = (_ptr(q), qs, _ptr(kv), ks, _ptr(gamma_q), _ptr(gamma_kv), ctypes.c_float(eps), M, Nq, Nkv,
             int(bool(transpose_scale)), _ptr(out_q), _ptr(out_scale), _ptr(out_kv),
             wl, _ptr(wd1), _ptr(ws1), _ptr(out1), N1, _ptr(wd2), _ptr(ws2), _ptr(out2), N2)

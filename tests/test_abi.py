@@ -290,3 +290,166 @@ def test_fused_step_launch_count(L):
     assert f(-1, 1536, 512, 24576, 8192) == -1
     assert f(1, 1500, 512, 24576, 8192) == -1
     assert f(1, 1536, 512, 1000, 8192) == -1
+
+
+# ---- binding-side validation (CPU tensors: every check below raises before
+# any library call, so no GPU is touched) ----
+
+def _dual_cpu(M=4, Nq=1536, Nkv=512):
+    import torch
+    buf = torch.zeros((M, Nq + Nkv), dtype=torch.bfloat16)
+    return dict(q=buf[:, :Nq], kv=buf[:, Nq:], gamma_q=torch.ones(Nq, dtype=torch.bfloat16),
+                gamma_kv=torch.ones(Nkv, dtype=torch.bfloat16), eps=1e-6, transpose_scale=True,
+                out_q=torch.empty((M, Nq), dtype=torch.uint8), out_scale=torch.empty(M * (Nq // 128)),
+                out_kv=torch.empty((M, Nkv), dtype=torch.bfloat16))
+
+
+def _e8m0(a):
+    import torch
+    a = dict(a)
+    a["out_scale"] = torch.empty(a["out_scale"].numel(), dtype=torch.uint8)
+    return a
+
+
+DUAL_CALLS = (
+    ("eager", lambda a: mi.mi_fused_dual_rmsnorm_group_quant(**a)),
+    ("prepared", lambda a: mi.prepare_fused_dual_rmsnorm_group_quant(**a)),
+    ("eager_e8m0", lambda a: mi.mi_fused_dual_rmsnorm_group_quant_e8m0(**_e8m0(a))),
+    ("prepared_e8m0", lambda a: mi.prepare_fused_dual_rmsnorm_group_quant_e8m0(**_e8m0(a))),
+)
+
+
+@pytest.mark.parametrize("name,call", DUAL_CALLS, ids=[n for n, _ in DUAL_CALLS])
+def test_dual_binding_checks(name, call):
+    """Each form of the dual norm-quant (eager, prepared, fp32 and e8m0
+    scales) runs the same checks: unit inner stride at every row count
+    (a strided single row included), kv rows == q rows, gammas bf16,
+    contiguous and of the row widths, contiguous outputs of the right type
+    and size, and every tensor on the GPU of q."""
+    import torch
+    ok = _dual_cpu()
+    with pytest.raises(ValueError, match="GPU tensor"):   # valid except for the device
+        call(ok)
+    one = _dual_cpu(M=1)
+    one["q"] = torch.zeros((1, 3072), dtype=torch.bfloat16)[:, ::2]   # strides (3072, 2)
+    with pytest.raises(ValueError, match="inner stride"):
+        call(one)
+    for key, value, msg in (
+            ("kv", torch.zeros((3, 512), dtype=torch.bfloat16), "same number of rows"),
+            ("gamma_q", torch.ones(1535, dtype=torch.bfloat16), "gamma_q"),
+            ("gamma_kv", torch.ones(512, dtype=torch.float32), "gamma_kv"),
+            ("gamma_q", torch.ones(3072, dtype=torch.bfloat16)[::2], "gamma_q"),
+            ("out_q", torch.empty((1536, 4), dtype=torch.uint8).T, "contiguous"),
+            ("out_kv", torch.empty((4, 511), dtype=torch.bfloat16), "too small"),
+            ("out_kv", torch.empty((4, 512), dtype=torch.float16), "out_kv")):
+        bad = _dual_cpu()
+        bad[key] = value
+        with pytest.raises(ValueError, match=msg):
+            call(bad)
+    if "e8m0" in name:
+        with pytest.raises(ValueError, match="out_scale"):  # fp32 scales where bytes are written
+            fn = (mi.mi_fused_dual_rmsnorm_group_quant_e8m0 if name == "eager_e8m0"
+                  else mi.prepare_fused_dual_rmsnorm_group_quant_e8m0)
+            fn(**_dual_cpu())
+    else:
+        bad = _dual_cpu()
+        bad["out_scale"] = torch.empty(48, dtype=torch.uint8)
+        with pytest.raises(ValueError, match="out_scale"):
+            call(bad)
+
+
+@pytest.mark.parametrize("prepared", [False, True])
+@pytest.mark.parametrize("normalize", [False, True])
+def test_single_input_binding_checks(prepared, normalize):
+    import torch
+    M, N = 4, 1536
+
+    def call(x, gamma=None, out_q=None, out_scale=None):
+        out_q = torch.empty((M, N), dtype=torch.uint8) if out_q is None else out_q
+        out_scale = torch.empty(M * 12) if out_scale is None else out_scale
+        gamma = torch.ones(N, dtype=torch.bfloat16) if gamma is None else gamma
+        if normalize:
+            f = mi.prepare_rmsnorm_group_quant if prepared else mi.mi_rmsnorm_group_quant
+            return f(x, gamma, 1e-6, True, out_q, out_scale)
+        f = mi.prepare_group_quant_1x128 if prepared else mi.mi_group_quant_1x128
+        return f(x, True, out_q, out_scale)
+
+    x = torch.zeros((M, N), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        call(x)
+    with pytest.raises(ValueError, match="inner stride"):
+        call(torch.zeros((1, 2 * N), dtype=torch.bfloat16)[:, ::2])
+    with pytest.raises(ValueError, match="contiguous"):
+        call(x, out_q=torch.empty((N, M), dtype=torch.uint8).T)
+    with pytest.raises(ValueError, match="out_scale"):
+        call(x, out_scale=torch.empty(M * 12, dtype=torch.float16))
+    if normalize:
+        with pytest.raises(ValueError, match="gamma"):
+            call(x, gamma=torch.ones(N, dtype=torch.float32))
+        with pytest.raises(ValueError, match="gamma"):
+            call(x, gamma=torch.ones(N - 128, dtype=torch.bfloat16))
+
+
+@pytest.mark.parametrize("prepared", [False, True])
+def test_gemm_binding_checks(prepared):
+    """The GEMM calls check operand types, shapes and the As strides, and
+    that every tensor sits on the GPU of the activation."""
+    import torch
+    M, N, K = 4, 256, 1536
+    a = torch.zeros((M, K), dtype=torch.uint8)
+    a_s = torch.ones((M, K // 128))
+    w = torch.zeros((N, K), dtype=torch.uint8)
+    w_s = torch.ones((N // 128, K // 128))
+    out = torch.empty((M, N), dtype=torch.bfloat16)
+
+    def call(a=a, a_s=a_s, w=w, w_s=w_s, out=out):
+        if prepared:
+            return mi.prepare_block_scaled_fp8_gemm(a, a_s, w, w_s, out)
+        return mi.mi_block_scaled_fp8_gemm(a, a_s, w, w_s, out)
+
+    with pytest.raises(ValueError, match="GPU tensor"):
+        call()
+    with pytest.raises(ValueError, match="neither row- nor column-major"):
+        call(a_s=torch.ones((M, 2 * K // 128))[:, ::2])
+    with pytest.raises(ValueError, match="neither row- nor column-major"):
+        call(a_s=torch.ones((1, 2 * K // 128))[:, ::2], a=a[:1], out=out[:1])
+    with pytest.raises(ValueError, match="shape mismatch"):
+        call(w_s=torch.ones((1, K // 128)))
+    with pytest.raises(ValueError, match="out"):
+        call(out=torch.empty((M, N), dtype=torch.float32))
+    with pytest.raises(ValueError, match="out"):
+        call(out=torch.empty((N, M), dtype=torch.bfloat16).T)
+    assert B.scale_is_transposed(torch.ones((12, M)).T) is True
+    assert B.scale_is_transposed(torch.ones((M, 12))) is False
+    assert B.scale_is_transposed(torch.ones((1, 12))) is False
+
+
+@pytest.mark.parametrize("prepared", [False, True])
+def test_step_binding_checks(prepared):
+    """The one-call step runs the dual norm-quant's checks (short kv, short
+    gamma, device) and the weights' ones."""
+    import torch
+    base = _dual_cpu()
+    W1 = torch.zeros((256, 1536), dtype=torch.uint8)
+    W2 = torch.zeros((128, 1536), dtype=torch.uint8)
+    S1, S2 = torch.ones((2, 12)), torch.ones((1, 12))
+    out1 = torch.empty((4, 256), dtype=torch.bfloat16)
+    out2 = torch.empty((4, 128), dtype=torch.bfloat16)
+
+    def call(**kw):
+        a = dict(base)
+        a.update(kw)
+        args = (a["q"], a["kv"], a["gamma_q"], a["gamma_kv"], 1e-6, True, W1, a.get("S1", S1), W2, S2)
+        outs = dict(out_q=a["out_q"], out_scale=a["out_scale"], out_kv=a["out_kv"], out1=out1, out2=out2)
+        if prepared:
+            return mi.prepare_fused_normquant_gemm_pair(*args, **outs)
+        return mi.mi_fused_normquant_gemm_pair(*args, **outs)
+
+    with pytest.raises(ValueError, match="GPU tensor"):
+        call()
+    with pytest.raises(ValueError, match="same number of rows"):
+        call(kv=torch.zeros((2, 512), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="gamma_kv"):
+        call(gamma_kv=torch.ones(100, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="w1"):
+        call(S1=torch.ones((2, 12), dtype=torch.float64))
