@@ -64,6 +64,9 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true", help="skip the M=1 / M=8192 / M=256 extras")
     ap.add_argument("--no-warm", action="store_true", help="skip the labelled warm-cache figures")
     ap.add_argument("--kernel-loop", default="", help="only launch this kernel in a loop (profiling)")
+    ap.add_argument("--profile-loop", default="",
+                    help="comma-separated profiling loops (" + ", ".join(PROFILE_LOOPS) + "), run in turn")
+    ap.add_argument("--flush", action="store_true", help="profiling loop nq1: evict the caches between launches")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 64 MiB device copy in a loop (scales the HBM byte counters)")
     return ap.parse_args()
@@ -105,6 +108,48 @@ def source_sha(*names):
         with open(os.path.join(ROOT, "rmsnorm_fp8_block_amd", "csrc", n), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+MEDIANS_FILE = os.path.join(ROOT, "profiles", "kernel_medians.json")
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_counters.json")
+
+
+def roofline_frac(flops, nbytes, us):
+    """Achieved / min(FP8 MFMA peak, arithmetic intensity x HBM peak), i.e.
+    the larger of the two ideal times over the measured time."""
+    t_ideal = max(flops / (FP8_MFMA_PEAK_TFLOPS * 1e6), nbytes / (HBM_PEAK_GBS * 1e3))
+    return round(t_ideal / us, 4)
+
+
+def mfma_counters(M, N, e8m0=False):
+    """MFMA-busy figures committed under profiles/ (rocprofv3 --pmc
+    SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_F8, GRBM_GUI_ACTIVE) for
+    the GEMM at this shape, if taken on the current kernel source."""
+    try:
+        with open(MFMA_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    sha = source_sha(*GEMM_SOURCES)
+    for e in t.values():
+        if e.get("M") == M and e.get("N") == N and bool(e.get("e8m0")) == e8m0 and e.get("source_sha") == sha:
+            return {k: e[k] for k in ("mfma_busy_frac", "mfma_busy_cycles", "gui_active_cycles_per_xcd",
+                                      "mops_f8") if k in e}
+    return None
+
+
+def kernel_medians(sources):
+    """rocprofv3 kernel-trace medians committed under profiles/ for the
+    kernel built from these sources (None when the source has changed since
+    they were taken)."""
+    try:
+        with open(MEDIANS_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    sha = source_sha(*sources)
+    out = {k: v for k, v in t.items() if isinstance(v, dict) and v.get("source_sha") == sha}
+    return out or None
 
 
 def measured_traffic(kernel, sha, M):
@@ -151,6 +196,22 @@ def make_graph(torch, fns):
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    return g
+
+
+CHUNK = 2000  # steps per captured graph in the timed region
+
+
+def capture(torch, fns):
+    """Capture the given launches as a graph, with no eager run first (the
+    kernels' device set-up is done by mi_init before any capture)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
         for f in fns:
             f()
     torch.cuda.synchronize()
@@ -232,22 +293,68 @@ def build_sets(torch, np, mi, W, M, layout, wa, wb, nsets, dev, tiled):
     return sets
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(np, W, M, layout, wa, wb):
-    """The oracle as it stands, on this host: one full step (norm-quant of
-    the same M rows, then both GEMMs over all their columns).  Returns the
-    bench entry and the oracle's outputs (q codes, scales in storage order,
-    kv bf16 bits, both GEMM outputs in fp64)."""
+    """The oracle as it stands, on this host, in the same run.
+    - Norm-quant legs at M = 1 (decode_single), 64 (strided batch) and 8192
+      (prefill): single-threaded and on every core this process may use,
+      median of 100 runs (M <= 256) or 5 (M = 8192), as us/call and the
+      equivalent GB/s of the same algorithmic bytes as the GPU kernel.
+    - The step (``value``): the norm-quant of the step's M rows and both GEMMs
+      over all their columns, once, on every core.
+    Returns the bench entry and the step's oracle outputs (q codes, scales in
+    storage order, kv bf16 bits, both GEMM outputs in fp64)."""
+    import ctypes
     import oracle
+    oracle.lib()
+    try:  # the oracle's OpenMP runtime (gcc's libgomp, loaded with it)
+        gomp = ctypes.CDLL("libgomp.so.1")
+        set_threads = gomp.omp_set_num_threads
+    except OSError:
+        set_threads = None
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    if os.environ.get("OMP_NUM_THREADS", "").isdigit():  # the host's share of CPUs, where it is set
+        cores = max(1, min(cores, int(os.environ["OMP_NUM_THREADS"])))
+    legs = {}
+    for Mx, reps in ((1, 100), (64, 100), (8192, 5)):
+        case = W.decode_single() if Mx == 1 else W.strided_batch(Mx) if Mx == 64 else W.prefill(Mx)
+        for threads in ((1, cores) if set_threads else (None,)):
+            if set_threads:
+                set_threads(threads)
+            ts = []
+            for _ in range(reps):
+                t0 = time.perf_counter()
+                oracle.dual_rmsnorm_group_quant(case.q, case.kv, case.gamma_q, case.gamma_kv, W.EPS, layout)
+                ts.append(time.perf_counter() - t0)
+            us = float(np.median(ts)) * 1e6
+            legs[f"normquant_M{Mx}_{oracle.num_threads()}t"] = {
+                "us_median": round(us, 1), "runs": reps,
+                "GB/s": round(algorithmic_bytes_normquant(Mx) / us / 1e3, 3)}
+    if set_threads:
+        set_threads(cores)
     case = W.producer_activations(M) if M <= 256 else W.strided_batch(M)
     t0 = time.perf_counter()
     r = oracle.dual_rmsnorm_group_quant(case.q, case.kv, case.gamma_q, case.gamma_kv, W.EPS, layout)
     o1 = oracle.block_scaled_fp8_gemm(r["q"], r["scale"], layout, wa.codes, wa.scale)
     o2 = oracle.block_scaled_fp8_gemm(r["q"], r["scale"], layout, wb.codes, wb.scale)
     dt = time.perf_counter() - t0
-    entry = {"value": round(dt * 1e6, 1), "unit": "µs/step", "cores": oracle.num_threads(),
-             "kind": "oracle",
+    flops = gemm_flops(M, wa.codes.shape[0] + wb.codes.shape[0], W.NQ)
+    entry = {"value": round(dt * 1e6, 1), "unit": "µs/step", "cores": oracle.num_threads(), "kind": "oracle",
              "sample": f"one full step at M={M}: fp64 norm-quant of {M} rows + both GEMMs over all "
-                       f"{wa.codes.shape[0] + wb.codes.shape[0]} output columns ({dt:.1f} s wall)"}
+                       f"{wa.codes.shape[0] + wb.codes.shape[0]} output columns ({dt:.1f} s wall, "
+                       f"{flops / dt / 1e9:.2f} GFLOP/s), on {oracle.num_threads()} threads; norm-quant legs "
+                       "below: median of 100 runs (M <= 64) or 5 (M = 8192), 1 thread and all threads",
+             "cpu_model": cpu_model(), "host_cpus_usable": cores, "legs": legs}
     return entry, (r["q"], r["scale"], r["kv"], o1, o2)
 
 
@@ -304,8 +411,12 @@ def sweep(torch, np, mi, W, wa, wb, dev, cold, tiled):
             torch.empty(12, dtype=torch.float32, device=dev),
             torch.empty(512, dtype=torch.bfloat16, device=dev)))
     g = make_graph(torch, fns)
-    res["normquant_M1_us_per_call_graph"] = round(time_graph(torch, g, len(fns), 20), 3)
-    res["normquant_M1_us_per_call_eager"] = round(time_eager(torch, fns, 2000), 3)
+    res["normquant_M1"] = {
+        "us_per_call_graph": round(time_graph(torch, g, len(fns), 20), 3),
+        "us_per_call_eager": round(time_eager(torch, fns, 2000), 3),
+        "cache": "warm (64 sets of 10.8 KB: Infinity Cache and L2 resident, as the decode step's freshly "
+                 "written latents are)",
+        "rocprof_median_us": kernel_medians(NORMQUANT_SOURCES)}
     del g, fns
     # M = 256 (a batch of 256 tokens: the outlier workload's rows),
     # column-major scales, many buffer sets in one graph
@@ -321,7 +432,8 @@ def sweep(torch, np, mi, W, wa, wb, dev, cold, tiled):
             torch.empty((256, 512), dtype=torch.bfloat16, device=dev)))
     g = make_graph(torch, fns)
     us = time_graph(torch, g, len(fns), 20)
-    res["normquant_M256_col"] = {"us": round(us, 3), "GB/s": round(algorithmic_bytes_normquant(256) / us / 1e3, 1)}
+    res["normquant_M256_col"] = {"us": round(us, 3), "GB/s": round(algorithmic_bytes_normquant(256) / us / 1e3, 1),
+                                 "cache": "warm (32 sets of 1.7 MB: Infinity Cache resident)"}
     del g, fns, b256
     # M = 8192 prefill, both layouts
     pre = W.prefill(8192)
@@ -520,7 +632,9 @@ def sweep(torch, np, mi, W, wa, wb, dev, cold, tiled):
         tf = gemm_flops(M, N, 1536) / us / 1e6
         res[f"e8m0_gemm_{name}_M256"] = {"us": round(us, 3), "TFLOP/s": round(tf, 1),
                                          "frac_fp8_mfma": round(tf / FP8_MFMA_PEAK_TFLOPS, 4),
-                                         "GB/s": round(perg / us / 1e3, 1)}
+                                         "GB/s": round(perg / us / 1e3, 1),
+                                         "roofline_frac": roofline_frac(gemm_flops(M, N, 1536), perg, us),
+                                         "mfma_counters": mfma_counters(M, N, e8m0=True)}
         del g, fns
     del eac0, ebc0
     torch.cuda.empty_cache()
@@ -544,7 +658,9 @@ def sweep(torch, np, mi, W, wa, wb, dev, cold, tiled):
         tf = gemm_flops(M, N, K) / us / 1e6
         res[f"gemm_{name}_M256"] = {"us": round(us, 3), "TFLOP/s": round(tf, 1),
                                     "frac_fp8_mfma": round(tf / FP8_MFMA_PEAK_TFLOPS, 4),
-                                    "GB/s": round(per / us / 1e3, 1)}
+                                    "GB/s": round(per / us / 1e3, 1),
+                                    "roofline_frac": roofline_frac(gemm_flops(M, N, K), per, us),
+                                    "mfma_counters": mfma_counters(M, N)}
         del g, fns
         torch.cuda.empty_cache()
 
@@ -564,6 +680,162 @@ def sweep(torch, np, mi, W, wa, wb, dev, cold, tiled):
         del sets
         torch.cuda.empty_cache()
     return res
+
+
+def ceilings(torch, np, W):
+    """Measured data-movement ceilings of this GPU for the kernels' access
+    patterns (libmi_ceiling.so: hand-written skeletons that move the same
+    bytes with no arithmetic), cold (buffer sets rotated past 2x the Infinity
+    Cache), HIP events around back-to-back launches:
+      normquant_M8192: the dual norm-quant's reads and writes at 8192 rows;
+      weight_stream_{W_a,W_b,pair}: every weight byte of the GEMM read once
+      from HBM into LDS by 256 workgroups (the floor of any GEMM kernel
+      that streams that weight, before activations and outputs)."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "rmsnorm_fp8_block_amd", "libmi_ceiling.so"))
+    p, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.mi_ceiling_normquant_skeleton.argtypes = [p, i64, p, p, p, i64, p]
+    lib.mi_ceiling_weight_stream.argtypes = [p, i64, i64, p, p]
+    dev = torch.device("cuda:0")
+    stream = lambda: ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    res = {}
+    M = 8192
+    nbytes = algorithmic_bytes_normquant(M)
+    sets = []
+    for _ in range(2 * MALL_BYTES // nbytes + 2):
+        sets.append((torch.empty((M, 2048), dtype=torch.bfloat16, device=dev).normal_(),
+                     torch.empty((M, 1536), dtype=torch.uint8, device=dev),
+                     torch.empty(M * 12, dtype=torch.float32, device=dev),
+                     torch.empty((M, 512), dtype=torch.bfloat16, device=dev)))
+
+    def nq(i):
+        b, q, sc, kv = sets[i % len(sets)]
+        st = lib.mi_ceiling_normquant_skeleton(b.data_ptr(), 2048, q.data_ptr(), sc.data_ptr(), kv.data_ptr(), M,
+                                               stream())
+        if st != 0:
+            raise RuntimeError(f"mi_ceiling_normquant_skeleton: hip error {st}")
+    fns = [lambda i=i: nq(i) for i in range(len(sets))]
+    us = time_eager(torch, fns, 20 * len(fns))
+    res["normquant_M8192"] = {"us": round(us, 3), "GB/s": round(nbytes / us / 1e3, 1),
+                              "frac_hbm": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
+                              "what": "dual norm-quant data movement at 8192 rows (reads 4096 B and writes 2608 B "
+                                      "per row, the kernel's launch shape and store widths, no arithmetic)"}
+    del sets, fns
+    torch.cuda.empty_cache()
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    for name, n in (("W_a", W.W_A_SHAPE[0]), ("W_b", W.W_B_SHAPE[0]), ("pair", W.W_A_SHAPE[0] + W.W_B_SHAPE[0])):
+        wbytes = n * W.NQ
+        slab = wbytes // 256
+        bufs = [torch.empty(wbytes, dtype=torch.uint8, device=dev).fill_(1)
+                for _ in range(2 * MALL_BYTES // wbytes + 2)]
+
+        def ws(i, bufs=bufs, slab=slab):
+            st = lib.mi_ceiling_weight_stream(bufs[i % len(bufs)].data_ptr(), slab, 256, sink.data_ptr(), stream())
+            if st != 0:
+                raise RuntimeError(f"mi_ceiling_weight_stream: hip error {st}")
+        fns = [lambda i=i: ws(i) for i in range(len(bufs))]
+        us = time_eager(torch, fns, 20 * len(fns))
+        res[f"weight_stream_{name}"] = {"us": round(us, 3), "bytes": wbytes, "GB/s": round(wbytes / us / 1e3, 1),
+                                        "frac_hbm": round(wbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+        del bufs, fns
+        torch.cuda.empty_cache()
+    return res
+
+
+PROFILE_LOOPS = ("nq1", "nq8192_row", "nq8192_col", "gemm_a256", "gemm_b256", "gemm_a256_e8m0",
+                 "gemm_b256_e8m0", "pair64")
+
+
+def profile_loops(torch, np, mi, W, names, steps, tiled, flush):
+    """Profiling aid: for each named loop in turn, ``steps`` back-to-back
+    launches of one kernel over buffer sets rotated past twice the Infinity
+    Cache (cold), after 3 untimed rounds; prints one JSON line per loop with
+    its launch order, so a rocprofv3 trace of the run splits by position.
+      nq1           dual norm-quant, M = 1 (decode_single); with ``flush`` a
+                    512 MiB fill runs between launches so every launch finds
+                    its input and weights of RMSNorm out of the caches
+      nq8192_row/col  dual norm-quant of the prefill batch, both layouts
+      gemm_{a,b}256[_e8m0]  W_a / W_b GEMM at M = 256, fp32 or e8m0 scales
+      pair64        both GEMMs at M = 64 (the decode step's pair launch)"""
+    dev = torch.device("cuda:0")
+    gq = bf16_dev(torch, np, W.gammas()[0], dev)
+    gk = bf16_dev(torch, np, W.gammas()[1], dev)
+
+    def cold_sets(nbytes):
+        return max(2, (2 * MALL_BYTES) // nbytes + 1)
+
+    def dev_weight(codes):
+        w = torch.from_numpy(np.ascontiguousarray(codes)).to(dev)
+        return mi.relayout_weight(w) if tiled else w
+
+    def copy_weight(w):
+        return mi.TiledWeight(w.data.clone(), w.N, w.K) if isinstance(w, mi.TiledWeight) else w.clone()
+
+    order = 0
+    for name in names:
+        fns, extra = [], None
+        if name == "nq1":
+            one = W.decode_single()
+            q0, k0 = bf16_dev(torch, np, one.q, dev), bf16_dev(torch, np, one.kv, dev)
+            for i in range(64):
+                fns.append(mi.prepare_fused_dual_rmsnorm_group_quant(
+                    q0.clone(), k0.clone(), gq.clone(), gk.clone(), W.EPS, False,
+                    torch.empty(1536, dtype=torch.uint8, device=dev), torch.empty(12, dtype=torch.float32, device=dev),
+                    torch.empty(512, dtype=torch.bfloat16, device=dev)))
+            if flush:
+                junk = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+                extra = lambda: junk.fill_(1)
+        elif name.startswith("nq8192"):
+            pre = W.prefill(8192)
+            b0 = bf16_dev(torch, np, pre.buffer, dev)
+            layout = 1 if name.endswith("col") else 0
+            for i in range(cold_sets(algorithmic_bytes_normquant(8192))):
+                b = b0 if i == 0 else b0.clone()
+                fns.append(mi.prepare_fused_dual_rmsnorm_group_quant(
+                    b[:, :W.NQ], b[:, W.NQ:], gq, gk, W.EPS, layout,
+                    torch.empty((8192, 1536), dtype=torch.uint8, device=dev),
+                    torch.empty(8192 * 12, dtype=torch.float32, device=dev),
+                    torch.empty((8192, 512), dtype=torch.bfloat16, device=dev)))
+        elif name.startswith("gemm_"):
+            M = 256
+            e8m0 = name.endswith("e8m0")
+            shape, seed = (W.W_A_SHAPE, W.W_A_SEED) if name.startswith("gemm_a") else (W.W_B_SHAPE, W.W_B_SEED)
+            wt = (W.block_fp8_weight_e8m0 if e8m0 else W.block_fp8_weight)(*shape, seed)
+            N, K = shape
+            a = torch.randint(0, 0x78, (M, K), dtype=torch.uint8, device=dev)
+            asc = (torch.randint(118, 127, (K // 128, M), dtype=torch.uint8, device=dev) if e8m0 else
+                   torch.rand((K // 128, M), dtype=torch.float32, device=dev) + 0.5).T
+            w0 = dev_weight(wt.codes)
+            ws = torch.from_numpy(wt.scale).to(dev)
+            for i in range(cold_sets(algorithmic_bytes_gemm(M, N, K))):
+                fns.append(mi.prepare_block_scaled_fp8_gemm(
+                    a, asc, w0 if i == 0 else copy_weight(w0), ws,
+                    torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
+        elif name == "pair64":
+            sets = build_sets(torch, np, mi, W, 64, 1, W.block_fp8_weight(*W.W_A_SHAPE, W.W_A_SEED),
+                              W.block_fp8_weight(*W.W_B_SHAPE, W.W_B_SEED),
+                              cold_sets(algorithmic_bytes_gemm_pair(64, W.W_A_SHAPE[0], W.W_B_SHAPE[0], W.NQ)), dev,
+                              tiled)
+            fns = [st["gp"] for st in sets]
+        else:
+            raise SystemExit(f"unknown profile loop {name!r}; known: {', '.join(PROFILE_LOOPS)}")
+        seq = []
+        for f in fns:
+            seq += [extra, f] if extra else [f]
+        for i in range(3 * len(seq)):          # untimed rounds
+            seq[i % len(seq)]()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps * (2 if extra else 1)):
+            seq[i % len(seq)]()
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        print(json.dumps({"profile_loop": name, "first_launch": order, "warmup_launches": 3 * len(fns),
+                          "launches": steps, "sets": len(fns), "interleaved_flush": bool(extra),
+                          "wall_us_per_launch": round(1e6 * dt / steps, 3)}), flush=True)
+        order += 3 * len(fns) + steps
+        del fns, seq
+        torch.cuda.empty_cache()
 
 
 def calibrate_copy(torch, steps):
@@ -599,6 +871,11 @@ def main():
     from rmsnorm_fp8_block_amd import workloads as W
 
     mi.lib()  # fails loudly if the HIP library is missing
+    mi.mi_init()
+    if args.profile_loop:
+        tiled = args.weight_layout != "row"
+        profile_loops(torch, np, mi, W, args.profile_loop.split(","), args.steps, tiled, args.flush)
+        return
     dev = torch.device("cuda:0")
     props = torch.cuda.get_device_properties(dev)
     layout = 1 if args.scale_layout == "col" else 0
@@ -626,30 +903,42 @@ def main():
         print(json.dumps({"kernel_loop": args.kernel_loop, "us_per_launch": us}))
         return
 
-    # ---- the timed region: K steps, graph-replayed over the buffer sets ----
-    def time_steps(one_launch):
-        step_fns = []
-        for s in sets:
-            step_fns += [s["fs"]] if one_launch else [s["nq"], s["gp"]]
-        g = make_graph(torch, step_fns)
-        replays_warm = max(1, -(-args.warmup // nsets))
-        replays = max(1, -(-args.steps // nsets))
-        for _ in range(replays_warm):
+    # ---- the timed region: exactly K steps after exactly W untimed ones,
+    # step i on buffer set i mod nsets, captured as HIP graphs (at most
+    # CHUNK steps per graph) and replayed ----
+    def step_graphs(one_launch, n, first):
+        """Graphs covering n steps starting at step `first`: (graph, replays)."""
+        out, done = [], 0
+        while done < n:
+            c = min(CHUNK, n - done)
+            fns = []
+            for i in range(c):
+                st = sets[(first + done + i) % nsets]
+                fns += [st["fs"]] if one_launch else [st["nq"], st["gp"]]
+            out.append(capture(torch, fns))
+            done += c
+        return out
+
+    def time_steps(one_launch, K, Wm):
+        warm = step_graphs(one_launch, Wm, 0)
+        timed = step_graphs(one_launch, K, Wm)
+        for g in warm:
             g.replay()
         torch.cuda.synchronize()
         tm = Timer(torch)
         tm.start()
-        for _ in range(replays):
+        for g in timed:
             g.replay()
         ms = tm.stop_ms()
         torch.cuda.synchronize()
-        del g
-        return 1000.0 * ms / (replays * nsets), replays * nsets, replays_warm * nsets
+        del warm, timed
+        return 1000.0 * ms / K
 
     launches = mi.mi_fused_normquant_gemm_pair_launches(M, W.NQ, W.NKV, W.W_A_SHAPE[0], W.W_B_SHAPE[0])
     library = args.step == "library"
-    us_step, steps, warmup_steps = time_steps(library)
-    us_other, _, _ = time_steps(not library)
+    steps, warmup_steps = max(1, args.steps), max(0, args.warmup)
+    us_step = time_steps(library, steps, warmup_steps)
+    us_other = time_steps(not library, steps, warmup_steps)
     one_launch = library and launches == 1
 
     # ---- per-kernel average launch duration (events around back-to-back
@@ -725,7 +1014,9 @@ def main():
             "weight_layout": "tiled (relaid out once at load time)" if tiled else "row-major",
             "cache": "warm" if args.warm else f"cold ({nsets} rotating buffer sets, "
                                               f"{nsets * step_bytes / 2**30:.2f} GiB)",
-            "timing": "HIP graph of one step per buffer set, replayed; HIP events",
+            "timing": "exactly `warmup` untimed steps, then `steps` timed steps (step i on buffer set "
+                      "i mod sets), as HIP graphs of up to 2000 steps, replayed; HIP events around the timed "
+                      "replays",
             "parallelism": "single GPU",
         },
         "roofline": roofline,
@@ -746,7 +1037,21 @@ def main():
             warm[f"{name}_GB/s"] = round(nbytes / us / 1e3, 1)
         line["warm"] = warm
     if not args.no_sweep:
-        line["sweep"] = sweep(torch, np, mi, W, wa, wb, dev, cold=not args.warm, tiled=tiled)
+        sw = sweep(torch, np, mi, W, wa, wb, dev, cold=not args.warm, tiled=tiled)
+        ceil = ceilings(torch, np, W)
+        # the kernels against the measured data-movement ceilings of the same
+        # access pattern (fraction = ceiling time / kernel time)
+        for lay in ("row", "col"):
+            e = sw.get(f"normquant_M8192_{lay}")
+            if e:
+                e["frac_ceiling"] = round(ceil["normquant_M8192"]["us"] / e["us"], 4)
+        for name in ("W_a", "W_b"):
+            for key in (f"gemm_{name}_M256", f"e8m0_gemm_{name}_M256"):
+                e = sw.get(key)
+                if e:
+                    e["frac_weight_stream_floor"] = round(ceil[f"weight_stream_{name}"]["us"] / e["us"], 4)
+        line["sweep"] = sw
+        line["ceilings"] = ceil
     if not args.no_cpu_baseline:
         # set 0 once more through the library's step (its outputs were last
         # written by the single-GEMM timing loops), then to the host

@@ -418,6 +418,24 @@ mi_status mi_fused_normquant_gemm_pair_e8m0(
     hipStream_t stream);
 
 /*
+ * mi_init
+ *
+ * Prepares the current device for this library's kernels: caches its
+ * compute-unit count and raises the dynamic-LDS limit (a per-device
+ * function attribute, not a stream operation) of every GEMM kernel that
+ * needs more than the default.  Optional for ordinary use: each entry point
+ * does the same lazily on its first launch of a kernel on a device.  A
+ * caller that captures calls of this library into a HIP graph calls mi_init
+ * on that device before the capture begins (or first makes one ordinary call
+ * of every entry point and shape it captures), so that no attribute change
+ * happens while the stream is capturing.  Enqueues nothing and allocates
+ * nothing; safe to call repeatedly and from several host threads (each for
+ * its current device).  MI_ERR_HIP if the HIP runtime reports an error (no
+ * device, for instance).
+ */
+mi_status mi_init(void);
+
+/*
  * mi_negotiate_scale_layout
  *
  * [D56433] item 4: the producer writes one scale buffer for several

@@ -25,6 +25,7 @@ from ._binding import (  # noqa: F401
     mi_rmsnorm_group_quant,
     mi_negotiate_scale_layout,
     mi_status_string,
+    mi_init,
     prepare_block_scaled_fp8_gemm,
     prepare_block_scaled_fp8_gemm_pair,
     prepare_fused_dual_rmsnorm_group_quant,

@@ -40,6 +40,7 @@ EXPORTED = (
     "mi_relayout_weight",
     "mi_negotiate_scale_layout",
     "mi_status_string",
+    "mi_init",
 )
 
 
@@ -99,10 +100,18 @@ def lib() -> ctypes.CDLL:
         L.mi_relayout_weight.argtypes = [p, c_int, p, c_int, i64, i64, p]
         L.mi_negotiate_scale_layout.restype = c_int
         L.mi_negotiate_scale_layout.argtypes = [ctypes.POINTER(c_int), c_int]
+        L.mi_init.restype = c_int
+        L.mi_init.argtypes = []
         L.mi_status_string.restype = ctypes.c_char_p
         L.mi_status_string.argtypes = [c_int]
         _lib = L
     return _lib
+
+
+def mi_init() -> None:
+    """Prepare the current device (see mi_init in include/mi_normquant.h):
+    call it before capturing calls of this library into a HIP graph."""
+    _check("mi_init", lib().mi_init())
 
 
 def mi_status_string(status: int) -> str:

@@ -20,6 +20,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["normquant.hip", "gemm_fp8_bs.hip", "api.cpp"]
+# the benchmark's data-movement ceilings (a separate library)
+CEILING_SOURCES = ["ceiling.hip"]
+CEILING_LIB = os.path.join(PKG, "libmi_ceiling.so")
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -42,18 +45,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Builds the library and, beside it, the benchmark's ceiling kernels
+    (libmi_ceiling.so: measurement only, not part of the library)."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=len(SOURCES) + len(CEILING_SOURCES)) as ex:
+        objs = list(ex.map(_compile, SOURCES + CEILING_SOURCES))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], CEILING_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CEILING_LIB}")
     return LIB
 
 

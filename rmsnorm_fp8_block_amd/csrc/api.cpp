@@ -441,6 +441,8 @@ extern "C" mi_status mi_relayout_weight(const uint8_t *src, int from_layout, uin
                : MI_ERR_HIP;
 }
 
+extern "C" mi_status mi_init(void) { return mi::init_device() == hipSuccess ? MI_OK : MI_ERR_HIP; }
+
 extern "C" int mi_negotiate_scale_layout(const int *consumer_wants_transposed, int n) {
     if (!consumer_wants_transposed || n <= 0)
         return -1;

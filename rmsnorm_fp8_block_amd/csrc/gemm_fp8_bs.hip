@@ -37,6 +37,7 @@
 //    share the weight tile through one XCD's L2.
 #include <algorithm>
 #include <atomic>
+#include <vector>
 
 #include "device.h"
 #include "launch.h"
@@ -992,23 +993,45 @@ __global__ __launch_bounds__(kWaves * kWave) void block_scaled_fp8_gemm_stream_k
     w.store_tile(p, m0, st0);
 }
 
-// The dynamic-LDS limit is a per-device function attribute: remember, per
-// kernel instance, on which devices it has been raised.
-template <typename Kern>
-hipError_t allow_dynamic_lds(Kern kern, size_t lds, std::atomic<uint64_t> &done) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess)
-        return e;
-    const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t{1} << dev) : 0;
-    if (bit && (done.load(std::memory_order_acquire) & bit))
-        return hipSuccess;
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            static_cast<int>(lds));
-    if (e == hipSuccess && bit)
-        done.fetch_or(bit, std::memory_order_acq_rel);
-    return e;
+// The dynamic-LDS limit is a per-device function attribute.  Every kernel
+// instance launched with more than the default registers a function that
+// raises it on the current device when the library is loaded (its launcher
+// names the instance's DynLds), so that init_dynamic_lds() can raise them all
+// before a caller starts capturing launches into a graph; launches also
+// raise it lazily, once per device and instance.
+using RaiseFn = hipError_t (*)();
+
+std::vector<RaiseFn> &lds_registry() {
+    static std::vector<RaiseFn> r;  // filled during the library's static initialisation
+    return r;
 }
+
+template <auto kKern, int kBytes>
+struct DynLds {
+    static inline std::atomic<uint64_t> done{0};  // bit d: raised on device d
+    static hipError_t raise() {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess)
+            return e;
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(kKern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                kBytes);
+        if (e == hipSuccess && dev >= 0 && dev < 64)
+            done.fetch_or(uint64_t{1} << dev, std::memory_order_acq_rel);
+        return e;
+    }
+    static inline const bool registered = (lds_registry().push_back(&raise), true);
+    static hipError_t ensure() {
+        (void)registered;
+        int dev = 0;
+        const hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess)
+            return e;
+        if (dev >= 0 && dev < 64 && (done.load(std::memory_order_acquire) & (uint64_t{1} << dev)))
+            return hipSuccess;
+        return raise();
+    }
+};
 
 int device_cu_count() {
     static std::atomic<int> cached[64] = {};  // per device; calls may come from several host threads
@@ -1204,12 +1227,11 @@ hipError_t launch_decode(const GemmParams &p, hipStream_t stream) {
     const int64_t blocks = (S + spb - 1) / spb;
     if (blocks > 0x7FFFFFFF)
         return hipErrorInvalidValue;
-    const size_t lds = static_cast<size_t>(kKB) * kMT * 2 * kWave * sizeof(uint4) +
-                       static_cast<size_t>(2 * kDecodeWaves) * kWave * sizeof(float) +
-                       static_cast<size_t>(kChunkRows) * 16 * kDecodeWaves * sizeof(uint16_t);
-    auto kern = block_scaled_fp8_gemm_decode_kernel<kMT, kKB>;
-    static std::atomic<uint64_t> lds_set{0};
-    const hipError_t e = allow_dynamic_lds(kern, lds, lds_set);
+    constexpr int lds = kKB * kMT * 2 * kWave * static_cast<int>(sizeof(uint4)) +
+                        2 * kDecodeWaves * kWave * static_cast<int>(sizeof(float)) +
+                        kChunkRows * 16 * kDecodeWaves * static_cast<int>(sizeof(uint16_t));
+    constexpr auto kern = block_scaled_fp8_gemm_decode_kernel<kMT, kKB>;
+    const hipError_t e = DynLds<kern, lds>::ensure();
     if (e != hipSuccess)
         return e;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kDecodeWaves * kWave), lds, stream, p, spb);
@@ -1246,9 +1268,8 @@ hipError_t launch_stream_scaled(const GemmParams &p, hipStream_t stream) {
     const int64_t blocks = ((p.N + p.N2) / 16 + per_block - 1) / per_block * nm;
     if (blocks > 0x7FFFFFFF || p.M > 256)
         return hipErrorInvalidValue;
-    auto kern = block_scaled_fp8_gemm_stream_kernel<kKB, kMT, kSW, kWaves, kD, kE8m0>;
-    static std::atomic<uint64_t> lds_set{0};
-    const hipError_t e = allow_dynamic_lds(kern, P::kLds, lds_set);
+    constexpr auto kern = block_scaled_fp8_gemm_stream_kernel<kKB, kMT, kSW, kWaves, kD, kE8m0>;
+    const hipError_t e = DynLds<kern, P::kLds>::ensure();
     if (e != hipSuccess)
         return e;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kWaves * kWave), P::kLds, stream, p);
@@ -1466,9 +1487,8 @@ hipError_t launch_normquant_gemm_pair_mt(const NormQuantParams &a, const GemmPar
     const int64_t blocks = ((p.N + p.N2) / 16 + per_block - 1) / per_block;
     if (blocks > 0x7FFFFFFF)
         return hipErrorInvalidValue;
-    auto kern = normquant_gemm_pair_kernel<kKB, kMT, kSW, kWaves, kD, kE8m0>;
-    static std::atomic<uint64_t> lds_set{0};
-    const hipError_t e = allow_dynamic_lds(kern, P::kLds, lds_set);
+    constexpr auto kern = normquant_gemm_pair_kernel<kKB, kMT, kSW, kWaves, kD, kE8m0>;
+    const hipError_t e = DynLds<kern, P::kLds>::ensure();
     if (e != hipSuccess)
         return e;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3((kWaves + 1) * kWave), P::kLds, stream, a, p);
@@ -1482,9 +1502,8 @@ hipError_t launch_wide_scaled(const GemmParams &p, hipStream_t stream) {
     const int64_t blocks = ((p.N + p.N2) / 16 + kNS - 1) / kNS * nm;
     if (blocks > 0x7FFFFFFF || p.M > 256)
         return hipErrorInvalidValue;
-    auto kern = block_scaled_fp8_gemm_wide_kernel<kKB, kNS, kMT, kWaves, kE8m0>;
-    static std::atomic<uint64_t> lds_set{0};
-    const hipError_t e = allow_dynamic_lds(kern, P::kLds, lds_set);
+    constexpr auto kern = block_scaled_fp8_gemm_wide_kernel<kKB, kNS, kMT, kWaves, kE8m0>;
+    const hipError_t e = DynLds<kern, P::kLds>::ensure();
     if (e != hipSuccess)
         return e;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kWaves * kWave), P::kLds, stream, p);
@@ -1670,6 +1689,16 @@ hipError_t launch_normquant_gemm_pair(const NormQuantParams &a, const GemmParams
                      : launch_normquant_gemm_pair_mt<1, 4, true>(a, p, stream);
     return three ? launch_normquant_gemm_pair_mt<1, 3, false>(a, p, stream)
                  : launch_normquant_gemm_pair_mt<1, 4, false>(a, p, stream);
+}
+
+hipError_t init_device() {
+    device_cu_count();
+    for (RaiseFn f : lds_registry()) {
+        const hipError_t e = f();
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
 }
 
 int gemm_pair_launches(int64_t M, int64_t K) {

@@ -76,6 +76,9 @@ int gemm_pair_launches(int64_t M, int64_t K);
 // consumer GEMMs of its outputs (p.a / p.a_scale are a.out_q / a.out_scale).
 // hipErrorNotSupported where the shapes or alignment do not allow it.
 hipError_t launch_normquant_gemm_pair(const NormQuantParams &a, const GemmParams &p, hipStream_t stream);
+// on the current device: caches the CU count and raises the dynamic-LDS
+// limit of every kernel instance that needs it
+hipError_t init_device();
 // whether launch_normquant_gemm_pair takes these sizes (alignment aside)
 bool normquant_gemm_pair_one_launch(int64_t M, int64_t Nq, int64_t Nkv, int64_t N1, int64_t N2);
 

@@ -453,3 +453,14 @@ def test_step_binding_checks(prepared):
         call(gamma_kv=torch.ones(100, dtype=torch.bfloat16))
     with pytest.raises(ValueError, match="w1"):
         call(S1=torch.ones((2, 12), dtype=torch.float64))
+
+
+def test_init_reports_hip_errors_without_a_device(L):
+    """mi_init needs a device: with none visible (this CPU host) it returns
+    MI_ERR_HIP and the binding raises; it never crashes."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    assert L.mi_init() == B.MI_ERR_HIP
+    with pytest.raises(mi.MiError):
+        mi.mi_init()
