@@ -133,8 +133,8 @@ def mfma_counters(M, N, e8m0=False):
     sha = source_sha(*GEMM_SOURCES)
     for e in t.values():
         if e.get("M") == M and e.get("N") == N and bool(e.get("e8m0")) == e8m0 and e.get("source_sha") == sha:
-            return {k: e[k] for k in ("mfma_busy_frac", "mfma_busy_cycles", "gui_active_cycles_per_xcd",
-                                      "mops_f8") if k in e}
+            return {k: e[k] for k in ("mfma_busy_frac", "mfma_busy_frac_trace", "mfma_busy_cycles",
+                                      "gui_active_cycles_per_xcd", "mops_f8") if k in e}
     return None
 
 
@@ -452,8 +452,11 @@ def sweep(torch, np, mi, W, wa, wb, dev, cold, tiled):
         g = make_graph(torch, fns)
         us = time_graph(torch, g, len(fns), max(1, 200 // len(fns)))
         gbs = nbytes / us / 1e3
-        res[f"normquant_M8192_{'col' if layout else 'row'}"] = {
-            "us": round(us, 3), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+        lay = "col" if layout else "row"
+        res[f"normquant_M8192_{lay}"] = {
+            "us": round(us, 3), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(f"fused_dual_rmsnorm_group_quant_{lay}", source_sha(*NORMQUANT_SOURCES),
+                                        8192)}
         del g, fns
         torch.cuda.empty_cache()
     del bufp
@@ -634,7 +637,9 @@ def sweep(torch, np, mi, W, wa, wb, dev, cold, tiled):
                                          "frac_fp8_mfma": round(tf / FP8_MFMA_PEAK_TFLOPS, 4),
                                          "GB/s": round(perg / us / 1e3, 1),
                                          "roofline_frac": roofline_frac(gemm_flops(M, N, 1536), perg, us),
-                                         "mfma_counters": mfma_counters(M, N, e8m0=True)}
+                                         "mfma_counters": mfma_counters(M, N, e8m0=True),
+                                         "traffic": measured_traffic(f"block_scaled_fp8_gemm_{name}_e8m0",
+                                                                     source_sha(*GEMM_SOURCES), M)}
         del g, fns
     del eac0, ebc0
     torch.cuda.empty_cache()
@@ -660,7 +665,9 @@ def sweep(torch, np, mi, W, wa, wb, dev, cold, tiled):
                                     "frac_fp8_mfma": round(tf / FP8_MFMA_PEAK_TFLOPS, 4),
                                     "GB/s": round(per / us / 1e3, 1),
                                     "roofline_frac": roofline_frac(gemm_flops(M, N, K), per, us),
-                                    "mfma_counters": mfma_counters(M, N)}
+                                    "mfma_counters": mfma_counters(M, N),
+                                    "traffic": measured_traffic(f"block_scaled_fp8_gemm_{name}",
+                                                                source_sha(*GEMM_SOURCES), M)}
         del g, fns
         torch.cuda.empty_cache()
 
@@ -723,19 +730,24 @@ def ceilings(torch, np, W):
     del sets, fns
     torch.cuda.empty_cache()
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
-    for name, n in (("W_a", W.W_A_SHAPE[0]), ("W_b", W.W_B_SHAPE[0]), ("pair", W.W_A_SHAPE[0] + W.W_B_SHAPE[0])):
+    for name, n in (("W_a", W.W_A_SHAPE[0]), ("W_b", W.W_B_SHAPE[0]), ("pair", W.W_A_SHAPE[0] + W.W_B_SHAPE[0]),
+                    ("tp8_pair", (W.W_A_SHAPE[0] + W.W_B_SHAPE[0]) // 8), ("tp8_W_a", W.W_A_SHAPE[0] // 8)):
         wbytes = n * W.NQ
-        slab = wbytes // 256
+        # the most workgroups (at most one per CU) that split the weight into
+        # whole 4 KB stages
+        blocks = next(b for b in range(256, 0, -1) if wbytes % (b * 4096) == 0)
+        slab = wbytes // blocks
         bufs = [torch.empty(wbytes, dtype=torch.uint8, device=dev).fill_(1)
                 for _ in range(2 * MALL_BYTES // wbytes + 2)]
 
-        def ws(i, bufs=bufs, slab=slab):
-            st = lib.mi_ceiling_weight_stream(bufs[i % len(bufs)].data_ptr(), slab, 256, sink.data_ptr(), stream())
+        def ws(i, bufs=bufs, slab=slab, blocks=blocks):
+            st = lib.mi_ceiling_weight_stream(bufs[i % len(bufs)].data_ptr(), slab, blocks, sink.data_ptr(), stream())
             if st != 0:
                 raise RuntimeError(f"mi_ceiling_weight_stream: hip error {st}")
         fns = [lambda i=i: ws(i) for i in range(len(bufs))]
         us = time_eager(torch, fns, 20 * len(fns))
-        res[f"weight_stream_{name}"] = {"us": round(us, 3), "bytes": wbytes, "GB/s": round(wbytes / us / 1e3, 1),
+        res[f"weight_stream_{name}"] = {"us": round(us, 3), "bytes": wbytes, "workgroups": blocks,
+                                        "GB/s": round(wbytes / us / 1e3, 1),
                                         "frac_hbm": round(wbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
         del bufs, fns
         torch.cuda.empty_cache()
@@ -900,7 +912,8 @@ def main():
                "step": "fs"}[args.kernel_loop]
         fns = [s[key] for s in sets]
         us = time_eager(torch, fns, args.steps)
-        print(json.dumps({"kernel_loop": args.kernel_loop, "us_per_launch": us}))
+        print(json.dumps({"kernel_loop": args.kernel_loop, "M": M, "warmup_launches": 3 * len(fns),
+                          "launches": args.steps, "sets": len(fns), "us_per_launch": us}))
         return
 
     # ---- the timed region: exactly K steps after exactly W untimed ones,
