@@ -125,9 +125,11 @@ def gemm_ref(a, As, w, Bs, cols=None, blocks=None):
 
 # decode-size batches (the wide kernel), 64 < M <= 256 (wide, row split for
 # narrow weights), M > 256 and K / 128 = 5 (the generic kernel)
+# (two subtiles per CU at M <= 16: the stream kernel with one subtile per wave)
 @pytest.mark.parametrize("M,N,K,seed", [(1, 24576, 1536, 1), (16, 8192, 1536, 2), (64, 1024, 512, 3),
                                         (100, 1536, 1536, 4), (256, 6144, 1536, 5), (300, 640, 1536, 6),
-                                        (40, 384, 640, 7), (64, 2048, 2048, 8)])
+                                        (40, 384, 640, 7), (64, 2048, 2048, 8), (1, 6144, 1536, 9),
+                                        (16, 6144, 1536, 10)])
 def test_gemm_e8m0_vs_oracle(M, N, K, seed):
     dev = gpu_or_skip()
     a, As, w, Bs = e8m0_operands(M, N, K, seed)
@@ -162,6 +164,29 @@ def test_gemm_pair_e8m0_equals_two_gemms(M):
     As = dev_u8(r.integers(118, 127, size=(12, M)).astype(np.uint8), dev).T
     dwa, dwb = mi.relayout_weight(dev_u8(wa.codes, dev)), mi.relayout_weight(dev_u8(wb.codes, dev))
     sa, sb = dev_u8(wa.scale, dev), dev_u8(wb.scale, dev)
+    o1, o2 = mi.mi_block_scaled_fp8_gemm_pair(a, As, dwa, sa, dwb, sb)
+    s1 = mi.mi_block_scaled_fp8_gemm(a, As, dwa, sa)
+    s2 = mi.mi_block_scaled_fp8_gemm(a, As, dwb, sb)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bf16_bits(o1), host_bf16_bits(s1))
+    assert np.array_equal(host_bf16_bits(o2), host_bf16_bits(s2))
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_gemm_pair_e8m0_tp4_shard_equals_two_gemms(M):
+    """The TP-4 shard of both weights (W_a rows 18432.., W_b rows 6144..):
+    the pair is one launch with two subtiles per CU, the W_b shard alone
+    another kernel; the outputs must agree bit for bit."""
+    dev = gpu_or_skip()
+    wa = W.block_fp8_weight_e8m0(*W.W_A_SHAPE, W.W_A_SEED)
+    wb = W.block_fp8_weight_e8m0(*W.W_B_SHAPE, W.W_B_SEED)
+    na, nb = W.W_A_SHAPE[0] // 4, W.W_B_SHAPE[0] // 4
+    r = np.random.default_rng(40 + M)
+    a = dev_u8(r.integers(0, 0x78, size=(M, 1536), dtype=np.uint8), dev)
+    As = dev_u8(r.integers(118, 127, size=(12, M)).astype(np.uint8), dev).T
+    dwa = mi.relayout_weight(dev_u8(wa.codes[3 * na:], dev))
+    dwb = mi.relayout_weight(dev_u8(wb.codes[3 * nb:], dev))
+    sa, sb = dev_u8(wa.scale[3 * na // 128:], dev), dev_u8(wb.scale[3 * nb // 128:], dev)
     o1, o2 = mi.mi_block_scaled_fp8_gemm_pair(a, As, dwa, sa, dwb, sb)
     s1 = mi.mi_block_scaled_fp8_gemm(a, As, dwa, sa)
     s2 = mi.mi_block_scaled_fp8_gemm(a, As, dwb, sb)
