@@ -1582,7 +1582,120 @@ hipError_t launch_mt(const GemmParams &p, hipStream_t stream) {
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Split-K variant: one 16-row weight subtile per block, for decode batches
+// (up to 16 rows) over a narrow weight, such as a tensor-parallel shard of
+// a few thousand rows, that gives every CU at most one subtile: there a K
+// loop per subtile leaves the memory system idle between its stages.
+// The block's kWaves waves take contiguous ranges of kKB / kWaves
+// K-blocks; each wave loads its weight fragments, the activation fragments
+// of its K-blocks and their scales straight into registers (every load
+// issued before the first MFMA: one memory round trip per block), runs
+// one MFMA per (m-tile, K-block) and leaves the partial sums with their
+// scales As * Bs in LDS.  After one barrier wave j folds m-tile j's
+// partials in K-block order, as every kernel here does, so the results are
+// bit-identical to theirs.  Activation rows at or beyond M repeat row M - 1
+// (their results are never stored).
+// ---------------------------------------------------------------------------
+namespace {
+
+template <int kKB, int kMT, int kWaves>
+__global__ __launch_bounds__(kWaves * kWave) void block_scaled_fp8_gemm_splitk_kernel(GemmParams p) {
+    static_assert(kKB % kWaves == 0 && kMT <= kWaves, "K ranges per wave; an m-tile per folding wave");
+    constexpr int kPer = kKB / kWaves;
+    __shared__ v4f s_part[kMT][kKB][kWave];
+    __shared__ float s_scl[kMT][kKB][kWave];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int64_t M = p.M, K = p.K;
+    const SubTile sub = subtile(p, blockIdx.x);
+    const WeightFrag wfr = weight_frag(lane, K, p.w_tiled);
+    const int kb0 = wave * kPer;
+
+    // the scales first (their latency then hides under the fragments'),
+    // then the weight fragments (HBM), then the activation fragments
+    v8i wf[kPer], af[kMT][kPer];
+    float as[kMT][kPer], bs[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+        bs[i] = sub.ws[kb0 + i];
+#pragma unroll
+    for (int j = 0; j < kMT; ++j) {
+        const int64_t row = min<int64_t>(16 * j + (lane & 15), M - 1);
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int64_t kb = kb0 + i;
+            as[j][i] = p.a_scale[p.a_scale_transposed ? kb * M + row : row * kKB + kb];
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+        wf[i] = load_weight_frag(sub.w + wfr.lane_off + (kb0 + i) * wfr.kstride, wfr.hstride);
+#pragma unroll
+    for (int j = 0; j < kMT; ++j) {
+        const int64_t row = min<int64_t>(16 * j + (lane & 15), M - 1);
+        const uint8_t *arow = p.a + row * K + 32 * (lane >> 4);
+#pragma unroll
+        for (int i = 0; i < kPer; ++i)
+            af[j][i] = load_weight_frag(arow + (kb0 + i) * kBlk, 16);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < kMT; ++j)
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            s_part[j][kb0 + i][lane] = mfma_e4m3_16x16x128(wf[i], af[j][i]);
+            s_scl[j][kb0 + i][lane] = as[j][i] * bs[i];
+        }
+    __syncthreads();
+    if (wave < kMT) {
+        const int j = wave;
+        v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kb = 0; kb < kKB; ++kb) {
+            const v4f part = s_part[j][kb][lane];
+            const float sc = s_scl[j][kb][lane];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[i] = fmaf(part[i], sc, acc[i]);
+        }
+        const int64_t row = 16 * j + (lane & 15);
+        if (row < M)
+            *reinterpret_cast<uint2 *>(sub.out + row * sub.ldo + sub.n0 + 4 * (lane >> 4)) =
+                make_uint2(pack2_bf16(acc[0], acc[1]), pack2_bf16(acc[2], acc[3]));
+    }
+}
+
+template <int kMT>
+hipError_t launch_splitk_mt(const GemmParams &p, int64_t blocks, hipStream_t stream) {
+    hipLaunchKernelGGL((block_scaled_fp8_gemm_splitk_kernel<12, kMT, 4>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(4 * kWave), 0, stream, p);
+    return hipGetLastError();
+}
+
+// The split-K kernel where it applies: fp32 scales, K = 1536, batches of
+// up to 16 rows (one m-tile), at most one weight subtile per CU.
+// hipErrorNotSupported otherwise.  (Measured on the TP-8 shards: the pair
+// at M = 1 4.9 -> 3.8 us, at M = 16 5.0 -> 4.3 us; at 32 rows and more the
+// activation fragments, read straight from memory in fragment order, cost
+// more than the split saves: M = 32 5.1 -> 5.3 us, M = 64 5.2 -> 7.1 us.)
+hipError_t launch_splitk(const GemmParams &p, hipStream_t stream) {
+    const int64_t S = (p.N + p.N2) / 16;
+    if (p.scale_e8m0 || p.K != 12 * kBlk || p.M < 1 || p.M > 16 || S < 1 || S > device_cu_count())
+        return hipErrorNotSupported;
+    return launch_splitk_mt<1>(p, S, stream);
+}
+
+}  // namespace
+
 hipError_t launch_block_scaled_gemm(const GemmParams &p, hipStream_t stream) {
+    // decode batches over narrow weights (a subtile per CU at most): split-K
+    {
+        const hipError_t e = launch_splitk(p, stream);
+        if (e != hipErrorNotSupported)
+            return e;
+    }
     // decode batches over wide weights: the barrier-free stream kernel
     {
         const hipError_t e = launch_stream(p, stream);
@@ -1716,10 +1829,12 @@ int gemm_pair_launches(int64_t M, int64_t K) {
 
 hipError_t launch_block_scaled_gemm_pair(const GemmParams &p, hipStream_t stream) {
     // decode batches: one launch over the subtiles of both weights, sharing
-    // the activation tile (the stream kernel where the weights are wide
-    // enough, else the wide kernel)
+    // the activation tile (split-K over narrow weights, the stream kernel
+    // where the weights are wide enough, else the wide kernel)
     if (p.M <= kChunkRows) {
-        const hipError_t e = launch_stream(p, stream);
+        hipError_t e = launch_splitk(p, stream);
+        if (e == hipErrorNotSupported)
+            e = launch_stream(p, stream);
         if (e != hipErrorNotSupported)
             return e;
         switch (p.K / kBlk) {

@@ -1,7 +1,7 @@
 """mi_init (include/mi_normquant.h): after it, the first call of each GEMM
-kernel that needs a raised LDS limit (the one-launch decode step, the
-stream pair, the wide and the decode GEMMs, fp32 and e8m0 scales) can be
-captured into a HIP graph with no ordinary call before it, and the replay
+kernel that needs a raised LDS limit (the decode step in one launch and in
+two, the stream pair, the wide and the decode GEMMs, fp32 and e8m0 scales)
+can be captured into a HIP graph with no ordinary call before it, and the replay
 equals an eager call bit for bit.  Run in a fresh process, so that no
 earlier test has launched (and thereby prepared) those kernels."""
 import os
@@ -55,6 +55,15 @@ def step_outs():
             torch.empty((M, 512), dtype=torch.bfloat16, device=dev), torch.empty((M, 24576), dtype=torch.bfloat16, device=dev),
             torch.empty((M, 8192), dtype=torch.bfloat16, device=dev))
 cases.append(("step M=8", step, step_outs))
+# the step at M = 48 (two launches: the norm-quant, then the stream pair)
+buf48 = torch.randn((48, 2048), generator=g).to(torch.bfloat16).to(dev)
+def step48(o):
+    return mi.prepare_fused_normquant_gemm_pair(buf48[:, :1536], buf48[:, 1536:], gq, gk, 1e-6, True, wa, sa, wb, sb, *o)
+def step48_outs():
+    return (torch.empty((48, 1536), dtype=torch.uint8, device=dev), torch.empty(48 * 12, device=dev),
+            torch.empty((48, 512), dtype=torch.bfloat16, device=dev), torch.empty((48, 24576), dtype=torch.bfloat16, device=dev),
+            torch.empty((48, 8192), dtype=torch.bfloat16, device=dev))
+cases.append(("step M=48", step48, step48_outs))
 # stream pair, M = 64, column-major scales
 a64, s64 = codes(64, 1536), fscale(12, 64).T
 def pair(o):

@@ -66,7 +66,7 @@ def assert_same(got, want, label):
 
 
 @pytest.mark.parametrize("layout", ["tiled", "row"])
-@pytest.mark.parametrize("M", [1, 2, 5, 8, 15, 16, 17, 33, 64])
+@pytest.mark.parametrize("M", [1, 2, 5, 8, 15, 16, 17, 20, 32, 33, 48, 64])
 def test_step_equals_the_two_calls(M, layout, weights):
     """One launch up to 16 rows, two launches above (the query says which),
     ragged sizes, both scale layouts, both weight layouts: bit-identical to
@@ -83,12 +83,14 @@ def test_step_equals_the_two_calls(M, layout, weights):
         assert_same(got, want, f"M{M} {layout} t{t}")
 
 
-def test_step_vs_oracle(weights):
-    """M = 16 (one launch), column-major scales, tiled weights: the
-    norm-quant outputs to the dual operation's bar, both GEMM outputs on
-    sampled 128-column blocks against the oracle chain on the same inputs."""
+@pytest.mark.parametrize("M", [16, 64])
+def test_step_vs_oracle(M, weights):
+    """M = 16 (one launch) and 64 (two), column-major scales, tiled
+    weights: the norm-quant outputs to the dual operation's bar, both GEMM
+    outputs on sampled 128-column blocks against the oracle chain on the
+    same inputs."""
     dev = gpu_or_skip()
-    case = W.strided_batch(16)
+    case = W.strided_batch(M)
     q, kv, gq, gk = device_case(case, dev)
     wa, wb = weights["W_a"], weights["W_b"]
     codes, scale, kvo, o1, o2 = mi.mi_fused_normquant_gemm_pair(
@@ -96,7 +98,7 @@ def test_step_vs_oracle(weights):
     torch.cuda.synchronize()
     ref = oracle.dual_rmsnorm_group_quant(case.q, case.kv, case.gamma_q, case.gamma_kv, case.eps, True,
                                           want_ratio=True)
-    compare_normquant(codes.cpu().numpy(), scale_buffer(scale), host_bf16_bits(kvo), ref, label="step M16")
+    compare_normquant(codes.cpu().numpy(), scale_buffer(scale), host_bf16_bits(kvo), ref, label=f"step M{M}")
     for name, out in (("W_a", o1), ("W_b", o2)):
         wt = weights[name]["host"]
         nb = wt.codes.shape[0] // 128
@@ -108,12 +110,12 @@ def test_step_vs_oracle(weights):
 
 def test_step_back_to_back_with_changing_inputs(weights):
     """Calls on one stream sharing the output buffers, with new activations
-    every call and batch sizes 64, 1, 16, 64, 33: each call equals the two
-    calls on its own inputs."""
+    every call and batch sizes 16, 1, 64, 7, 33, 64, 17, 16 (one and two
+    launches in turn): each call equals the two calls on its own inputs."""
     dev = gpu_or_skip()
     wa, wb = weights["W_a"], weights["W_b"]
     bufs = {k: None for k in ("q", "s", "kv", "o1", "o2")}
-    Ms = (16, 1, 64, 7, 16)
+    Ms = (16, 1, 64, 7, 33, 64, 17, 16)
     for i, M in enumerate(Ms):
         q, kv, gq, gk = device_case(W.producer_activations(M, seed=40 + i), dev)
         if bufs["q"] is None or bufs["q"].shape[0] != M:
@@ -152,13 +154,13 @@ def test_step_shapes_that_take_two_launches(M, Nq, Nkv, N1, N2):
     assert_same(got, want, f"M{M} Nq{Nq} Nkv{Nkv} N{N1}+{N2}")
 
 
-def test_step_graph_replays(weights):
-    """The one-launch step captured in a HIP graph: four replays, the input
-    rewritten by eager work between them, each replay equal to the eager two
-    calls on that input."""
+@pytest.mark.parametrize("M", [16, 64])
+def test_step_graph_replays(M, weights):
+    """The step captured in a HIP graph (one launch at 16 rows, two at 64):
+    four replays, the input rewritten by eager work between them, each
+    replay equal to the eager two calls on that input."""
     dev = gpu_or_skip()
     wa, wb = weights["W_a"], weights["W_b"]
-    M = 16
     case = W.strided_batch(M)
     q, kv, gq, gk = device_case(case, dev)
     buf = q._base if q._base is not None else None
@@ -244,7 +246,7 @@ def two_calls_e8m0(q, kv, gq, gk, t, w1, s1, w2, s2):
 
 
 @pytest.mark.parametrize("layout", ["tiled", "row"])
-@pytest.mark.parametrize("M", [1, 7, 16, 33])
+@pytest.mark.parametrize("M", [1, 7, 16, 33, 64])
 def test_step_e8m0_equals_the_two_calls(M, layout, weights_e8m0):
     """e8m0 scales: one launch up to 16 rows, two above; both scale layouts:
     bit-identical to the e8m0 norm-quant followed by the e8m0 pair."""

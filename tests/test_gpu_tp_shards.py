@@ -101,3 +101,34 @@ def test_shard_wrong_layout_flag_is_caught_by_a_large_error(tp):
         torch.cuda.synchronize()
         fro, _ = gemm_error(bf16_to_f64(out)[:, cols], ref)
         assert (fro <= 2e-2) if expect_ok else (fro > 0.1), f"TP{tp} M{M}: fro {fro:.3e}"
+
+
+@pytest.mark.parametrize("M", [1, 7, 16])
+def test_split_k_equals_the_k_loop_kernels(M):
+    """A TP-8 shard gives each CU at most one 16-row subtile, where the GEMM
+    of up to 16 rows splits K over the waves of a block and folds the
+    partial sums in K-block order afterwards.  Its output must equal, bit
+    for bit, the same shard's
+    output from a K-loop kernel: the shard paired with a full consumer
+    weight (a grid too wide for the split), both As layouts, row-major and
+    tiled weights."""
+    dev = gpu_or_skip()
+    wa, wb = full_weights()
+    r = np.random.default_rng(500 + M)
+    a = dev_u8(r.integers(0, 0x100, size=(M, 1536), dtype=np.uint8) & 0xF7, dev)   # no NaN codes
+    As = np.exp2(r.uniform(-8, 0, (M, 12))).astype(np.float32)
+    for shard_w, other in ((shard(wa, 8, 7), wb), (shard(wb, 8, 7), wa)):
+        (cs, ss) = shard_w
+        for tiled in (False, True):
+            dw = dev_u8(cs, dev)
+            dw = mi.relayout_weight(dw) if tiled else dw
+            do = dev_u8(other.codes, dev)
+            do = mi.relayout_weight(do) if tiled else do
+            dss, dos = dev_f32(ss, dev), dev_f32(other.scale, dev)
+            for layout in (False, True):
+                das = dev_f32(As.T.copy(), dev).T if layout else dev_f32(As, dev)
+                single = mi.mi_block_scaled_fp8_gemm(a, das, dw, dss)
+                paired, _ = mi.mi_block_scaled_fp8_gemm_pair(a, das, dw, dss, do, dos)
+                torch.cuda.synchronize()
+                assert np.array_equal(host_bf16_bits(single), host_bf16_bits(paired)), \
+                    f"M{M} [{cs.shape[0]}] tiled={tiled} t={layout}"
