@@ -689,20 +689,34 @@ def sweep(torch, np, mi, W, wa, wb, dev, cold, tiled):
     return res
 
 
+def time_ceiling(torch, fns, replays=20):
+    """A ceiling timed like the kernels it bounds: its launches captured in
+    one graph (after an eager warm-up), us per launch over the replays."""
+    g = make_graph(torch, fns)
+    us = time_graph(torch, g, len(fns), replays)
+    del g
+    return us
+
+
 def ceilings(torch, np, W):
     """Measured data-movement ceilings of this GPU for the kernels' access
     patterns (libmi_ceiling.so: hand-written skeletons that move the same
     bytes with no arithmetic), cold (buffer sets rotated past 2x the Infinity
-    Cache), HIP events around back-to-back launches:
+    Cache), HIP events around graph replays (as the kernels are timed):
       normquant_M8192: the dual norm-quant's reads and writes at 8192 rows;
       weight_stream_{W_a,W_b,pair}: every weight byte of the GEMM read once
       from HBM into LDS by 256 workgroups (the floor of any GEMM kernel
-      that streams that weight, before activations and outputs)."""
+      that streams that weight, before activations and outputs);
+      mfma[_fold]_{W_a,W_b}_M256: the GEMM's 16x16x128 FP8 MFMAs at M = 256
+      (W_a: 256 workgroups x 12 waves x 96, W_b: 256 x 4 x 96) on register
+      operands, no memory traffic, with the fp32-scale fold or accumulating
+      in place (e8m0): the matrix-core floor at the clock the chip holds."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "rmsnorm_fp8_block_amd", "libmi_ceiling.so"))
     p, i64 = ctypes.c_void_p, ctypes.c_int64
     lib.mi_ceiling_normquant_skeleton.argtypes = [p, i64, p, p, p, i64, p]
     lib.mi_ceiling_weight_stream.argtypes = [p, i64, i64, p, p]
+    lib.mi_ceiling_mfma.argtypes = [i64, ctypes.c_int, i64, ctypes.c_int, ctypes.c_float, p, p]
     dev = torch.device("cuda:0")
     stream = lambda: ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     res = {}
@@ -722,7 +736,7 @@ def ceilings(torch, np, W):
         if st != 0:
             raise RuntimeError(f"mi_ceiling_normquant_skeleton: hip error {st}")
     fns = [lambda i=i: nq(i) for i in range(len(sets))]
-    us = time_eager(torch, fns, 20 * len(fns))
+    us = time_ceiling(torch, fns)
     res["normquant_M8192"] = {"us": round(us, 3), "GB/s": round(nbytes / us / 1e3, 1),
                               "frac_hbm": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
                               "what": "dual norm-quant data movement at 8192 rows (reads 4096 B and writes 2608 B "
@@ -745,12 +759,24 @@ def ceilings(torch, np, W):
             if st != 0:
                 raise RuntimeError(f"mi_ceiling_weight_stream: hip error {st}")
         fns = [lambda i=i: ws(i) for i in range(len(bufs))]
-        us = time_eager(torch, fns, 20 * len(fns))
+        us = time_ceiling(torch, fns)
         res[f"weight_stream_{name}"] = {"us": round(us, 3), "bytes": wbytes, "workgroups": blocks,
                                         "GB/s": round(wbytes / us / 1e3, 1),
                                         "frac_hbm": round(wbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
         del bufs, fns
         torch.cuda.empty_cache()
+    msink = torch.zeros(1024, dtype=torch.float32, device=dev)
+    for name, blocks, waves, per_wave in (("W_a_M256", 256, 12, 96), ("W_b_M256", 256, 4, 96)):
+        for fold in (True, False):
+            def mf(blocks=blocks, waves=waves, per_wave=per_wave, fold=fold):
+                st = lib.mi_ceiling_mfma(blocks, waves, per_wave, int(fold), 1.0, msink.data_ptr(), stream())
+                if st != 0:
+                    raise RuntimeError(f"mi_ceiling_mfma: hip error {st}")
+            us = time_ceiling(torch, [mf] * 20)
+            flops = blocks * waves * per_wave * 16 * 16 * 128 * 2
+            res[f"mfma{'_fold' if fold else ''}_{name}"] = {
+                "us": round(us, 3), "mfmas": blocks * waves * per_wave, "launch": [blocks, waves, per_wave],
+                "TFLOP/s": round(flops / us / 1e6, 1), "frac_fp8_peak": round(flops / us / 1e6 / FP8_MFMA_PEAK_TFLOPS, 4)}
     return res
 
 
@@ -1059,10 +1085,12 @@ def main():
             if e:
                 e["frac_ceiling"] = round(ceil["normquant_M8192"]["us"] / e["us"], 4)
         for name in ("W_a", "W_b"):
-            for key in (f"gemm_{name}_M256", f"e8m0_gemm_{name}_M256"):
+            for key, mf in ((f"gemm_{name}_M256", f"mfma_fold_{name}_M256"), (f"e8m0_gemm_{name}_M256",
+                                                                             f"mfma_{name}_M256")):
                 e = sw.get(key)
                 if e:
                     e["frac_weight_stream_floor"] = round(ceil[f"weight_stream_{name}"]["us"] / e["us"], 4)
+                    e["frac_mfma_floor"] = round(ceil[mf]["us"] / e["us"], 4)
         line["sweep"] = sw
         line["ceilings"] = ceil
     if not args.no_cpu_baseline:

@@ -12,11 +12,21 @@
 //    row, 4 waves per block, rows dealt to XCDs in contiguous ranges, rows
 //    read and outputs written non-temporally (the kernel's form from 1024
 //    rows on).
-//  - weight_stream: a GEMM's weight stream: `blocks` workgroups of 8 waves,
-//    each reading its own contiguous slab through an LDS ring by direct
-//    global -> LDS loads of 1 KB per wave instruction, never waiting for
-//    another wave (the floor of any kernel that reads every weight byte
-//    once from HBM into LDS).
+//  - weight_stream: a GEMM's weight stream: `blocks` workgroups of 4 waves,
+//    each reading its own contiguous slab through a 12-stage LDS ring by
+//    direct global -> LDS loads of 1 KB per wave instruction, never waiting
+//    for another wave (the floor of any kernel that reads every weight byte
+//    once from HBM into LDS; with a few MB the launch and memory latency
+//    dominate it).
+//  - mfma: the matrix-core floor of a block-scaled FP8 GEMM of a given
+//    launch shape: `blocks` workgroups of `waves` waves, each wave issuing
+//    `mfmas` 16x16x128 e4m3 MFMAs on operands held in registers, with no
+//    memory traffic at all.  With `fold`, each MFMA starts from zero and its
+//    partial sum is folded into an accumulator with an fp32 scale two MFMAs
+//    later (the fp32-scale kernels' per-K-block fold); without, every MFMA
+//    accumulates in place (the e8m0 kernels, whose scales the matrix core
+//    applies).  Its time is what the matrix cores allow at the clock the
+//    chip holds under that load, launch and ramp included.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -49,22 +59,20 @@ __global__ __launch_bounds__(256) void normquant_skeleton_kernel(const uint16_t 
         __builtin_nontemporal_store(__uint_as_float(x[0].x), s + m * 12 + (lane >> 4) * 3 + (lane & 15));
 }
 
-constexpr int kRing = 8;          // K-block stages in flight per block
-constexpr int kStageBytes = 16384;  // 8 waves x 2 KB
+constexpr int kRing = 12;          // stages in flight per block
+constexpr int kStageBytes = 4096;  // 4 waves x 1 KB
 
-__global__ __launch_bounds__(512) void weight_stream_kernel(const uint8_t *w, int64_t slab_bytes, unsigned *sink) {
+__global__ __launch_bounds__(256) void weight_stream_kernel(const uint8_t *w, int64_t slab_bytes, unsigned *sink) {
     extern __shared__ v4u lds[];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const uint8_t *slab = w + static_cast<int64_t>(blockIdx.x) * slab_bytes;
     char *ring = reinterpret_cast<char *>(lds);
     const int64_t stages = slab_bytes / kStageBytes;
     for (int64_t st = 0; st < stages; ++st) {
-        const uint8_t *src = slab + st * kStageBytes + wave * 2048 + lane * 16;
-        char *dst = ring + (st % kRing) * kStageBytes + wave * 2048;
-        __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 2);
-        __builtin_amdgcn_global_load_lds(src + 1024, dst + 1024, 16, 0, 2);
-        // keep kRing - 1 stages (2 loads each) in flight
-        __builtin_amdgcn_s_waitcnt((2 * (kRing - 1)) | (7 << 4) | (15 << 8));
+        __builtin_amdgcn_global_load_lds(slab + st * kStageBytes + wave * 1024 + lane * 16,
+                                         ring + (st % kRing) * kStageBytes + wave * 1024, 16, 0, 2);
+        // keep kRing - 1 stages in flight
+        __builtin_amdgcn_s_waitcnt((kRing - 1) | (7 << 4) | (15 << 8));
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -73,9 +81,57 @@ __global__ __launch_bounds__(512) void weight_stream_kernel(const uint8_t *w, in
         sink[0] = v;
 }
 
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ v4f mfma16(const v8i &a, const v8i &b, const v4f &c) {
+    // format 0 = e4m3 for both operands; zero scale operands: unscaled
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+template <bool kFold>
+__global__ __launch_bounds__(1024) void mfma_kernel(int64_t rounds, float scale, float *sink) {
+    const int lane = threadIdx.x & 63;
+    v8i a, b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        a[i] = 0x38383838 ^ (lane * (i + 1));
+        b[i] = 0x30303030 ^ (lane + i);
+    }
+    v4f acc[8], part[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        acc[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        part[j] = acc[j];
+    }
+    const float sc = scale * (1.0f + lane * 0x1p-10f);
+    for (int64_t r = 0; r < rounds; ++r) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            asm volatile("" : "+v"(a));  // a new operand for every MFMA (none can be merged)
+            if constexpr (kFold) {
+                const v4f pj = mfma16(a, b, v4f{0.0f, 0.0f, 0.0f, 0.0f});
+                const int f = (j + 6) & 7;  // the partial of two MFMAs earlier
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[f][i] = fmaf(part[f][i], sc, acc[f][i]);
+                part[j] = pj;
+            } else {
+                acc[j] = mfma16(a, b, acc[j]);
+            }
+        }
+    }
+    float t = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        t += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3] + part[j][0];
+    if (scale < 0.0f)  // never for a valid call: keeps the work observable
+        sink[threadIdx.x] = t;
+}
+
 }  // namespace
 
-// Both return a hipError_t value (0 = success); arguments are device
+// All return a hipError_t value (0 = success); arguments are device
 // pointers owned by the caller, the launch goes to `stream`.
 extern "C" int mi_ceiling_normquant_skeleton(const uint16_t *in, int64_t row_stride, uint8_t *out_q, float *out_scale,
                                             uint16_t *out_kv, int64_t M, hipStream_t stream) {
@@ -87,17 +143,35 @@ extern "C" int mi_ceiling_normquant_skeleton(const uint16_t *in, int64_t row_str
     return hipGetLastError();
 }
 
-// slab_bytes: a multiple of 16 KB; reads blocks * slab_bytes bytes from w
+// slab_bytes: a multiple of 4 KB; reads blocks * slab_bytes bytes from w
 extern "C" int mi_ceiling_weight_stream(const uint8_t *w, int64_t slab_bytes, int64_t blocks, unsigned *sink,
                                         hipStream_t stream) {
     if (slab_bytes <= 0 || slab_bytes % kStageBytes != 0 || blocks <= 0 || blocks > 0x7FFFFFFF)
         return hipErrorInvalidValue;
     const size_t lds = static_cast<size_t>(kRing) * kStageBytes;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(weight_stream_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    if (e != hipSuccess)
-        return e;
-    hipLaunchKernelGGL(weight_stream_kernel, dim3(static_cast<unsigned>(blocks)), dim3(512), lds, stream, w,
+    // the LDS limit once per process (first call outside any graph capture;
+    // the benchmark runs on one device)
+    static const hipError_t raised = hipFuncSetAttribute(reinterpret_cast<const void *>(weight_stream_kernel),
+                                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                         static_cast<int>(lds));
+    if (raised != hipSuccess)
+        return raised;
+    hipLaunchKernelGGL(weight_stream_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), lds, stream, w,
                        slab_bytes, sink);
+    return hipGetLastError();
+}
+
+// mfmas_per_wave: a multiple of 8; waves_per_block in 1 .. 16; scale > 0;
+// sink: 64 * waves_per_block floats (written only for an invalid scale)
+extern "C" int mi_ceiling_mfma(int64_t blocks, int waves_per_block, int64_t mfmas_per_wave, int fold, float scale,
+                               float *sink, hipStream_t stream) {
+    if (blocks <= 0 || blocks > 0x7FFFFFFF || waves_per_block < 1 || waves_per_block > 16 || mfmas_per_wave <= 0 ||
+        mfmas_per_wave % 8 != 0 || !(scale > 0.0f))
+        return hipErrorInvalidValue;
+    const dim3 grid(static_cast<unsigned>(blocks)), block(static_cast<unsigned>(64 * waves_per_block));
+    if (fold)
+        hipLaunchKernelGGL(mfma_kernel<true>, grid, block, 0, stream, mfmas_per_wave / 8, scale, sink);
+    else
+        hipLaunchKernelGGL(mfma_kernel<false>, grid, block, 0, stream, mfmas_per_wave / 8, scale, sink);
     return hipGetLastError();
 }
