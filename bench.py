@@ -781,7 +781,7 @@ def ceilings(torch, np, W):
 
 
 PROFILE_LOOPS = ("nq1", "nq8192_row", "nq8192_col", "gemm_a256", "gemm_b256", "gemm_a256_e8m0",
-                 "gemm_b256_e8m0", "pair64")
+                 "gemm_b256_e8m0", "pair64", "tp8pair1")
 
 
 def profile_loops(torch, np, mi, W, names, steps, tiled, flush):
@@ -794,7 +794,9 @@ def profile_loops(torch, np, mi, W, names, steps, tiled, flush):
                     its input and weights of RMSNorm out of the caches
       nq8192_row/col  dual norm-quant of the prefill batch, both layouts
       gemm_{a,b}256[_e8m0]  W_a / W_b GEMM at M = 256, fp32 or e8m0 scales
-      pair64        both GEMMs at M = 64 (the decode step's pair launch)"""
+      pair64        both GEMMs at M = 64 (the decode step's pair launch)
+      tp8pair1      both GEMMs' tensor-parallel shards at TP = 8 (the last
+                    rank's 3072 + 1024 rows), M = 1, one pair launch"""
     dev = torch.device("cuda:0")
     gq = bf16_dev(torch, np, W.gammas()[0], dev)
     gk = bf16_dev(torch, np, W.gammas()[1], dev)
@@ -855,6 +857,21 @@ def profile_loops(torch, np, mi, W, names, steps, tiled, flush):
                               cold_sets(algorithmic_bytes_gemm_pair(64, W.W_A_SHAPE[0], W.W_B_SHAPE[0], W.NQ)), dev,
                               tiled)
             fns = [st["gp"] for st in sets]
+        elif name == "tp8pair1":
+            M, K = 1, W.NQ
+            wa_full = W.block_fp8_weight(*W.W_A_SHAPE, W.W_A_SEED)
+            wb_full = W.block_fp8_weight(*W.W_B_SHAPE, W.W_B_SEED)
+            na, nb = W.W_A_SHAPE[0] // 8, W.W_B_SHAPE[0] // 8
+            wa0, wb0 = dev_weight(wa_full.codes[-na:]), dev_weight(wb_full.codes[-nb:])
+            sa = torch.from_numpy(np.ascontiguousarray(wa_full.scale[-na // 128:])).to(dev)
+            sb = torch.from_numpy(np.ascontiguousarray(wb_full.scale[-nb // 128:])).to(dev)
+            a = torch.randint(0, 0x78, (M, K), dtype=torch.uint8, device=dev)
+            asc = (torch.rand((K // 128, M), dtype=torch.float32, device=dev) + 0.5).T
+            for i in range(cold_sets(algorithmic_bytes_gemm_pair(M, na, nb, K))):
+                fns.append(mi.prepare_block_scaled_fp8_gemm_pair(
+                    a, asc, wa0 if i == 0 else copy_weight(wa0), sa, torch.empty((M, na), dtype=torch.bfloat16,
+                                                                                   device=dev),
+                    wb0 if i == 0 else copy_weight(wb0), sb, torch.empty((M, nb), dtype=torch.bfloat16, device=dev)))
         else:
             raise SystemExit(f"unknown profile loop {name!r}; known: {', '.join(PROFILE_LOOPS)}")
         seq = []

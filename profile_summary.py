@@ -113,6 +113,8 @@ def main(d):
         "gemm_b256_e8m0": ("block_scaled_fp8_gemm_W_b_e8m0", 256,
                            bench.algorithmic_bytes_gemm(256, NB, K) - 3 * (256 * 12 + NB // 128 * 12), gemm_sha),
         "pair64": ("block_scaled_fp8_gemm_pair", 64, bench.algorithmic_bytes_gemm_pair(64, NA, NB, K), gemm_sha),
+        "tp8pair1": ("block_scaled_fp8_gemm_pair_tp8", 1, bench.algorithmic_bytes_gemm_pair(1, NA // 8, NB // 8, K),
+                     gemm_sha),
         "nq8192_row": ("fused_dual_rmsnorm_group_quant_row", 8192, bench.algorithmic_bytes_normquant(8192), nq_sha),
         "nq8192_col": ("fused_dual_rmsnorm_group_quant_col", 8192, bench.algorithmic_bytes_normquant(8192), nq_sha),
         "normquant": ("fused_dual_rmsnorm_group_quant", 64, bench.algorithmic_bytes_normquant(64), nq_sha),
