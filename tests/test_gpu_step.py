@@ -108,6 +108,37 @@ def test_step_vs_oracle(M, weights):
         assert_gemm_close(bf16_to_f64(out)[:, cols], gref, f"step {name}")
 
 
+@pytest.mark.parametrize("M", [16, 64])
+def test_step_every_column_vs_oracle(M, weights):
+    """The decode-step configurations at their full widths (W_a [24576, 1536]
+    and W_b [8192, 1536], all 32 768 output columns; M = 16 in one launch,
+    64 in two): every GEMM output element against the oracle GEMM on the
+    step's own quantised pair, to the element-wise bar: bf16 rounding of the
+    result plus an accumulation error of at most 2^-12 of the sum of the
+    scaled |a| |w| products."""
+    dev = gpu_or_skip()
+    case = W.strided_batch(M)
+    q, kv, gq, gk = device_case(case, dev)
+    wa, wb = weights["W_a"], weights["W_b"]
+    codes, scale, _, o1, o2 = mi.mi_fused_normquant_gemm_pair(
+        q, kv, gq, gk, case.eps, True, wa["tiled"], wa["scale"], wb["tiled"], wb["scale"])
+    torch.cuda.synchronize()
+    q_np, s_np = codes.cpu().numpy(), scale_buffer(scale)
+    a_abs = np.abs(oracle.e4m3_decode_array(q_np)) * np.repeat(s_np.reshape(12, M).T.astype(np.float64), 128, axis=1)
+    for name, out in (("W_a", o1), ("W_b", o2)):
+        wt = weights[name]["host"]
+        ref = oracle.block_scaled_fp8_gemm(q_np, s_np, True, wt.codes, wt.scale)
+        w_abs = np.abs(oracle.e4m3_decode_array(wt.codes)) * np.repeat(
+            np.repeat(wt.scale.astype(np.float64), 128, axis=0), 128, axis=1)
+        mag = a_abs @ w_abs.T
+        got = bf16_to_f64(out)
+        err = np.abs(got - ref)
+        fro, mx = assert_gemm_close(got, ref, f"step M{M} {name} all columns")
+        print(f"step M{M} {name} [{wt.codes.shape[0]} columns]: fro {fro:.2e} max {mx:.2e} "
+              f"max(err/mag) {np.max(err / mag):.3e}")
+        assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 2.0 ** -12 * mag), f"step M{M} {name}"
+
+
 def test_step_back_to_back_with_changing_inputs(weights):
     """Calls on one stream sharing the output buffers, with new activations
     every call and batch sizes 16, 1, 64, 7, 33, 64, 17, 16 (one and two
