@@ -710,13 +710,15 @@ def ceilings(torch, np, W):
       mfma[_fold]_{W_a,W_b}_M256: the GEMM's 16x16x128 FP8 MFMAs at M = 256
       (W_a: 256 workgroups x 12 waves x 96, W_b: 256 x 4 x 96) on register
       operands, no memory traffic, with the fp32-scale fold or accumulating
-      in place (e8m0): the matrix-core floor at the clock the chip holds."""
+      in place (e8m0): the matrix-core floor at the clock the chip holds,
+      whose waves' shader-clock / real-time counters give that clock
+      (`shader_clock_GHz`: 5th, 50th, 95th percentile over the waves)."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "rmsnorm_fp8_block_amd", "libmi_ceiling.so"))
     p, i64 = ctypes.c_void_p, ctypes.c_int64
     lib.mi_ceiling_normquant_skeleton.argtypes = [p, i64, p, p, p, i64, p]
     lib.mi_ceiling_weight_stream.argtypes = [p, i64, i64, p, p]
-    lib.mi_ceiling_mfma.argtypes = [i64, ctypes.c_int, i64, ctypes.c_int, ctypes.c_float, p, p]
+    lib.mi_ceiling_mfma.argtypes = [i64, ctypes.c_int, i64, ctypes.c_int, ctypes.c_float, p, p, p]
     dev = torch.device("cuda:0")
     stream = lambda: ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     res = {}
@@ -768,15 +770,27 @@ def ceilings(torch, np, W):
     msink = torch.zeros(1024, dtype=torch.float32, device=dev)
     for name, blocks, waves, per_wave in (("W_a_M256", 256, 12, 96), ("W_b_M256", 256, 4, 96)):
         for fold in (True, False):
-            def mf(blocks=blocks, waves=waves, per_wave=per_wave, fold=fold):
-                st = lib.mi_ceiling_mfma(blocks, waves, per_wave, int(fold), 1.0, msink.data_ptr(), stream())
+            def mf(blocks=blocks, waves=waves, per_wave=per_wave, fold=fold, clocks=None):
+                st = lib.mi_ceiling_mfma(blocks, waves, per_wave, int(fold), 1.0, msink.data_ptr(),
+                                         None if clocks is None else clocks.data_ptr(), stream())
                 if st != 0:
                     raise RuntimeError(f"mi_ceiling_mfma: hip error {st}")
             us = time_ceiling(torch, [mf] * 20)
             flops = blocks * waves * per_wave * 16 * 16 * 128 * 2
-            res[f"mfma{'_fold' if fold else ''}_{name}"] = {
-                "us": round(us, 3), "mfmas": blocks * waves * per_wave, "launch": [blocks, waves, per_wave],
-                "TFLOP/s": round(flops / us / 1e6, 1), "frac_fp8_peak": round(flops / us / 1e6 / FP8_MFMA_PEAK_TFLOPS, 4)}
+            entry = {"us": round(us, 3), "mfmas": blocks * waves * per_wave, "launch": [blocks, waves, per_wave],
+                     "TFLOP/s": round(flops / us / 1e6, 1),
+                     "frac_fp8_peak": round(flops / us / 1e6 / FP8_MFMA_PEAK_TFLOPS, 4)}
+            # one more launch (eager, after the timed ones) with the waves' clock
+            # counters: shader cycles over 100 MHz real time
+            clocks = torch.zeros(4 * blocks * waves, dtype=torch.int64, device=dev)
+            mf(clocks=clocks)
+            torch.cuda.synchronize()
+            c = clocks.view(-1, 4).cpu().numpy().astype(np.float64)
+            ok = c[:, 3] > c[:, 1]
+            if ok.any():
+                ghz = (c[ok, 2] - c[ok, 0]) / (c[ok, 3] - c[ok, 1]) * 0.1
+                entry["shader_clock_GHz"] = [round(float(np.percentile(ghz, q)), 3) for q in (5, 50, 95)]
+            res[f"mfma{'_fold' if fold else ''}_{name}"] = entry
     return res
 
 

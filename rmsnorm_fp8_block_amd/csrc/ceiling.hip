@@ -26,7 +26,9 @@
 //    later (the fp32-scale kernels' per-K-block fold); without, every MFMA
 //    accumulates in place (the e8m0 kernels, whose scales the matrix core
 //    applies).  Its time is what the matrix cores allow at the clock the
-//    chip holds under that load, launch and ramp included.
+//    chip holds under that load, launch and ramp included; on request it
+//    records each wave's shader-clock and real-time counters, which give
+//    that clock.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -90,8 +92,11 @@ __device__ __forceinline__ v4f mfma16(const v8i &a, const v8i &b, const v4f &c) 
 }
 
 template <bool kFold>
-__global__ __launch_bounds__(1024) void mfma_kernel(int64_t rounds, float scale, float *sink) {
+__global__ __launch_bounds__(1024) void mfma_kernel(int64_t rounds, float scale, float *sink,
+                                                    unsigned long long *clocks) {
     const int lane = threadIdx.x & 63;
+    const int64_t wave = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const unsigned long long c0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
     v8i a, b;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -127,6 +132,14 @@ __global__ __launch_bounds__(1024) void mfma_kernel(int64_t rounds, float scale,
         t += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3] + part[j][0];
     if (scale < 0.0f)  // never for a valid call: keeps the work observable
         sink[threadIdx.x] = t;
+    if (clocks != nullptr && lane == 0) {
+        // shader-clock and 100 MHz real-time counters around this wave's work
+        const unsigned long long c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+        clocks[4 * wave + 0] = c0;
+        clocks[4 * wave + 1] = r0;
+        clocks[4 * wave + 2] = c1;
+        clocks[4 * wave + 3] = r1;
+    }
 }
 
 }  // namespace
@@ -162,16 +175,18 @@ extern "C" int mi_ceiling_weight_stream(const uint8_t *w, int64_t slab_bytes, in
 }
 
 // mfmas_per_wave: a multiple of 8; waves_per_block in 1 .. 16; scale > 0;
-// sink: 64 * waves_per_block floats (written only for an invalid scale)
+// sink: 64 * waves_per_block floats (written only for an invalid scale);
+// clocks: null, or 4 * blocks * waves_per_block counters (per wave: shader
+// clock and 100 MHz real time at its start, then at its end)
 extern "C" int mi_ceiling_mfma(int64_t blocks, int waves_per_block, int64_t mfmas_per_wave, int fold, float scale,
-                               float *sink, hipStream_t stream) {
+                               float *sink, unsigned long long *clocks, hipStream_t stream) {
     if (blocks <= 0 || blocks > 0x7FFFFFFF || waves_per_block < 1 || waves_per_block > 16 || mfmas_per_wave <= 0 ||
         mfmas_per_wave % 8 != 0 || !(scale > 0.0f))
         return hipErrorInvalidValue;
     const dim3 grid(static_cast<unsigned>(blocks)), block(static_cast<unsigned>(64 * waves_per_block));
     if (fold)
-        hipLaunchKernelGGL(mfma_kernel<true>, grid, block, 0, stream, mfmas_per_wave / 8, scale, sink);
+        hipLaunchKernelGGL(mfma_kernel<true>, grid, block, 0, stream, mfmas_per_wave / 8, scale, sink, clocks);
     else
-        hipLaunchKernelGGL(mfma_kernel<false>, grid, block, 0, stream, mfmas_per_wave / 8, scale, sink);
+        hipLaunchKernelGGL(mfma_kernel<false>, grid, block, 0, stream, mfmas_per_wave / 8, scale, sink, clocks);
     return hipGetLastError();
 }
