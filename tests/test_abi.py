@@ -464,3 +464,23 @@ def test_init_reports_hip_errors_without_a_device(L):
     assert L.mi_init() == B.MI_ERR_HIP
     with pytest.raises(mi.MiError):
         mi.mi_init()
+
+
+def test_ceiling_library_loads_and_refuses_bad_arguments():
+    """The benchmark's ceiling library (bench.py only; nothing in the hot
+    path calls it) exports its three skeletons, and each refuses malformed
+    sizes before touching the device (so this runs without a GPU)."""
+    from rmsnorm_fp8_block_amd import build
+    C = ctypes.CDLL(build.CEILING_LIB)
+    p, i64 = ctypes.c_void_p, ctypes.c_int64
+    C.mi_ceiling_normquant_skeleton.argtypes = [p, i64, p, p, p, i64, p]
+    C.mi_ceiling_weight_stream.argtypes = [p, i64, i64, p, p]
+    C.mi_ceiling_mfma.argtypes = [i64, ctypes.c_int, i64, ctypes.c_int, ctypes.c_float, p, p, p]
+    ok = 0
+    assert C.mi_ceiling_normquant_skeleton(None, 2048, None, None, None, 0, None) == ok   # M = 0: nothing to launch
+    for slab, blocks in ((4096 + 1, 1), (0, 1), (4096, 0), (4096, 1 << 31)):
+        assert C.mi_ceiling_weight_stream(None, slab, blocks, None, None) != ok, (slab, blocks)
+    for blocks, waves, per_wave, scale in ((0, 4, 96, 1.0), (1, 0, 96, 1.0), (1, 17, 96, 1.0), (1, 4, 95, 1.0),
+                                           (1, 4, 0, 1.0), (1, 4, 96, 0.0), (1, 4, 96, -1.0)):
+        assert C.mi_ceiling_mfma(blocks, waves, per_wave, 1, scale, None, None, None) != ok, \
+            (blocks, waves, per_wave, scale)
