@@ -1291,6 +1291,22 @@ hipError_t launch_stream_kb(const GemmParams &p, int waves, hipStream_t stream) 
     return waves == 3 ? launch_stream_w<kKB, 4, 3>(p, stream) : launch_stream_w<kKB, 4, 4>(p, stream);
 }
 
+// The stream kernel with one 16-row subtile per wave and as many waves per
+// block as the CU has subtiles (2 .. 5), for decode batches of up to 16 rows.
+template <bool kE8m0>
+hipError_t launch_stream_one_per_wave(const GemmParams &p, int waves, hipStream_t stream) {
+    switch (waves) {
+    case 2:
+        return launch_stream_scaled<12, 1, 1, 2, kE8m0>(p, stream);
+    case 3:
+        return launch_stream_scaled<12, 1, 1, 3, kE8m0>(p, stream);
+    case 4:
+        return launch_stream_scaled<12, 1, 1, 4, kE8m0>(p, stream);
+    default:
+        return launch_stream_scaled<12, 1, 1, 5, kE8m0>(p, stream);
+    }
+}
+
 // The stream kernel, 2 subtiles per wave, where its grid (weight slabs x
 // 64-row chunks) covers the CUs: decode batches (M <= 64) over at least 6
 // weight subtiles per CU (3 waves per block at 6, else 4), and 64 < M <= 256
@@ -1298,14 +1314,16 @@ hipError_t launch_stream_kb(const GemmParams &p, int waves, hipStream_t stream) 
 hipError_t launch_stream(const GemmParams &p, hipStream_t stream) {
     const int64_t S = (p.N + p.N2) / 16, cus = device_cu_count();
     const int64_t per_cu = (S + cus - 1) / cus;
-    // Decode batches over narrow weights with two 16-row subtiles per CU (a
-    // tensor-parallel shard of 4096-8192 weight rows): one subtile per wave,
-    // two waves per block, a block per CU (measured: the TP4 pair at M = 1
-    // 5.4 -> 4.9 us against the wide kernel's half as many blocks; with one
-    // subtile per CU, one-wave blocks were no faster than the wide kernel).
-    if (p.M <= 16 && per_cu == 2 && p.K / kBlk == 12)
-        return p.scale_e8m0 ? launch_stream_scaled<12, 1, 1, 2, true>(p, stream)
-                            : launch_stream_scaled<12, 1, 1, 2, false>(p, stream);
+    // Decode batches over narrow weights with two to five 16-row subtiles
+    // per CU (a tensor-parallel shard of 4096-20480 weight rows): one
+    // subtile per wave, a wave per subtile of the CU, a block per CU
+    // (measured against the wide kernel: the TP4 pair at M = 1 5.4 -> 4.9
+    // us, the TP2 pair 7.5 -> 6.0 us at M = 1 and 7.6 -> 6.4 us at M = 16,
+    // TP2 W_a alone 6.7 -> 5.4 us; at 32 and 64 rows no steady gain; one
+    // subtile per CU takes the split-K kernel).
+    if (p.M <= 16 && per_cu >= 2 && per_cu <= 5 && p.K / kBlk == 12)
+        return p.scale_e8m0 ? launch_stream_one_per_wave<true>(p, static_cast<int>(per_cu), stream)
+                            : launch_stream_one_per_wave<false>(p, static_cast<int>(per_cu), stream);
     if (p.M > 256 || (p.M <= 64 && per_cu < 6))
         return hipErrorNotSupported;
     if (p.M > 64) {

@@ -132,3 +132,27 @@ def test_split_k_equals_the_k_loop_kernels(M):
                 torch.cuda.synchronize()
                 assert np.array_equal(host_bf16_bits(single), host_bf16_bits(paired)), \
                     f"M{M} [{cs.shape[0]}] tiled={tiled} t={layout}"
+
+
+@pytest.mark.parametrize("M", [1, 16])
+@pytest.mark.parametrize("N", [12288, 16384, 20480])
+def test_one_subtile_per_wave_equals_the_two_subtile_kernel(N, M):
+    """Weights of three to five 16-row subtiles per CU (N = 12288, 16384,
+    20480 on 256 CUs) at up to 16 rows run the stream kernel with one subtile
+    per wave and a wave per subtile; paired with W_a the same weight runs
+    the stream kernel with two subtiles per wave.  The outputs must be equal
+    bit for bit, tiled weights, both As layouts."""
+    dev = gpu_or_skip()
+    wa, _ = full_weights()
+    wt = W.block_fp8_weight(N, 1536, 700 + N // 4096)
+    r = np.random.default_rng(800 + M + N)
+    a = dev_u8(r.integers(0, 0x100, size=(M, 1536), dtype=np.uint8) & 0xF7, dev)   # no NaN codes
+    As = np.exp2(r.uniform(-8, 0, (M, 12))).astype(np.float32)
+    dw, ds = mi.relayout_weight(dev_u8(wt.codes, dev)), dev_f32(wt.scale, dev)
+    da, dsa = mi.relayout_weight(dev_u8(wa.codes, dev)), dev_f32(wa.scale, dev)
+    for layout in (False, True):
+        das = dev_f32(As.T.copy(), dev).T if layout else dev_f32(As, dev)
+        single = mi.mi_block_scaled_fp8_gemm(a, das, dw, ds)
+        paired, _ = mi.mi_block_scaled_fp8_gemm_pair(a, das, dw, ds, da, dsa)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bf16_bits(single), host_bf16_bits(paired)), f"N{N} M{M} t={layout}"
