@@ -1292,7 +1292,7 @@ hipError_t launch_stream_kb(const GemmParams &p, int waves, hipStream_t stream) 
 }
 
 // The stream kernel with one 16-row subtile per wave and as many waves per
-// block as the CU has subtiles (2 .. 5), for decode batches of up to 16 rows.
+// block as the CU has subtiles (2 .. 8), for decode batches of up to 16 rows.
 template <bool kE8m0>
 hipError_t launch_stream_one_per_wave(const GemmParams &p, int waves, hipStream_t stream) {
     switch (waves) {
@@ -1302,8 +1302,14 @@ hipError_t launch_stream_one_per_wave(const GemmParams &p, int waves, hipStream_
         return launch_stream_scaled<12, 1, 1, 3, kE8m0>(p, stream);
     case 4:
         return launch_stream_scaled<12, 1, 1, 4, kE8m0>(p, stream);
-    default:
+    case 5:
         return launch_stream_scaled<12, 1, 1, 5, kE8m0>(p, stream);
+    case 6:
+        return launch_stream_scaled<12, 1, 1, 6, kE8m0>(p, stream);
+    case 7:
+        return launch_stream_scaled<12, 1, 1, 7, kE8m0>(p, stream);
+    default:
+        return launch_stream_scaled<12, 1, 1, 8, kE8m0>(p, stream);
     }
 }
 
@@ -1314,14 +1320,16 @@ hipError_t launch_stream_one_per_wave(const GemmParams &p, int waves, hipStream_
 hipError_t launch_stream(const GemmParams &p, hipStream_t stream) {
     const int64_t S = (p.N + p.N2) / 16, cus = device_cu_count();
     const int64_t per_cu = (S + cus - 1) / cus;
-    // Decode batches over narrow weights with two to five 16-row subtiles
-    // per CU (a tensor-parallel shard of 4096-20480 weight rows): one
-    // subtile per wave, a wave per subtile of the CU, a block per CU
-    // (measured against the wide kernel: the TP4 pair at M = 1 5.4 -> 4.9
-    // us, the TP2 pair 7.5 -> 6.0 us at M = 1 and 7.6 -> 6.4 us at M = 16,
-    // TP2 W_a alone 6.7 -> 5.4 us; at 32 and 64 rows no steady gain; one
-    // subtile per CU takes the split-K kernel).
-    if (p.M <= 16 && per_cu >= 2 && per_cu <= 5 && p.K / kBlk == 12)
+    // Decode batches of up to 16 rows over weights of two to eight 16-row
+    // subtiles per CU (4096-32768 weight rows: tensor-parallel shards, W_a,
+    // the pair): one subtile per wave, a wave per subtile of the CU, a block
+    // per CU.  Measured against the wide kernel (two to five subtiles per
+    // CU): the TP4 pair at M = 1 5.4 -> 4.9 us, the TP2 pair 7.5 -> 6.0 us
+    // at M = 1 and 7.6 -> 6.4 us at M = 16, TP2 W_a alone 6.7 -> 5.4 us;
+    // against two subtiles per wave (six and eight per CU): W_a alone and
+    // the pair 2-5 % faster at M = 1 and 16.  At 32 and 64 rows no steady
+    // gain; one subtile per CU takes the split-K kernel.
+    if (p.M <= 16 && per_cu >= 2 && per_cu <= 8 && p.K / kBlk == 12)
         return p.scale_e8m0 ? launch_stream_one_per_wave<true>(p, static_cast<int>(per_cu), stream)
                             : launch_stream_one_per_wave<false>(p, static_cast<int>(per_cu), stream);
     if (p.M > 256 || (p.M <= 64 && per_cu < 6))
@@ -1352,7 +1360,7 @@ hipError_t launch_stream(const GemmParams &p, hipStream_t stream) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode step in one launch (M <= 64 rows of the MLA latent shape: Nq = K =
+// Decode step in one launch (up to 16 rows of the MLA latent shape: Nq = K =
 // 1536, Nkv = 512): the fused dual RMSNorm + 1x128 FP8 group quantisation of
 // the rows and both consumer GEMMs of its output.
 //
@@ -1504,9 +1512,9 @@ __global__ __launch_bounds__((kWaves + 1) * kWave) void normquant_gemm_pair_kern
     w.store_tile(p, 0, st0);
 }
 
-template <int kMT, int kWaves, bool kE8m0>
+template <int kMT, int kWaves, bool kE8m0, int kSW>
 hipError_t launch_normquant_gemm_pair_mt(const NormQuantParams &a, const GemmParams &p, hipStream_t stream) {
-    constexpr int kKB = 12, kSW = 2;
+    constexpr int kKB = 12;
     constexpr int kD = stream_depth<kKB, kMT, kSW, kWaves, kE8m0>();
     using P = StreamPlan<kKB, kMT, kSW, kWaves, kD, kE8m0>;
     const int64_t per_block = kWaves * kSW;
@@ -1808,7 +1816,7 @@ bool normquant_gemm_pair_one_launch(int64_t M, int64_t Nq, int64_t Nkv, int64_t 
         return false;
     const int64_t S = (N1 + N2) / 16, cus = device_cu_count();
     const int64_t per_cu = (S + cus - 1) / cus;
-    return per_cu >= 6 && M <= S / (2 * (per_cu <= 6 ? 3 : 4));
+    return per_cu >= 6 && M <= S / (per_cu <= 6 ? 6 : 8);  // the grid's blocks (6 or 8 subtiles each)
 }
 
 hipError_t launch_normquant_gemm_pair(const NormQuantParams &a, const GemmParams &p, hipStream_t stream) {
@@ -1823,11 +1831,14 @@ hipError_t launch_normquant_gemm_pair(const NormQuantParams &a, const GemmParams
     const int64_t S = (p.N + p.N2) / 16, cus = device_cu_count();
     const bool three = (S + cus - 1) / cus <= 6;
     static_assert(kStepMaxRows <= 16, "one 16-row chunk per block");
+    // one weight subtile per compute wave (six or eight waves: the stream
+    // kernel's decode form for these widths; the M = 16 step 11.7 -> 10.9 us
+    // against two subtiles per wave, M = 1 unchanged)
     if (e8m0)
-        return three ? launch_normquant_gemm_pair_mt<1, 3, true>(a, p, stream)
-                     : launch_normquant_gemm_pair_mt<1, 4, true>(a, p, stream);
-    return three ? launch_normquant_gemm_pair_mt<1, 3, false>(a, p, stream)
-                 : launch_normquant_gemm_pair_mt<1, 4, false>(a, p, stream);
+        return three ? launch_normquant_gemm_pair_mt<1, 6, true, 1>(a, p, stream)
+                     : launch_normquant_gemm_pair_mt<1, 8, true, 1>(a, p, stream);
+    return three ? launch_normquant_gemm_pair_mt<1, 6, false, 1>(a, p, stream)
+                 : launch_normquant_gemm_pair_mt<1, 8, false, 1>(a, p, stream);
 }
 
 hipError_t init_device() {
