@@ -1,6 +1,7 @@
 """mi_init (include/mi_normquant.h): after it, the first call of each GEMM
 kernel that needs a raised LDS limit (the decode step in one launch and in
-two, the stream pair, the wide and the decode GEMMs, fp32 and e8m0 scales)
+two, the stream pair, the TP-shard forms, the wide and the decode GEMMs, fp32
+and e8m0 scales)
 can be captured into a HIP graph with no ordinary call before it, and the replay
 equals an eager call bit for bit.  Run in a fresh process, so that no
 earlier test has launched (and thereby prepared) those kernels."""
@@ -64,6 +65,18 @@ def step48_outs():
             torch.empty((48, 512), dtype=torch.bfloat16, device=dev), torch.empty((48, 24576), dtype=torch.bfloat16, device=dev),
             torch.empty((48, 8192), dtype=torch.bfloat16, device=dev))
 cases.append(("step M=48", step48, step48_outs))
+# TP shards at M = 1: the TP-8 pair (split-K, one subtile per CU) and the
+# TP-2 pair (stream kernel, one subtile per wave, four per CU)
+a1, s1 = codes(1, 1536), fscale(12, 1).T
+wa8, wb8 = mi.relayout_weight(codes(3072, 1536)), mi.relayout_weight(codes(1024, 1536))
+wa2, wb2 = mi.relayout_weight(codes(12288, 1536)), mi.relayout_weight(codes(4096, 1536))
+for tag, x1, x2 in (("TP-8", wa8, wb8), ("TP-2", wa2, wb2)):
+    y1, y2 = fscale(x1.N // 128, 12), fscale(x2.N // 128, 12)
+    cases.append((f"{tag} pair M=1",
+                  lambda o, x1=x1, x2=x2, y1=y1, y2=y2: mi.prepare_block_scaled_fp8_gemm_pair(
+                      a1, s1, x1, y1, o[0], x2, y2, o[1]),
+                  lambda x1=x1, x2=x2: (torch.empty((1, x1.N), dtype=torch.bfloat16, device=dev),
+                                        torch.empty((1, x2.N), dtype=torch.bfloat16, device=dev))))
 # stream pair, M = 64, column-major scales
 a64, s64 = codes(64, 1536), fscale(12, 64).T
 def pair(o):
