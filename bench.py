@@ -1056,6 +1056,13 @@ def main():
     roofline = {"bound": "hbm", "achieved": dk["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": dk["frac_hbm"], "traffic": dk["traffic"],
                 "kernel": dom, "bytes_per_launch": dk["bytes"], "us_per_launch": dk["us"]}
+    # the committed rocprofv3 kernel-trace median of the same kernel source
+    # and launch (profile loop pair64: the pair at 64 rows, cold), beside the
+    # events figure, which also holds the gap between back-to-back launches
+    med = kernel_medians(GEMM_SOURCES) if dom == "block_scaled_fp8_gemm_pair" and M == 64 else None
+    if med and "pair64" in med:
+        roofline["rocprof_median_us"] = med["pair64"]["median_us"]
+        roofline["frac_rocprof_median"] = round(dk["bytes"] / med["pair64"]["median_us"] / 1e3 / HBM_PEAK_GBS, 4)
 
     line = {
         "metric": METRIC,
