@@ -78,10 +78,11 @@ def test_gemm_random_vs_oracle(M, N, K, seed):
 
 @pytest.mark.parametrize("M,N,K,seed", [(65, 384, 512, 21), (129, 1280, 1024, 22), (100, 1536, 1536, 23),
                                         (256, 16640, 1536, 24), (72, 32768, 512, 25), (200, 12288, 1536, 26),
-                                        (256, 8192, 2048, 27), (256, 24576, 1536, 28)])
+                                        (256, 8192, 2048, 27), (256, 24576, 1536, 28), (193, 8192, 1536, 29)])
 def test_gemm_wide_shapes_sampled(M, N, K, seed):
     """64 < M <= 256 at widths that give 2, 4, 6 and 8 weight subtiles per
-    block, with a ragged last block (N = 16640: 1040 subtiles in blocks of 6).
+    block, with a ragged last block (N = 16640: 1040 subtiles in blocks of 6);
+    W_b's width at 193 rows (the stream kernel, one row in its last chunk).
     The oracle runs on the first, the last and two random 128-column blocks."""
     dev = gpu_or_skip()
     a, As, w, Bs = random_operands(M, N, K, seed)

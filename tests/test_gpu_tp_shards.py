@@ -156,3 +156,28 @@ def test_one_subtile_per_wave_equals_the_two_subtile_kernel(N, M):
         paired, _ = mi.mi_block_scaled_fp8_gemm_pair(a, das, dw, ds, da, dsa)
         torch.cuda.synchronize()
         assert np.array_equal(host_bf16_bits(single), host_bf16_bits(paired)), f"N{N} M{M} t={layout}"
+
+
+@pytest.mark.parametrize("which", ["W_b", "TP2 W_a"])
+def test_a_row_does_not_depend_on_its_batch(which):
+    """Every output row depends only on its own activation row and scales, and
+    every kernel folds the K blocks in the same order, so a row must come out
+    bit for bit the same whatever batch it is computed in: 256 rows (the stream
+    kernel in 64-row chunks) against slices of 16 (one subtile per wave), 64,
+    100 and 200 rows, for W_b and the last TP-2 shard of W_a, both As layouts."""
+    dev = gpu_or_skip()
+    wa, wb = full_weights()
+    codes, scale = (wb.codes, wb.scale) if which == "W_b" else shard(wa, 2, 1)
+    r = np.random.default_rng(900 + (which == "W_b"))
+    a = r.integers(0, 0x100, size=(256, 1536), dtype=np.uint8) & 0xF7   # no NaN codes
+    As = np.exp2(r.uniform(-8, 0, (256, 12))).astype(np.float32)
+    dw, ds = mi.relayout_weight(dev_u8(codes, dev)), dev_f32(scale, dev)
+    for layout in (False, True):
+        def run(lo, hi):
+            das = dev_f32(As[lo:hi].T.copy(), dev).T if layout else dev_f32(As[lo:hi].copy(), dev)
+            out = mi.mi_block_scaled_fp8_gemm(dev_u8(a[lo:hi].copy(), dev), das, dw, ds)
+            torch.cuda.synchronize()
+            return host_bf16_bits(out)
+        full = run(0, 256)
+        for lo, hi in ((0, 16), (240, 256), (64, 128), (3, 103), (0, 200), (56, 256)):
+            assert np.array_equal(run(lo, hi), full[lo:hi]), f"{which} rows {lo}:{hi} t={layout}"
