@@ -1313,11 +1313,10 @@ hipError_t launch_stream_one_per_wave(const GemmParams &p, int waves, hipStream_
     }
 }
 
-// The stream kernel where its grid (weight slabs x 64-row chunks) covers the
-// CUs: decode batches (M <= 64) over at least 6 weight subtiles per CU (2
-// subtiles per wave, 3 waves per block at 6, else 4), and 64 < M <= 256 (one
-// subtile per wave, 8 waves at K/128 = 12; else 2 per wave, 4 waves).  K/128
-// in {4, 8, 12}.  Returns hipErrorNotSupported otherwise.
+// The stream kernel, 2 subtiles per wave, where its grid (weight slabs x
+// 64-row chunks) covers the CUs: decode batches (M <= 64) over at least 6
+// weight subtiles per CU (3 waves per block at 6, else 4), and 64 < M <= 256
+// (4 waves).  K/128 in {4, 8, 12}.  Returns hipErrorNotSupported otherwise.
 hipError_t launch_stream(const GemmParams &p, hipStream_t stream) {
     const int64_t S = (p.N + p.N2) / 16, cus = device_cu_count();
     const int64_t per_cu = (S + cus - 1) / cus;
@@ -1346,13 +1345,6 @@ hipError_t launch_stream(const GemmParams &p, hipStream_t stream) {
         const int64_t stream_bytes = nm * wbytes + slabs * nm * 64 * p.K;
         if (slabs * nm < cus || stream_bytes >= wide_bytes)
             return hipErrorNotSupported;
-        // One subtile per wave, 8 waves: the same grid as 4 waves of two, each
-        // wave's fold and stores half as long.  Measured (alternating order,
-        // bit-identical): W_b at M = 128 7.1-7.7 -> 7.0 us, the TP2 W_a shard at
-        // M = 256 14.6-14.8 -> 14.2 us, W_b at M = 256 unchanged (8.8-9.8 us).
-        if (p.K / kBlk == 12)
-            return p.scale_e8m0 ? launch_stream_scaled<12, 4, 1, 8, true>(p, stream)
-                                : launch_stream_scaled<12, 4, 1, 8, false>(p, stream);
     }
     const int waves = p.M <= 64 && per_cu <= 6 ? 3 : 4;
     switch (p.K / kBlk) {
