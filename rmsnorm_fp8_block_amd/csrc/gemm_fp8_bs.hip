@@ -253,10 +253,15 @@ __device__ __forceinline__ void wait_vmcnt() {
 // Per K-block kb: wait until this wave's loads of stage kb + 1 have landed
 // (exact vmcnt count, worked out at compile time from the issue order),
 // drain LDS reads, one plain s_barrier (all waves' parts of stage kb + 1 are
-// in LDS and every wave has stage kb in registers), refill the slots of
-// stage kb, read stage kb + 1 into the second register set, then the MFMAs
-// of stage kb.  The scale FMAs of an MFMA are issued two MFMAs later, in
-// the matrix core's shadow.
+// in LDS and every wave has stage kb in registers), then the MFMAs of stage
+// kb with the refill of stage kb's slots and the reads of stage kb + 1 into
+// the second register set spread between them, one direct load and one
+// read step after each MFMA.  The scale FMAs of an MFMA are issued two
+// MFMAs later.  With one wave per SIMD a K-block is bound by that wave's
+// issue of loads, LDS reads and fold FMAs, which run beside its MFMAs only
+// when interleaved with them (measured per K-block at M = 256: 1800 cycles
+// with the loads and reads issued as a group before the MFMAs, 1300-1500
+// interleaved; the MFMAs alone take 768).
 // ---------------------------------------------------------------------------
 constexpr int kWideWaves = 4;  // 1 per SIMD
 
@@ -409,6 +414,90 @@ struct WideWave {
         }
     }
 
+    // One direct load of iteration kb's refill: the i-th of the order in
+    // which issue_a (stage kb + kRA) and then issue_w (stage kb + kRW) issue
+    // them, so the wait counts, which depend only on that order, still hold.
+    template <int kb, int i>
+    __device__ __forceinline__ void load_step() {
+        constexpr int sa = kb + P::kRA, sw = kb + P::kRW;
+        constexpr int na = sa < kKB ? P::kNA : 0;
+        constexpr int nw = sw < kKB ? P::kNW : 0;
+        if constexpr (i < na) {
+            if constexpr (i < 2 * kMT) {
+                uint8_t *dst = lds + P::kAOff + (sa % P::kRA) * P::kAStage + wave * kMT * 2 * P::kSlot;
+                load_to_lds<16>(a + sa * kBlk + a_off[i / 2][i % 2], dst + i * P::kSlot);
+            } else {
+                uint8_t *sdst = lds + P::kSOff + (sa % P::kRA) * P::kSStage + wave * (kE8m0 ? 1 : 2) * kWave * 4;
+                const uint8_t *ssrc = a_scale + sa * s_stride;
+                if constexpr (kE8m0)
+                    load_to_lds<1>(ssrc + s_off, sdst);
+                else if constexpr (i == 2 * kMT)
+                    load_to_lds<4>(ssrc + s_off, sdst);
+                else
+                    load_to_lds<4>(bsrc + sa, sdst + kWave * 4);
+            }
+        } else if constexpr (i < na + nw) {
+            constexpr int k = i - na;
+            uint8_t *dst = lds + P::kWOff + (sw % P::kRW) * P::kWStage;
+            load_to_lds<16, 2>(wbase[k] + sw * w_kstride + w_off, dst + wslot[k] * P::kSlot);
+        }
+    }
+
+    // One step of read_frags<st>: step i < kMT reads m-tile i's activation
+    // fragment and scale, step kMT + t subtile t's weight fragment and scale.
+    template <int st, int i>
+    __device__ __forceinline__ void read_step() {
+        constexpr int b = st & 1;
+        if constexpr (i < kMT) {
+            const uint8_t *as = lds + P::kAOff + (st % P::kRA) * P::kAStage + wave * kMT * 2 * P::kSlot;
+            const float *ss = reinterpret_cast<const float *>(lds + P::kSOff + (st % P::kRA) * P::kSStage) +
+                              wave * (kE8m0 ? 1 : 2) * kWave;
+            af[b][i] = join4(*reinterpret_cast<const v4u32 *>(as + (2 * i) * P::kSlot + frag_lo),
+                             *reinterpret_cast<const v4u32 *>(as + (2 * i) * P::kSlot + frag_hi));
+            if constexpr (kE8m0)
+                asb[b][i] = reinterpret_cast<const uint32_t *>(ss)[16 * i + (lane & 15)];
+            else
+                asv[b][i] = ss[16 * i + (lane & 15)];
+        } else if constexpr (i < kMT + kNS) {
+            constexpr int t = i - kMT;
+            const uint8_t *ws = lds + P::kWOff + (st % P::kRW) * P::kWStage;
+            wfs[b][t] = join4(*reinterpret_cast<const v4u32 *>(ws + (2 * t) * P::kSlot + wfrag_lo),
+                              *reinterpret_cast<const v4u32 *>(ws + (2 * t) * P::kSlot + wfrag_hi));
+            if constexpr (!kE8m0) {
+                const float *ss = reinterpret_cast<const float *>(lds + P::kSOff + (st % P::kRA) * P::kSStage) +
+                                  wave * 2 * kWave;
+                bss[b][t] = ss[kWave + t];  // same address in every lane: broadcast read
+            }
+        }
+    }
+
+    // The work issued after MFMA n of K-block kb: loads [n kLPer, (n + 1) kLPer)
+    // of the refill, and the read steps of stage kb + 1 whose slot is n (step
+    // i after MFMA i when they fit, else spread evenly over the MFMAs).
+    static constexpr int kSlots = kNS * kMT;
+    static constexpr int kLoads = P::kNA + P::kNW;
+    static constexpr int kLPer = (kLoads + kSlots - 1) / kSlots;
+    static constexpr int kReads = kMT + kNS;
+    static constexpr int read_slot(int i) { return kReads <= kSlots ? i : (i * kSlots) / kReads; }
+    static_assert(kLPer * kSlots >= kLoads && read_slot(kReads - 1) < kSlots, "every load and read has a slot");
+
+    template <int kb, int n, int i = 0>
+    __device__ __forceinline__ void loads_at() {
+        if constexpr (i < kLoads) {
+            if constexpr (i / kLPer == n)
+                load_step<kb, i>();
+            loads_at<kb, n, i + 1>();
+        }
+    }
+    template <int st, int n, int i = 0>
+    __device__ __forceinline__ void reads_at() {
+        if constexpr (i < kReads) {
+            if constexpr (read_slot(i) == n)
+                read_step<st, i>();
+            reads_at<st, n, i + 1>();
+        }
+    }
+
     // The wait counts assume exactly this issue order (activations, then
     // weights, stage by stage); the scheduling barriers keep the compiler
     // from interleaving the groups.
@@ -476,47 +565,46 @@ struct WideWave {
         }
     }
 
-    template <int kb>
-    __device__ __forceinline__ void kblock() {
-        if constexpr (kb + 1 < kKB) {
-            arrive<kb + 1>();
-            // the stages of K-block kb are in registers: refill their slots
-            if constexpr (kb + P::kRA < kKB)
-                issue_a(kb + P::kRA);
-            __builtin_amdgcn_sched_barrier(0);
-            if constexpr (kb + P::kRW < kKB)
-                issue_w(kb + P::kRW);
-            __builtin_amdgcn_sched_barrier(0);
-            read_frags<kb + 1>();
-        }
+    // MFMA n = (t, j) of K-block kb (and, with fp32 scales, the fold of
+    // MFMA n - kLag), then the loads and reads of slot n; the scheduling
+    // barrier keeps each slot's work where it is.
+    template <int kb, int t, int j>
+    __device__ __forceinline__ void mfma_step() {
         constexpr int b = kb & 1;
+        constexpr int n = (kb * kNS + t) * kMT + j;
         if constexpr (kE8m0) {
             // the scales ride on the MFMA: accumulate the whole K in place
             constexpr int wd = kb / 4, sh = 8 * (kb % 4);
-#pragma unroll
-            for (int t = 0; t < kNS; ++t)
-#pragma unroll
-                for (int j = 0; j < kMT; ++j)
-                    acc[j][t] = mfma_e4m3_16x16x128_scaled(wfs[b][t], af[b][j], acc[j][t], (bsw[t][wd] >> sh) & 0xFFu,
-                                                           asb[b][j]);
+            acc[j][t] = mfma_e4m3_16x16x128_scaled(wfs[b][t], af[b][j], acc[j][t], (bsw[t][wd] >> sh) & 0xFFu,
+                                                   asb[b][j]);
         } else {
-#pragma unroll
-        for (int t = 0; t < kNS; ++t) {
-#pragma unroll
-            for (int j = 0; j < kMT; ++j) {
-                const int n = (kb * kNS + t) * kMT + j;
-                part[n % kRing] = mfma_e4m3_16x16x128(wfs[b][t], af[b][j]);
-                scl[n % kRing] = asv[b][j] * bss[b][t];
-                if (n >= kLag) {
-                    fold(n - kLag);
-                    // the next MFMA reads af[] after this asm, so it stays
-                    // behind these FMAs (VALU work in the matrix core's shadow)
-                    v4f &folded = acc[(n - kLag) % kMT][((n - kLag) / kMT) % kNS];
-                    asm volatile("" : "+v"(af[b][(j + 1) % kMT]), "+v"(folded));
-                }
+            part[n % kRing] = mfma_e4m3_16x16x128(wfs[b][t], af[b][j]);
+            scl[n % kRing] = asv[b][j] * bss[b][t];
+            if constexpr (n >= kLag) {
+                fold(n - kLag);
+                // the next MFMA reads af[] after this asm, so it stays
+                // behind these FMAs (VALU work in the matrix core's shadow)
+                v4f &folded = acc[(n - kLag) % kMT][((n - kLag) / kMT) % kNS];
+                asm volatile("" : "+v"(af[b][(j + 1) % kMT]), "+v"(folded));
             }
         }
+        if constexpr (kb + 1 < kKB) {
+            loads_at<kb, t * kMT + j>();
+            reads_at<kb + 1, t * kMT + j>();
         }
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (j + 1 < kMT)
+            mfma_step<kb, t, j + 1>();
+        else if constexpr (t + 1 < kNS)
+            mfma_step<kb, t + 1, 0>();
+    }
+
+    template <int kb>
+    __device__ __forceinline__ void kblock() {
+        if constexpr (kb + 1 < kKB)
+            arrive<kb + 1>();
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_step<kb, 0, 0>();
         if constexpr (kb + 1 < kKB)
             kblock<kb + 1>();
     }
