@@ -292,8 +292,8 @@ __device__ __forceinline__ SubTile subtile(const GemmParams &p, int64_t st) {
 // kE8m0: e8m0 scales, applied by the matrix core (no scale stages in LDS).
 template <int kKB, int kNS, int kMT, int kWaves, bool kE8m0 = false>
 struct WidePlan {
-    static_assert(kNS % 2 == 0 && kNS >= 2 && kNS <= (kMT == 1 ? 8 : 6),
-                  "whole 2-slot subtiles; two fragment sets fit the registers");
+    static_assert(kNS >= 1 && (kNS == 1 || kNS % 2 == 0) && kNS <= (kMT == 1 ? 8 : 6),
+                  "one subtile, or whole pairs of them; two fragment sets fit the registers");
     static_assert(kWaves == 4 || kWaves == 8, "4 or 8 waves");
     static_assert(kMT >= 1 && kMT * kWaves * 16 <= 256, "at most 256 rows");
     static constexpr int kSlot = 1024;                         // 8 rows x 128 bytes
@@ -302,7 +302,14 @@ struct WidePlan {
     // per wave: As (a dword per lane; e8m0: its byte, zero-extended) and,
     // with fp32 scales, Bs
     static constexpr int kSStage = kWaves * (kE8m0 ? 1 : 2) * kWave * 4;
-    static constexpr int kRA = cmin(kKB, 3);                   // activation stages
+    // Blocks of one 64-row chunk over one or two subtiles (narrow weights:
+    // tensor-parallel shards) have 1-2 MFMAs per wave and K-block, so their
+    // K loop is paced by the L2 round trip of each activation stage: give
+    // them 5 activation stages (74 KB with 6 weight stages, still two blocks
+    // per CU; measured: TP-8 W_b at M = 256 5.17 -> 4.70 us, TP-4 pair at
+    // M = 64 5.97 -> 5.48 us), the rest 3.
+    static constexpr bool kShallowWork = kNS <= 2 && kMT == 1 && kWaves == 4;
+    static constexpr int kRA = cmin(kKB, kShallowWork ? 5 : 3);  // activation stages
     // weight stages: as many as the rest of the 160 KB allows, up to 6
     static constexpr int kRW = cmin(kKB, cmin(6, (160 * 1024 - kRA * (kAStage + kSStage)) / kWStage));
     // weight loads per wave per stage; when 2 kNS slots do not split evenly,
@@ -1643,8 +1650,15 @@ template <int kKB, int kMT>
 hipError_t launch_wide_ns(const GemmParams &p, hipStream_t stream) {
     // subtiles per block: the smallest even count that covers N (+ N2) with
     // one block per CU; beyond 6 per CU (8 with one 16-row tile per wave)
-    // the grid simply has more blocks than CUs (registers: two fragment sets)
+    // the grid simply has more blocks than CUs (registers: two fragment sets).
+    // At most one subtile per CU (a TP-8 shard pair, 17-64 rows): one subtile
+    // per block, so every CU streams (measured: TP-8 pair at M = 32 5.40 ->
+    // 4.64 us, at M = 64 5.55 -> 5.17 us).
     const int64_t per_cu = ((p.N + p.N2) / 16 + device_cu_count() - 1) / device_cu_count();
+    if constexpr (kMT == 1) {
+        if (per_cu <= 1)
+            return launch_wide<kKB, 1, kMT, kWideWaves>(p, stream);
+    }
     if (per_cu <= 2)
         return launch_wide<kKB, 2, kMT, kWideWaves>(p, stream);
     if (per_cu <= 4)

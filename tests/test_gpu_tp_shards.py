@@ -181,3 +181,36 @@ def test_a_row_does_not_depend_on_its_batch(which):
         full = run(0, 256)
         for lo, hi in ((0, 16), (240, 256), (64, 128), (3, 103), (0, 200), (56, 256)):
             assert np.array_equal(run(lo, hi), full[lo:hi]), f"{which} rows {lo}:{hi} t={layout}"
+
+
+@pytest.mark.parametrize("M", [20, 40, 64])
+def test_one_subtile_blocks_equal_the_slab_kernels(M):
+    """Between 17 and 64 rows a weight of at most one 16-row subtile per CU
+    (a TP-8 shard, alone or paired with the other shard) runs the wide
+    kernel with one subtile per block; paired with a full consumer weight the
+    same shard runs in slabs of several subtiles.  Outputs must be equal bit
+    for bit, row-major and tiled weights, both As layouts, and match the
+    oracle on sampled column blocks."""
+    dev = gpu_or_skip()
+    wa, wb = full_weights()
+    r = np.random.default_rng(600 + M)
+    a_np = r.integers(0, 0x100, size=(M, 1536), dtype=np.uint8) & 0xF7   # no NaN codes
+    a = dev_u8(a_np, dev)
+    As = np.exp2(r.uniform(-8, 0, (M, 12))).astype(np.float32)
+    for shard_w, other in ((shard(wa, 8, 7), wb), (shard(wb, 8, 7), wa)):
+        cs, ss = shard_w
+        for tiled in (False, True):
+            dw = dev_u8(cs, dev)
+            dw = mi.relayout_weight(dw) if tiled else dw
+            do = dev_u8(other.codes, dev)
+            do = mi.relayout_weight(do) if tiled else do
+            dss, dos = dev_f32(ss, dev), dev_f32(other.scale, dev)
+            for layout in (False, True):
+                das = dev_f32(As.T.copy(), dev).T if layout else dev_f32(As, dev)
+                single = mi.mi_block_scaled_fp8_gemm(a, das, dw, dss)
+                paired, _ = mi.mi_block_scaled_fp8_gemm_pair(a, das, dw, dss, do, dos)
+                torch.cuda.synchronize()
+                assert np.array_equal(host_bf16_bits(single), host_bf16_bits(paired)), \
+                    f"M{M} [{cs.shape[0]}] tiled={tiled} t={layout}"
+            cols, ref = sampled_ref(a_np, As.reshape(-1), False, cs, ss, seed=M)
+            assert_gemm_close(bf16_to_f64(single)[:, cols], ref, f"M{M} [{cs.shape[0]}] tiled={tiled}")
