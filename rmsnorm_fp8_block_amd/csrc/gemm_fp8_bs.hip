@@ -292,8 +292,8 @@ __device__ __forceinline__ SubTile subtile(const GemmParams &p, int64_t st) {
 // kE8m0: e8m0 scales, applied by the matrix core (no scale stages in LDS).
 template <int kKB, int kNS, int kMT, int kWaves, bool kE8m0 = false>
 struct WidePlan {
-    static_assert(kNS >= 1 && (kNS == 1 || kNS % 2 == 0) && kNS <= (kMT == 1 ? 8 : 6),
-                  "one subtile, or whole pairs of them; two fragment sets fit the registers");
+    static_assert(kNS >= 1 && (kNS <= 3 || kNS % 2 == 0) && kNS <= (kMT == 1 ? 8 : 6),
+                  "1-3 subtiles or whole pairs of them; two fragment sets fit the registers");
     static_assert(kWaves == 4 || kWaves == 8, "4 or 8 waves");
     static_assert(kMT >= 1 && kMT * kWaves * 16 <= 256, "at most 256 rows");
     static constexpr int kSlot = 1024;                         // 8 rows x 128 bytes
@@ -302,13 +302,13 @@ struct WidePlan {
     // per wave: As (a dword per lane; e8m0: its byte, zero-extended) and,
     // with fp32 scales, Bs
     static constexpr int kSStage = kWaves * (kE8m0 ? 1 : 2) * kWave * 4;
-    // Blocks of one 64-row chunk over one or two subtiles (narrow weights:
-    // tensor-parallel shards) have 1-2 MFMAs per wave and K-block, so their
+    // Blocks of one 64-row chunk over one to three subtiles (narrow weights:
+    // tensor-parallel shards) have 1-3 MFMAs per wave and K-block, so their
     // K loop is paced by the L2 round trip of each activation stage: give
-    // them 5 activation stages (74 KB with 6 weight stages, still two blocks
-    // per CU; measured: TP-8 W_b at M = 256 5.17 -> 4.70 us, TP-4 pair at
-    // M = 64 5.97 -> 5.48 us), the rest 3.
-    static constexpr bool kShallowWork = kNS <= 2 && kMT == 1 && kWaves == 4;
+    // them 5 activation stages (74 KB with 6 weight stages at two subtiles,
+    // still two blocks per CU; measured: TP-8 W_b at M = 256 5.17 -> 4.70 us,
+    // TP-4 pair at M = 64 5.97 -> 5.48 us), the rest 3.
+    static constexpr bool kShallowWork = kNS <= 3 && kMT == 1 && kWaves == 4;
     static constexpr int kRA = cmin(kKB, kShallowWork ? 5 : 3);  // activation stages
     // weight stages: as many as the rest of the 160 KB allows, up to 6
     static constexpr int kRW = cmin(kKB, cmin(6, (160 * 1024 - kRA * (kAStage + kSStage)) / kWStage));
@@ -1661,6 +1661,12 @@ hipError_t launch_wide_ns(const GemmParams &p, hipStream_t stream) {
     }
     if (per_cu <= 2)
         return launch_wide<kKB, 2, kMT, kWideWaves>(p, stream);
+    // three subtiles per CU (e.g. a TP-2 W_a shard): three per block rather
+    // than four, so no CU idles (TP-2 W_a at M = 32 6.80 -> 6.49 us)
+    if constexpr (kMT == 1) {
+        if (per_cu == 3)
+            return launch_wide<kKB, 3, kMT, kWideWaves>(p, stream);
+    }
     if (per_cu <= 4)
         return launch_wide<kKB, 4, kMT, kWideWaves>(p, stream);
     if constexpr (kMT == 1) {
@@ -1676,6 +1682,13 @@ hipError_t launch_wide_split(const GemmParams &p, int64_t slabs, hipStream_t str
     const int64_t chunks128 = (p.M + 127) / 128;
     if (slabs * chunks128 >= device_cu_count())
         return launch_wide<kKB, kNS, 2, kWideWaves>(p, stream);
+    // 64-row chunks of two-subtile slabs, or of three-subtile slabs where
+    // two would give more blocks than CUs and three do not (TP-8 W_a at
+    // M = 256: 384 blocks, half the CUs holding two, against 256; 7.37 ->
+    // 6.18 us)
+    const int64_t S = (p.N + p.N2) / 16, nm = (p.M + 63) / 64, cus = device_cu_count();
+    if ((S + 1) / 2 * nm > cus && (S + 2) / 3 * nm <= cus)
+        return launch_wide<kKB, 3, 1, kWideWaves>(p, stream);
     return launch_wide<kKB, kNS, 1, kWideWaves>(p, stream);
 }
 
@@ -1692,6 +1705,15 @@ hipError_t launch_wide_kb(const GemmParams &p, hipStream_t stream) {
     const int64_t slabs = (S + 1) / 2;  // at 2 subtiles per block
     if (2 * slabs < cus)
         return launch_wide_split<kKB, 2>(p, slabs, stream);
+    // Fewer two-subtile slabs than CUs (at most two subtiles per CU) would
+    // leave CUs idle with all M rows per block: three-subtile slabs of half
+    // the rows where that fills more of them (a TP-4 W_a shard at M = 256:
+    // 256 blocks against 192; 9.77 -> 8.43 us, at M = 128 6.72 -> 6.52 us).
+    if (slabs < cus && (S + 2) / 3 * 2 <= cus && (S + 2) / 3 * 2 > slabs) {
+        if (p.M <= 128)
+            return launch_wide<kKB, 3, 1, kWideWaves>(p, stream);
+        return launch_wide<kKB, 3, 2, kWideWaves>(p, stream);
+    }
     if (p.M <= 128)
         return launch_wide_ns<kKB, 2>(p, stream);
     return launch_wide_ns<kKB, 4>(p, stream);

@@ -134,12 +134,13 @@ def test_split_k_equals_the_k_loop_kernels(M):
                     f"M{M} [{cs.shape[0]}] tiled={tiled} t={layout}"
 
 
-@pytest.mark.parametrize("M", [1, 16])
+@pytest.mark.parametrize("M", [1, 16, 40])
 @pytest.mark.parametrize("N", [12288, 16384, 20480])
 def test_one_subtile_per_wave_equals_the_two_subtile_kernel(N, M):
     """Weights of three to five 16-row subtiles per CU (N = 12288, 16384,
     20480 on 256 CUs) at up to 16 rows run the stream kernel with one subtile
-    per wave and a wave per subtile; paired with W_a the same weight runs
+    per wave and a wave per subtile, and at 40 rows the wide kernel (three
+    subtiles per block at N = 12288); paired with W_a the same weight runs
     the stream kernel with two subtiles per wave.  The outputs must be equal
     bit for bit, tiled weights, both As layouts."""
     dev = gpu_or_skip()
@@ -183,21 +184,24 @@ def test_a_row_does_not_depend_on_its_batch(which):
             assert np.array_equal(run(lo, hi), full[lo:hi]), f"{which} rows {lo}:{hi} t={layout}"
 
 
-@pytest.mark.parametrize("M", [20, 40, 64])
+@pytest.mark.parametrize("M", [20, 40, 64, 128, 200, 256])
 def test_one_subtile_blocks_equal_the_slab_kernels(M):
     """Between 17 and 64 rows a weight of at most one 16-row subtile per CU
     (a TP-8 shard, alone or paired with the other shard) runs the wide
-    kernel with one subtile per block; paired with a full consumer weight the
-    same shard runs in slabs of several subtiles.  Outputs must be equal bit
-    for bit, row-major and tiled weights, both As layouts, and match the
-    oracle on sampled column blocks."""
+    kernel with one subtile per block; above 64 rows the TP-8 W_a shard runs
+    64-row chunks of three-subtile slabs and the W_b shard of two-subtile
+    slabs, and the TP-4 W_a shard three-subtile slabs of half the rows.
+    Paired with a full consumer weight the same shard runs in slabs of four
+    to six subtiles.  Outputs must be equal bit for bit, row-major
+    and tiled weights, both As layouts, and match the oracle on sampled
+    column blocks."""
     dev = gpu_or_skip()
     wa, wb = full_weights()
     r = np.random.default_rng(600 + M)
     a_np = r.integers(0, 0x100, size=(M, 1536), dtype=np.uint8) & 0xF7   # no NaN codes
     a = dev_u8(a_np, dev)
     As = np.exp2(r.uniform(-8, 0, (M, 12))).astype(np.float32)
-    for shard_w, other in ((shard(wa, 8, 7), wb), (shard(wb, 8, 7), wa)):
+    for shard_w, other in ((shard(wa, 8, 7), wb), (shard(wb, 8, 7), wa), (shard(wa, 4, 3), wb)):
         cs, ss = shard_w
         for tiled in (False, True):
             dw = dev_u8(cs, dev)
