@@ -126,11 +126,16 @@ def gemm_ref(a, As, w, Bs, cols=None, blocks=None):
 # decode-size batches (the wide kernel), 64 < M <= 256 (wide, row split for
 # narrow weights), M > 256 and K / 128 = 5 (the generic kernel)
 # (two subtiles per CU at M <= 16: the stream kernel with one subtile per wave;
-# 200 and 256 rows of 8192 and 12288 weight rows: the stream kernel in 64-row chunks)
+# 200 and 256 rows of 8192 and 12288 weight rows: the stream kernel in 64-row chunks;
+# the wide kernel's narrow-weight blocks: one subtile per block at 40 rows of 3072,
+# three subtiles per block at 32 rows of 12288, 64-row chunks of three-subtile slabs
+# at 256 rows of 3072, three-subtile slabs of half the rows at 200 rows of 6144)
 @pytest.mark.parametrize("M,N,K,seed", [(1, 24576, 1536, 1), (16, 8192, 1536, 2), (64, 1024, 512, 3),
                                         (100, 1536, 1536, 4), (256, 6144, 1536, 5), (300, 640, 1536, 6),
                                         (40, 384, 640, 7), (64, 2048, 2048, 8), (1, 6144, 1536, 9),
-                                        (16, 6144, 1536, 10), (200, 8192, 1536, 11), (256, 12288, 1536, 12)])
+                                        (16, 6144, 1536, 10), (200, 8192, 1536, 11), (256, 12288, 1536, 12),
+                                        (40, 3072, 1536, 13), (32, 12288, 1536, 14), (256, 3072, 1536, 15),
+                                        (200, 6144, 1536, 16)])
 def test_gemm_e8m0_vs_oracle(M, N, K, seed):
     dev = gpu_or_skip()
     a, As, w, Bs = e8m0_operands(M, N, K, seed)

@@ -78,11 +78,15 @@ def test_gemm_random_vs_oracle(M, N, K, seed):
 
 @pytest.mark.parametrize("M,N,K,seed", [(65, 384, 512, 21), (129, 1280, 1024, 22), (100, 1536, 1536, 23),
                                         (256, 16640, 1536, 24), (72, 32768, 512, 25), (200, 12288, 1536, 26),
-                                        (256, 8192, 2048, 27), (256, 24576, 1536, 28), (193, 8192, 1536, 29)])
+                                        (256, 8192, 2048, 27), (256, 24576, 1536, 28), (193, 8192, 1536, 29),
+                                        (256, 3072, 1536, 30), (150, 6144, 1536, 31), (100, 3072, 1536, 32)])
 def test_gemm_wide_shapes_sampled(M, N, K, seed):
     """64 < M <= 256 at widths that give 2, 4, 6 and 8 weight subtiles per
     block, with a ragged last block (N = 16640: 1040 subtiles in blocks of 6);
-    W_b's width at 193 rows (the stream kernel, one row in its last chunk).
+    W_b's width at 193 rows (the stream kernel, one row in its last chunk);
+    narrow weights split into row chunks: 64-row chunks of three-subtile
+    slabs (N = 3072 at 256 rows), three-subtile slabs of half the rows
+    (N = 6144 at 150 rows), and two-subtile slabs (N = 3072 at 100 rows).
     The oracle runs on the first, the last and two random 128-column blocks."""
     dev = gpu_or_skip()
     a, As, w, Bs = random_operands(M, N, K, seed)
