@@ -521,22 +521,22 @@ def sweep(torch, np, mi, W, wa, wb, dev, cold, tiled):
             del g, fns, wat0, wbt0
             torch.cuda.empty_cache()
     # tensor-parallel shards: rank r holds N/TP rows of W_a and W_b; the pair
-    # launch at decode sizes, the W_a shard alone at M = 256
+    # launch at decode sizes and at M = 256, and the W_a shard alone at M = 256
     for tp in (2, 4, 8):
         na, nb = wa.codes.shape[0] // tp, wb.codes.shape[0] // tp
         wac0, was = dev_weight(wa.codes[:na], tiled), torch.from_numpy(wa.scale[:na // 128]).to(dev)
         wbc0, wbs = dev_weight(wb.codes[:nb], tiled), torch.from_numpy(wb.scale[:nb // 128]).to(dev)
-        for M in (1, 16, 64, 256):
+        for M, pair in ((1, True), (16, True), (64, True), (256, False), (256, True)):
             a = torch.randint(0, 0x78, (M, 1536), dtype=torch.uint8, device=dev)
             asc = (torch.rand((12, M), dtype=torch.float32, device=dev) + 0.5).T   # column-major
-            per = (algorithmic_bytes_gemm_pair(M, na, nb, 1536) if M <= 64
+            per = (algorithmic_bytes_gemm_pair(M, na, nb, 1536) if pair
                    else algorithmic_bytes_gemm(M, na, 1536))
             nsets = max(1, COLD_BYTES // per + 1) if cold else 1
             fns = []
             for i in range(nsets):
                 wac = wac0 if i == 0 else copy_weight(wac0)
                 oa = torch.empty((M, na), dtype=torch.bfloat16, device=dev)
-                if M <= 64:
+                if pair:
                     wbc = wbc0 if i == 0 else copy_weight(wbc0)
                     ob = torch.empty((M, nb), dtype=torch.bfloat16, device=dev)
                     fns.append(mi.prepare_block_scaled_fp8_gemm_pair(a, asc, wac, was, oa, wbc, wbs, ob))
@@ -544,9 +544,11 @@ def sweep(torch, np, mi, W, wa, wb, dev, cold, tiled):
                     fns.append(mi.prepare_block_scaled_fp8_gemm(a, asc, wac, was, oa))
             g = make_graph(torch, fns)
             us = time_graph(torch, g, len(fns), max(1, 200 // len(fns)))
-            key = f"tp{tp}_pair_M{M}" if M <= 64 else f"tp{tp}_W_a_M{M}"
-            res[key] = {"N": [na, nb] if M <= 64 else na, "us": round(us, 3), "GB/s": round(per / us / 1e3, 1),
+            key = f"tp{tp}_pair_M{M}" if pair else f"tp{tp}_W_a_M{M}"
+            res[key] = {"N": [na, nb] if pair else na, "us": round(us, 3), "GB/s": round(per / us / 1e3, 1),
                         "frac_hbm": round(per / us / 1e3 / HBM_PEAK_GBS, 4)}
+            if pair and M > 64:   # the pair's own launches (the step's count less the norm-quant's)
+                res[key]["launches"] = mi.mi_fused_normquant_gemm_pair_launches(M, W.NQ, W.NKV, na, nb) - 1
             del g, fns
         del wac0, wbc0
         torch.cuda.empty_cache()

@@ -333,7 +333,7 @@ extern "C" int mi_fused_normquant_gemm_pair_launches(int64_t M, int64_t Nq, int6
         return -1;
     if (M == 0)
         return 0;
-    return mi::normquant_gemm_pair_one_launch(M, Nq, Nkv, N1, N2) ? 1 : 1 + mi::gemm_pair_launches(M, Nq);
+    return mi::normquant_gemm_pair_one_launch(M, Nq, Nkv, N1, N2) ? 1 : 1 + mi::gemm_pair_launches(M, Nq, N1, N2);
 }
 
 extern "C" mi_status mi_block_scaled_fp8_gemm_e8m0(

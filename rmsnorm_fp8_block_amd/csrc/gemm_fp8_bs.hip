@@ -1702,6 +1702,23 @@ hipError_t launch_wide_kb(const GemmParams &p, hipStream_t stream) {
     // L2) rather than leave CUs idle; otherwise one block holds all M rows
     // (measured: splitting a grid that fills more than half the CUs loses).
     const int64_t S = (p.N + p.N2) / 16, cus = device_cu_count();
+    // One to two subtiles per CU (a TP-4 / TP-8 shard pair, a TP-4 shard):
+    // 64-row chunks of the fewest subtiles per block that still give one
+    // block per CU (measured, paired A/B: the TP-8 pair at M = 128 9.78 ->
+    // 5.12 us and at M = 256 10.95 -> 6.64 us together with its one launch,
+    // the TP-4 W_a shard at M = 256 8.37 -> 8.10 us, 5120 rows at M = 256
+    // 9.10 -> 8.11 us).
+    if (S >= cus && S < 2 * cus) {
+        const int64_t nm = (p.M + 63) / 64;
+        if ((S + 1) / 2 * nm <= cus)
+            return launch_wide<kKB, 2, 1, kWideWaves>(p, stream);
+        if ((S + 2) / 3 * nm <= cus)
+            return launch_wide<kKB, 3, 1, kWideWaves>(p, stream);
+        if ((S + 3) / 4 * nm <= cus)
+            return launch_wide<kKB, 4, 1, kWideWaves>(p, stream);
+        if ((S + 5) / 6 * nm <= cus)
+            return launch_wide<kKB, 6, 1, kWideWaves>(p, stream);
+    }
     const int64_t slabs = (S + 1) / 2;  // at 2 subtiles per block
     if (2 * slabs < cus)
         return launch_wide_split<kKB, 2>(p, slabs, stream);
@@ -1975,15 +1992,28 @@ hipError_t init_device() {
     return hipSuccess;
 }
 
-int gemm_pair_launches(int64_t M, int64_t K) {
+// Both consumers in one launch: decode batches, and above 64 rows narrow
+// pairs (at most two subtiles per CU together, K / 128 = 12).
+static bool gemm_pair_one_launch(int64_t M, int64_t K, int64_t N1, int64_t N2) {
     const int64_t kb = K / kBlk;
-    return M <= kChunkRows && (kb == 4 || kb == 8 || kb == 12 || kb == 16) ? 1 : 2;
+    if (M <= kChunkRows)
+        return kb == 4 || kb == 8 || kb == 12 || kb == 16;
+    return M <= 256 && kb == 12 && (N1 + N2) / 16 <= 2 * device_cu_count();
+}
+
+int gemm_pair_launches(int64_t M, int64_t K, int64_t N1, int64_t N2) {
+    return gemm_pair_one_launch(M, K, N1, N2) ? 1 : 2;
 }
 
 hipError_t launch_block_scaled_gemm_pair(const GemmParams &p, hipStream_t stream) {
     // decode batches: one launch over the subtiles of both weights, sharing
     // the activation tile (split-K over narrow weights, the stream kernel
     // where the weights are wide enough, else the wide kernel)
+    // narrow pairs above 64 rows: one wide launch over the subtiles of both
+    // (TP-8 pair at M = 128 9.8 -> 5.1 us, TP-4 pair at M = 128 11.3 -> 7.0 us
+    // against two launches)
+    if (p.M > kChunkRows && gemm_pair_one_launch(p.M, p.K, p.N, p.N2))
+        return launch_wide_kb<12>(p, stream);
     if (p.M <= kChunkRows) {
         hipError_t e = launch_splitk(p, stream);
         if (e == hipErrorNotSupported)

@@ -70,8 +70,9 @@ hipError_t launch_group_quant(const NormQuantParams &p, bool normalize, hipStrea
 hipError_t launch_block_scaled_gemm(const GemmParams &p, hipStream_t stream);
 // both consumers (p.N2 > 0) in one launch where the shape allows, else two
 hipError_t launch_block_scaled_gemm_pair(const GemmParams &p, hipStream_t stream);
-// kernel launches launch_block_scaled_gemm_pair makes for M rows, depth K
-int gemm_pair_launches(int64_t M, int64_t K);
+// kernel launches launch_block_scaled_gemm_pair makes for M rows, depth K,
+// consumers of N1 and N2 rows (on the current device)
+int gemm_pair_launches(int64_t M, int64_t K, int64_t N1, int64_t N2);
 // the decode step in one launch: the norm-quant of a.M rows and both
 // consumer GEMMs of its outputs (p.a / p.a_scale are a.out_q / a.out_scale).
 // hipErrorNotSupported where the shapes or alignment do not allow it.

@@ -285,6 +285,10 @@ def test_fused_step_launch_count(L):
     assert f(256, 1536, 512, 24576, 8192) == 3
     assert f(64, 2560, 512, 24576, 8192) == 3         # K / 128 = 20: two GEMMs
     assert f(1, 1536, 512, 3072, 1024) == 2       # narrow weights
+    assert f(256, 1536, 512, 3072, 1024) == 2     # narrow pair above 64 rows: one launch
+    assert f(256, 1536, 512, 6144, 2048) == 2
+    assert f(256, 1536, 512, 12288, 4096) == 3    # 1024 subtiles: two GEMMs
+    assert f(256, 2048, 512, 3072, 1024) == 3     # K / 128 = 16 above 64 rows: two GEMMs
     assert f(1, 1024, 512, 24576, 8192) == 2      # other latent width
     assert f(1, 1536, 448, 24576, 8192) == 2
     assert f(-1, 1536, 512, 24576, 8192) == -1

@@ -165,10 +165,11 @@ def test_step_back_to_back_with_changing_inputs(weights):
 
 @pytest.mark.parametrize("M,Nq,Nkv,N1,N2", [(65, 1536, 512, 24576, 8192), (100, 1536, 512, 24576, 8192),
                                             (64, 1536, 512, 3072, 1024), (16, 1024, 512, 24576, 8192),
-                                            (8, 1536, 448, 24576, 8192)])
+                                            (8, 1536, 448, 24576, 8192), (200, 1536, 512, 3072, 1024)])
 def test_step_shapes_that_take_two_launches(M, Nq, Nkv, N1, N2):
-    """Beyond 64 rows, narrow weights (a TP-8 shard), other latent widths:
-    two launches, the same results as the two calls."""
+    """Beyond 64 rows (three launches over the full weights, two over a
+    TP-8 shard pair), narrow weights, other latent widths: the same results
+    as the two calls."""
     dev = gpu_or_skip()
     r = np.random.default_rng(M + Nq + N1)
     buf = W.f32_to_bf16_bits(r.standard_normal((M, Nq + Nkv), dtype=np.float32))
@@ -183,6 +184,8 @@ def test_step_shapes_that_take_two_launches(M, Nq, Nkv, N1, N2):
     want = two_calls(q, kv, gq, gk, True, *args)
     torch.cuda.synchronize()
     assert_same(got, want, f"M{M} Nq{Nq} Nkv{Nkv} N{N1}+{N2}")
+    narrow_above_64 = M > 64 and Nq == 1536 and (N1 + N2) // 16 <= 2 * torch.cuda.get_device_properties(dev).multi_processor_count
+    assert mi.mi_fused_normquant_gemm_pair_launches(M, Nq, Nkv, N1, N2) == (2 if narrow_above_64 or M <= 64 else 3)
 
 
 @pytest.mark.parametrize("M", [16, 64])
