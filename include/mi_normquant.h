@@ -201,9 +201,9 @@ mi_status mi_block_scaled_fp8_gemm(
  * mi_block_scaled_fp8_gemm defines it (bit-identical results).  One launch
  * streams both weights and stages the shared activations once per compute
  * unit, for decode batches (M <= 64, K / 128 in {4, 8, 12, 16}) and for
- * narrow pairs above 64 rows (N1 + N2 <= 32 x the compute units: tensor-
- * parallel shards; K / 128 = 12); other shapes are run as two launches of
- * mi_block_scaled_fp8_gemm on the same stream.
+ * narrow pairs of up to 256 rows (N1 + N2 <= 64 x the compute units:
+ * tensor-parallel shards; K / 128 = 12); other shapes are run as two launches
+ * of mi_block_scaled_fp8_gemm on the same stream.
  *
  * a_fp8, a_scale, a_scale_transposed, M, K: as in mi_block_scaled_fp8_gemm.
  * w1_fp8, w1_scale, out1_bf16, N1: first consumer ([N1, K], [N1/128, K/128],
@@ -333,9 +333,9 @@ mi_status mi_fused_normquant_gemm_pair(
  * Kernel launches mi_fused_normquant_gemm_pair makes for these sizes on the
  * current device when every operand meets the alignment above: 1 (one
  * launch), else the norm-quant's one plus the pair's (one up to 64 rows with
- * K / 128 in {4, 8, 12, 16}, and above 64 rows for N1 + N2 <= 32 x the
- * compute units with K / 128 = 12; else two); 0 for M == 0; -1 for sizes the
- * call rejects.  Host only; enqueues nothing.
+ * K / 128 in {4, 8, 12, 16}, and from 65 to 256 rows for N1 + N2 <= 64 x
+ * the compute units with K / 128 = 12; else two); 0 for M == 0; -1 for sizes
+ * the call rejects.  Host only; enqueues nothing.
  */
 int mi_fused_normquant_gemm_pair_launches(int64_t M, int64_t Nq, int64_t Nkv, int64_t N1, int64_t N2);
 

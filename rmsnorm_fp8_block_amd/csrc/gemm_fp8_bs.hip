@@ -1992,13 +1992,15 @@ hipError_t init_device() {
     return hipSuccess;
 }
 
-// Both consumers in one launch: decode batches, and above 64 rows narrow
-// pairs (at most two subtiles per CU together, K / 128 = 12).
+// Both consumers in one launch: decode batches, and above 64 rows
+// tensor-parallel shard pairs (at most four subtiles per CU together,
+// K / 128 = 12; the full W_a + W_b pair, eight per CU, is 2.0-2.6 us faster
+// as two launches).
 static bool gemm_pair_one_launch(int64_t M, int64_t K, int64_t N1, int64_t N2) {
     const int64_t kb = K / kBlk;
     if (M <= kChunkRows)
         return kb == 4 || kb == 8 || kb == 12 || kb == 16;
-    return M <= 256 && kb == 12 && (N1 + N2) / 16 <= 2 * device_cu_count();
+    return M <= 256 && kb == 12 && (N1 + N2) / 16 <= 4 * device_cu_count();
 }
 
 int gemm_pair_launches(int64_t M, int64_t K, int64_t N1, int64_t N2) {
@@ -2009,9 +2011,9 @@ hipError_t launch_block_scaled_gemm_pair(const GemmParams &p, hipStream_t stream
     // decode batches: one launch over the subtiles of both weights, sharing
     // the activation tile (split-K over narrow weights, the stream kernel
     // where the weights are wide enough, else the wide kernel)
-    // narrow pairs above 64 rows: one wide launch over the subtiles of both
-    // (TP-8 pair at M = 128 9.8 -> 5.1 us, TP-4 pair at M = 128 11.3 -> 7.0 us
-    // against two launches)
+    // shard pairs above 64 rows: one wide launch over the subtiles of both
+    // (against two launches: TP-8 pair at M = 128 9.8 -> 5.1 us, TP-4 pair
+    // 11.3 -> 7.0 us, TP-2 pair 14.8 -> 10.6 us)
     if (p.M > kChunkRows && gemm_pair_one_launch(p.M, p.K, p.N, p.N2))
         return launch_wide_kb<12>(p, stream);
     if (p.M <= kChunkRows) {

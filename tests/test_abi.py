@@ -287,7 +287,8 @@ def test_fused_step_launch_count(L):
     assert f(1, 1536, 512, 3072, 1024) == 2       # narrow weights
     assert f(256, 1536, 512, 3072, 1024) == 2     # narrow pair above 64 rows: one launch
     assert f(256, 1536, 512, 6144, 2048) == 2
-    assert f(256, 1536, 512, 12288, 4096) == 3    # 1024 subtiles: two GEMMs
+    assert f(256, 1536, 512, 12288, 4096) == 2    # TP-2 pair: 1024 subtiles, one launch
+    assert f(257, 1536, 512, 3072, 1024) == 3     # beyond 256 rows: two GEMMs
     assert f(256, 2048, 512, 3072, 1024) == 3     # K / 128 = 16 above 64 rows: two GEMMs
     assert f(1, 1024, 512, 24576, 8192) == 2      # other latent width
     assert f(1, 1536, 448, 24576, 8192) == 2

@@ -214,13 +214,14 @@ def test_producer_and_two_consumers(M, transpose):
                                             (64, 3200, 1664, 1024, 35), (100, 1280, 640, 1536, 36),
                                             (256, 2048, 1024, 2048, 37), (7, 384, 128, 896, 38),
                                             (64, 12800, 6400, 1536, 39), (200, 3072, 1024, 1536, 40),
-                                            (128, 6144, 2048, 1536, 41), (100, 3200, 2944, 1536, 42)])
+                                            (128, 6144, 2048, 1536, 41), (100, 3200, 2944, 1536, 42),
+                                            (256, 12288, 4096, 1536, 43)])
 def test_gemm_pair_equals_two_gemms(M, N1, N2, K, seed):
     """The two-consumer entry point returns, bit for bit, what two calls of
     the single GEMM return (fused launch for M <= 64 and K/128 in {4, 8, 12,
     16}, including 6-subtile slabs that straddle the two weights at
-    N1 = 12800, and above 64 rows for narrow pairs with K/128 = 12: TP-8 and
-    TP-4 shard pairs, and three-subtile slabs straddling the two weights
+    N1 = 12800, and above 64 rows for shard pairs with K/128 = 12: TP-8,
+    TP-4 and TP-2 pairs, and three-subtile slabs straddling the two weights
     at N1 = 3200;
     two launches otherwise), and matches the oracle on sampled column blocks
     of both."""
