@@ -1429,6 +1429,11 @@ hipError_t launch_stream(const GemmParams &p, hipStream_t stream) {
                             : launch_stream_one_per_wave<false>(p, static_cast<int>(per_cu), stream);
     if (p.M > 256 || (p.M <= 64 && per_cu < 6))
         return hipErrorNotSupported;
+    // three subtiles per CU above 64 rows: the wide kernel's six-subtile
+    // slabs in two row chunks are faster (TP-2 W_a shard at M = 256 13.6 ->
+    // 12.4 us, at M = 128 9.75 -> 8.69 us)
+    if (p.M > 64 && per_cu == 3)
+        return hipErrorNotSupported;
     if (p.M > 64) {
         // Row chunks re-read their slab's weights (from L2), the wide kernel
         // re-reads every activation row per block: take the stream kernel only
@@ -1722,6 +1727,13 @@ hipError_t launch_wide_kb(const GemmParams &p, hipStream_t stream) {
     const int64_t slabs = (S + 1) / 2;  // at 2 subtiles per block
     if (2 * slabs < cus)
         return launch_wide_split<kKB, 2>(p, slabs, stream);
+    // three subtiles per CU: six-subtile slabs in two row chunks, a block
+    // per CU
+    if ((S + cus - 1) / cus == 3) {
+        if (p.M <= 128)
+            return launch_wide<kKB, 6, 1, kWideWaves>(p, stream);
+        return launch_wide<kKB, 6, 2, kWideWaves>(p, stream);
+    }
     // Fewer two-subtile slabs than CUs (at most two subtiles per CU) would
     // leave CUs idle with all M rows per block: three-subtile slabs of half
     // the rows where that fills more of them (a TP-4 W_a shard at M = 256:
