@@ -1411,7 +1411,8 @@ hipError_t launch_stream_one_per_wave(const GemmParams &p, int waves, hipStream_
 // The stream kernel, 2 subtiles per wave, where its grid (weight slabs x
 // 64-row chunks) covers the CUs: decode batches (M <= 64) over at least 6
 // weight subtiles per CU (3 waves per block at 6, else 4), and 64 < M <= 256
-// (4 waves).  K/128 in {4, 8, 12}.  Returns hipErrorNotSupported otherwise.
+// (4 waves) except at three subtiles per CU.  K/128 in {4, 8, 12}.  Returns
+// hipErrorNotSupported otherwise.
 hipError_t launch_stream(const GemmParams &p, hipStream_t stream) {
     const int64_t S = (p.N + p.N2) / 16, cus = device_cu_count();
     const int64_t per_cu = (S + cus - 1) / cus;
