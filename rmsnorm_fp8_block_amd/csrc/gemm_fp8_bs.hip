@@ -302,13 +302,15 @@ struct WidePlan {
     // per wave: As (a dword per lane; e8m0: its byte, zero-extended) and,
     // with fp32 scales, Bs
     static constexpr int kSStage = kWaves * (kE8m0 ? 1 : 2) * kWave * 4;
-    // Blocks of one 64-row chunk over one to three subtiles (narrow weights:
-    // tensor-parallel shards) have 1-3 MFMAs per wave and K-block, so their
+    // Blocks of one 64-row chunk over one to four subtiles (narrow weights:
+    // tensor-parallel shards) have 1-4 MFMAs per wave and K-block, so their
     // K loop is paced by the L2 round trip of each activation stage: give
     // them 5 activation stages (74 KB with 6 weight stages at two subtiles,
-    // still two blocks per CU; measured: TP-8 W_b at M = 256 5.17 -> 4.70 us,
-    // TP-4 pair at M = 64 5.97 -> 5.48 us), the rest 3.
-    static constexpr bool kShallowWork = kNS <= 3 && kMT == 1 && kWaves == 4;
+    // still two blocks per CU; 98 KB at four, chosen only where the grid has
+    // a block per CU; measured: TP-8 W_b at M = 256 5.17 -> 4.70 us, TP-4
+    // pair at M = 64 5.97 -> 5.48 us, TP-2 pair at M = 32 8.01 -> 6.88 us),
+    // the rest 3.
+    static constexpr bool kShallowWork = kNS <= 4 && kMT == 1 && kWaves == 4;
     static constexpr int kRA = cmin(kKB, kShallowWork ? 5 : 3);  // activation stages
     // weight stages: as many as the rest of the 160 KB allows, up to 6
     static constexpr int kRW = cmin(kKB, cmin(6, (160 * 1024 - kRA * (kAStage + kSStage)) / kWStage));
